@@ -1,0 +1,384 @@
+"""float64 CPU oracle of block-sparse global attention — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module. It is deliberately plain: numpy in
+float64, no blocking, fusion or reordering beyond what the definitions state,
+so that each function can be checked against the pages by eye.
+
+Sources ("the ReSS page" below is "ReSS: Residual-Restoring Sparse Attention
+for 3D Vision Transformers"; "the subject page" is "Block-Sparse Global
+Attention for Efficient Multi-View Geometry Transformers"):
+
+* §3 "Block-Sparse Attention for 3D ViTs" of the ReSS page: blocks are mean
+  pooled into a block-level attention map; per (query block, head) key blocks
+  are selected up to a per-head budget; exact attention runs over the
+  selected blocks only, with softmax renormalised among them; blocks holding
+  special tokens are never dropped.
+* §4.1 (Eq. 1-2), §4.2 (Eq. 3-9), §4.3 (Eq. 10-17) of the ReSS page: the
+  pooled dense output, the drift score and the drop-set refinement.
+* The subject page's abstract: training-free block-sparse replacement of
+  dense global attention.
+
+Readings where the pages leave a step open (each one is listed with its
+reason in the design notes of the repository):
+
+* softmax scale 1/sqrt(D) for both the pooled map and token attention;
+* the pooled map is the softmax over all key blocks of the scaled dot
+  products of mean-pooled Q and K (not token probabilities pooled after the
+  fact); a partial (padded) block is pooled over its valid tokens only;
+* ties in any top-k / top-m go to the lower block index;
+* refinement rounds are batched: restore and drop gains both come from the
+  round-start state, m_r = floor(rho * c / 2^(r+1)), both sets applied, then
+  g, K, G recomputed from their definitions; a drop whose K + u <= 0 gets a
+  gain of -inf; track-best keeps a new set only when its J is strictly lower.
+
+Parity pins: every function here is checked against closed forms, library
+routines, explicit masking and brute force in ``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Step 1: mean pooling and the pooled block-level map (ReSS page, §3 step (1))
+# ---------------------------------------------------------------------------
+
+def block_pool(x: np.ndarray, N: int, B: int) -> np.ndarray:
+    """Mean of the valid tokens of every block.
+
+    x: float64 [H][N_pad][D]; tokens t >= N are padding and are ignored.
+    Returns float64 [H][n][D], n = N_pad / B.  (ReSS page, §3: "mean pooling
+    within each block".)
+    """
+    H, N_pad, D = x.shape
+    n = N_pad // B
+    out = np.empty((H, n, D), dtype=np.float64)
+    for b in range(n):
+        lo, hi = b * B, min((b + 1) * B, N)
+        out[:, b, :] = x[:, lo:hi, :].mean(axis=1)
+    return out
+
+
+def block_map(qpool: np.ndarray, kpool: np.ndarray, scale: float) -> np.ndarray:
+    """Pooled attention probabilities P[h][i][j], normalised over all key blocks.
+
+    P_ij = softmax_j(scale * qpool_i . kpool_j) over every key block j
+    (ReSS page, §4.1: the map is normalised over the set of all key blocks).
+    """
+    logits = scale * np.matmul(qpool, np.swapaxes(kpool, 1, 2))
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: block scores
+# ---------------------------------------------------------------------------
+
+def pooled_output(P: np.ndarray, vpool: np.ndarray) -> np.ndarray:
+    """Dense pooled attention output, ReSS page Eq. 1: vout_i = sum_j P_ij V_j."""
+    return np.matmul(P, vpool)
+
+
+def _gram(M: Optional[np.ndarray], h: int, D: int) -> np.ndarray:
+    return np.eye(D) if M is None else M[h]
+
+
+def drift_key(P: np.ndarray, vpool: np.ndarray, M: Optional[np.ndarray],
+              eps: float = 1e-4, row_chunk: int = 64):
+    """ReSS drift ranking key, Eq. 5-7, in the direct (unexpanded) form.
+
+    e_ij = vout_i - V_j (Eq. 4's deviation), q_ij = e_ij^T M_h e_ij (the
+    squared residual-space norm of Eq. 6 written with the Gram matrix of
+    Eq. 8; M_h = I when M is None), s_ij = P_ij sqrt(q_ij) (Eq. 6), and the
+    key is s_ij / max(1 - P_ij, eps) (Eq. 7). q is clamped at 0 against
+    rounding. Returns (key, vout, q), all float64.
+    """
+    H, n, D = vpool.shape
+    vout = pooled_output(P, vpool)
+    q = np.empty((H, n, n), dtype=np.float64)
+    for h in range(H):
+        Mh = _gram(M, h, D)
+        for i0 in range(0, n, row_chunk):
+            i1 = min(n, i0 + row_chunk)
+            e = vout[h, i0:i1, None, :] - vpool[h, None, :, :]  # [ci][n][D]
+            q[h, i0:i1] = np.sum(np.matmul(e, Mh) * e, axis=-1)
+    q = np.maximum(q, 0.0)
+    s = P * np.sqrt(q)
+    key = s / np.maximum(1.0 - P, eps)
+    return key, vout, q
+
+
+def score_key(P, vpool, M, mode: str, eps: float = 1e-4):
+    """Ranking key of every (h, i, j): the pooled probability ("prob",
+    SparseVGGT/HeSS as described in the ReSS page §3 "The Probability
+    Assumption") or the drift key ("drift", ReSS page Eq. 7)."""
+    if mode == "prob":
+        return P.copy()
+    if mode == "drift":
+        return drift_key(P, vpool, M, eps)[0]
+    raise ValueError(mode)
+
+
+# ---------------------------------------------------------------------------
+# Step 3: per-row top-k selection (ReSS page, §3 step (2) and §4.1 Eq. 2)
+# ---------------------------------------------------------------------------
+
+def _order_desc(values: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Positions of idx sorted by value descending, then index ascending."""
+    return np.lexsort((idx, -values))
+
+
+def _rel_gap(a: float, b: float) -> float:
+    den = max(abs(a), abs(b))
+    if den == 0.0:
+        return 0.0
+    if not (math.isfinite(a) and math.isfinite(b)):
+        return math.inf if a != b else 0.0
+    return abs(a - b) / den
+
+
+def select_topk(key: np.ndarray, keep: np.ndarray, always: np.ndarray):
+    """Kept key blocks of every (head, query-block row).
+
+    Candidates are the blocks not flagged in ``always``; per row the c_h =
+    keep[h] - |always| candidates with the largest key are selected (ties to
+    the lower block index), and the always-kept blocks are added (ReSS page
+    §4.1: blocks holding special tokens are always kept, the candidate set P
+    is the rest, |S| = c_h).
+
+    Returns (kept bool [H][n][n], margin float64 [H][n]) where margin is the
+    relative gap between the c-th and (c+1)-th candidate keys of the row
+    (inf when every candidate is kept).
+    """
+    H, n, _ = key.shape
+    cand = np.nonzero(always == 0)[0]
+    alw = np.nonzero(always != 0)[0]
+    kept = np.zeros(key.shape, dtype=bool)
+    margin = np.full((H, n), np.inf)
+    for h in range(H):
+        c = int(keep[h]) - len(alw)
+        for i in range(n):
+            kv = key[h, i, cand]
+            order = _order_desc(kv, cand)
+            chosen = cand[order[:c]]
+            kept[h, i, chosen] = True
+            kept[h, i, alw] = True
+            if c < len(cand):
+                margin[h, i] = _rel_gap(kv[order[c - 1]], kv[order[c]])
+    return kept, margin
+
+
+def kept_lists(kept: np.ndarray):
+    """Ascending block-index lists and counts from a kept mask."""
+    H, n, nk = kept.shape
+    cnt = kept.sum(axis=-1).astype(np.int32)
+    kmax = int(cnt.max()) if cnt.size else 0
+    idx = np.full((H, n, kmax), -1, dtype=np.int32)
+    for h in range(H):
+        for i in range(n):
+            js = np.nonzero(kept[h, i])[0]
+            idx[h, i, : len(js)] = js
+    return idx, cnt
+
+
+# ---------------------------------------------------------------------------
+# Step 4: drop-set refinement (ReSS page, §4.3, Eq. 10-17)
+# ---------------------------------------------------------------------------
+
+def swap_schedule(c: int, rounds: int, rho: float):
+    """Swaps per round, Eq. 17 m_r = rho 2^-(r+1) c, rounded down."""
+    return [int(math.floor(rho * c / (2.0 ** (r + 1)))) for r in range(rounds)]
+
+
+def drop_objective(p_row, d_row, Mh, D_mask):
+    """Eq. 10 and Eq. 12 for one row and drop set D.
+
+    g = sum_{j in D} d_j, K = 1 - sum_{j in D} P_j, G = g^T M g, J = G / K^2.
+    J is +inf when K <= 0.
+    """
+    g = d_row[D_mask].sum(axis=0)
+    K = 1.0 - p_row[D_mask].sum()
+    G = float(g @ Mh @ g)
+    J = G / (K * K) if K > 0 else math.inf
+    return g, K, G, J
+
+
+def swap_gains(p_row, d, s2, Mh, g, K, G):
+    """Objective decrease of every single swap from the state (g, K, G).
+
+    Restore of k (k in D): Delta G = -2 d_k^T M g + s_k^2 (Eq. 14), u = +P_k.
+    Drop of k (k kept):    Delta G = +2 d_k^T M g + s_k^2 (Eq. 15), u = -P_k.
+    Delta J = G / K^2 - (G + Delta G) / (K + u)^2 (Eq. 16); a drop with
+    K + u <= 0 gets -inf. Both arrays cover every k; the caller masks them.
+    """
+    dMg = d @ (Mh @ g)                      # d_k^T M g for every k
+    dG_restore = -2.0 * dMg + s2
+    dG_drop = 2.0 * dMg + s2
+    dJ_restore = G / K**2 - (G + dG_restore) / (K + p_row) ** 2
+    Kd = K - p_row
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dJ_drop = np.where(Kd > 0, G / K**2 - (G + dG_drop) / Kd**2, -np.inf)
+    return dJ_restore, dJ_drop
+
+
+def _top_m(gain, members, m):
+    """Indices of the m members with the largest gain (ties: lower index),
+    and the relative gap at the cut (inf if all members are taken)."""
+    idx = np.nonzero(members)[0]
+    order = _order_desc(gain[idx], idx)
+    chosen = idx[order[:m]]
+    gap = math.inf
+    if m < len(idx):
+        gap = _rel_gap(gain[idx[order[m - 1]]], gain[idx[order[m]]])
+    return chosen, gap
+
+
+def refine_row(p_row, vpool_h, vout_row, Mh, cand, kept_row, c, rounds, rho):
+    """Iterative residual restoration of one (head, query-block) row.
+
+    Follows §4.3 of the ReSS page: start from D = P minus the initial
+    selection; each round r computes, from the round-start g, K and G, the
+    restore gain of every k in D (Eq. 13-14, u = +P_k) and the drop gain of
+    every kept candidate (Eq. 15, u = -P_k) as the exact objective decrease
+    of Eq. 16; restores the m_r blocks of D with the largest gains and drops
+    the m_r kept candidates with the largest gains (Eq. 17); then recomputes
+    g, K, G (Eq. 10, 12). The drop set with the smallest J seen is returned
+    (track-best).
+
+    Returns (best_kept_row bool [n], J_init, J_best, min_margin) where
+    min_margin is the smallest relative gap met at any selection cut or
+    track-best comparison along the way.
+    """
+    e = vout_row[None, :] - vpool_h            # e_j = vout_i - V_j
+    d = p_row[:, None] * e                      # Eq. 5
+    s2 = np.einsum("jd,de,je->j", d, Mh, d)     # (s_j)^2 = d_j^T M d_j (Eq. 6)
+    D_mask = cand & ~kept_row
+    g, K, G, J = drop_objective(p_row, d, Mh, D_mask)
+    J_init = J
+    best, J_best = D_mask.copy(), J
+    margin = math.inf
+    for m in swap_schedule(c, rounds, rho):
+        S_mask = cand & ~D_mask
+        m = min(m, int(D_mask.sum()), int(S_mask.sum()))
+        if m <= 0:
+            continue
+        dJ_restore, dJ_drop = swap_gains(p_row, d, s2, Mh, g, K, G)
+        restore, gap_r = _top_m(dJ_restore, D_mask, m)
+        drop, gap_d = _top_m(dJ_drop, S_mask, m)
+        margin = min(margin, gap_r, gap_d)
+        D_mask = D_mask.copy()
+        D_mask[restore] = False
+        D_mask[drop] = True
+        g, K, G, J = drop_objective(p_row, d, Mh, D_mask)
+        margin = min(margin, _rel_gap(J, J_best))
+        if J < J_best:
+            best, J_best = D_mask.copy(), J
+    return cand & ~best, J_init, J_best, margin
+
+
+def refine_dropset(P, vpool, vout, M, keep, always, kept, rounds, rho,
+                   rows=None):
+    """Refine every (or the listed) rows. Returns (kept', J_init, J_final,
+    margin); kept' is a copy of ``kept`` with the refined rows replaced, and
+    the per-row arrays are NaN for rows not refined."""
+    H, n, D = vpool.shape
+    cand = always == 0
+    n_alw = int((always != 0).sum())
+    out = kept.copy()
+    J0 = np.full((H, n), np.nan)
+    J1 = np.full((H, n), np.nan)
+    mg = np.full((H, n), np.nan)
+    todo = rows if rows is not None else [(h, i) for h in range(H) for i in range(n)]
+    for h, i in todo:
+        Mh = _gram(M, h, D)
+        c = int(keep[h]) - n_alw
+        kr, a, b, m = refine_row(P[h, i], vpool[h], vout[h, i], Mh, cand,
+                                 kept[h, i] & cand, c, rounds, rho)
+        out[h, i] = kr | (always != 0)
+        J0[h, i], J1[h, i], mg[h, i] = a, b, m
+    return out, J0, J1, mg
+
+
+# ---------------------------------------------------------------------------
+# Step 5: exact attention over the kept blocks (ReSS page §3 step (3))
+# ---------------------------------------------------------------------------
+
+def masked_attention(q, k, v, kept, N: int, B: int, scale: float,
+                     blocks=None):
+    """O[h, t] = sum_u softmax_u(scale q_t . k_u) v_u over the valid keys u < N
+    of the blocks kept for t's query block; softmax renormalised among them
+    (ReSS page §3: "as if the unselected blocks never existed").
+
+    q, k, v: float64 [H][N_pad][D]; kept: bool [H][n][n]. Padded query rows
+    are 0. ``blocks``: optional list of (h, i) query blocks to compute (the
+    rest stay 0). Returns (O float64 [H][N_pad][D], lse float64 [H][N_pad]).
+    """
+    H, N_pad, D = q.shape
+    n = N_pad // B
+    O = np.zeros((H, N_pad, D), dtype=np.float64)
+    lse = np.full((H, N_pad), np.nan)
+    todo = blocks if blocks is not None else [(h, i) for h in range(H) for i in range(n)]
+    for h, i in todo:
+        r0, r1 = i * B, min((i + 1) * B, N)
+        if r1 <= r0:
+            continue
+        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, N))
+                               for j in np.nonzero(kept[h, i])[0]])
+        s = scale * (q[h, r0:r1] @ k[h, keys].T)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        l = p.sum(axis=1, keepdims=True)
+        O[h, r0:r1] = (p @ v[h, keys]) / l
+        lse[h, r0:r1] = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def dense_attention(q, k, v, N: int, B: int, scale: float, blocks=None):
+    """Dense softmax attention over all valid keys: every block kept."""
+    H, N_pad, _ = q.shape
+    n = N_pad // B
+    kept = np.ones((H, n, n), dtype=bool)
+    return masked_attention(q, k, v, kept, N, B, scale, blocks)
+
+
+# ---------------------------------------------------------------------------
+# The whole selection path for one workload
+# ---------------------------------------------------------------------------
+
+def run_selection(q, k, v, N, B, keep, always, mode, rounds=0, rho=0.5,
+                  M=None, eps=1e-4, scale=None):
+    """pool -> map -> key -> top-k (-> refine) on float64 inputs.
+
+    Returns a dict with qpool, kpool, vpool, P, key, vout (drift only),
+    kept (after top-k), topk_margin, and when rounds > 0: kept_refined,
+    J_init, J_final, refine_margin.
+    """
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = {}
+    out["qpool"] = block_pool(q, N, B)
+    out["kpool"] = block_pool(k, N, B)
+    out["P"] = block_map(out["qpool"], out["kpool"], scale)
+    if mode == "drift" or rounds > 0:
+        out["vpool"] = block_pool(v, N, B)
+    if mode == "drift":
+        key, vout, qd = drift_key(out["P"], out["vpool"], M, eps)
+        out["key"], out["vout"], out["q"] = key, vout, qd
+    else:
+        out["key"] = out["P"].copy()
+    out["kept"], out["topk_margin"] = select_topk(out["key"], keep, always)
+    if rounds > 0:
+        if "vout" not in out:
+            out["vout"] = pooled_output(out["P"], out["vpool"])
+        kr, J0, J1, mg = refine_dropset(out["P"], out["vpool"], out["vout"], M,
+                                        keep, always, out["kept"], rounds, rho)
+        out["kept_refined"], out["J_init"], out["J_final"], out["refine_margin"] = (
+            kr, J0, J1, mg)
+    return out
