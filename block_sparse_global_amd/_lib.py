@@ -1,0 +1,240 @@
+"""ctypes binding of libress: the C ABI of include/ress.h, one Python function
+per entry point with the same name.
+
+This layer only marshals arguments: it checks device, dtype, contiguity and
+shape of torch tensors, passes their device pointers and the current HIP
+stream, and raises RessError on a negative status. Every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the
+library is missing, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libress.so")
+
+RESS_OK = 0
+RESS_ERR_INVALID_ARG = -1
+RESS_ERR_UNSUPPORTED = -2
+RESS_ERR_HIP = -3
+
+RESS_DTYPE_BF16 = 0
+RESS_DTYPE_F32 = 1
+RESS_SCORE_PROB = 0
+RESS_SCORE_DRIFT = 1
+RESS_MAX_BLOCKS = 4096
+
+ENTRY_POINTS = (
+    "ress_block_pool",
+    "ress_block_score",
+    "ress_select_topk",
+    "ress_refine_dropset",
+    "ress_sparse_attn_fwd",
+    "ress_last_error",
+    "ress_version",
+)
+
+
+class RessError(RuntimeError):
+    def __init__(self, func: str, code: int, msg: str):
+        super().__init__(f"{func} failed with status {code}: {msg}")
+        self.code = code
+
+
+class ress_shape(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("N_pad", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("B", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Shape:
+    H: int
+    N: int
+    N_pad: int
+    D: int
+    B: int
+
+    @property
+    def n(self) -> int:
+        return self.N_pad // self.B
+
+    def c(self) -> ress_shape:
+        return ress_shape(self.H, self.N, self.N_pad, self.D, self.B)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libress is not built ({LIB_PATH} missing); run "
+            "`python -m block_sparse_global_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, dp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.ress_block_pool.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, dp, dp, dp, vp]
+    lib.ress_block_score.argtypes = [dp, dp, dp, dp, ress_shape, ctypes.c_int,
+                                     ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, vp]
+    lib.ress_select_topk.argtypes = [dp, ress_shape, ip, vp, i32, ip, ip, vp]
+    lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
+                                        ctypes.c_double, i32, ip, ip, dp, dp, vp]
+    lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
+                                         ctypes.c_float, vp, vp, vp]
+    for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
+              "ress_refine_dropset", "ress_sparse_attn_fwd"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.ress_last_error.restype = ctypes.c_char_p
+    lib.ress_last_error.argtypes = []
+    lib.ress_version.restype = ctypes.c_int
+    lib.ress_version.argtypes = []
+    return lib
+
+
+LIB = _load()
+
+
+def _check(func: str, rc: int):
+    if rc != RESS_OK:
+        msg = LIB.ress_last_error().decode(errors="replace")
+        raise RessError(func, rc, msg)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor or None")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RESS_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return RESS_DTYPE_F32
+    raise ValueError(f"unsupported token dtype {t.dtype}")
+
+
+def _host_i32(a, name):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a.cpu() if isinstance(a, torch.Tensor) else a,
+                                          dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host_u8(a, name):
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a.cpu() if isinstance(a, torch.Tensor) else a,
+                                          dtype=np.uint8))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def ress_version() -> int:
+    return LIB.ress_version()
+
+
+def ress_last_error() -> str:
+    return LIB.ress_last_error().decode(errors="replace")
+
+
+def ress_block_pool(q, k, v, shape: Shape, qpool, kpool, vpool, stream=None):
+    ref = next(t for t in (q, k, v) if t is not None)
+    dt = _dtype_code(ref)
+    tok = (shape.H, shape.N_pad, shape.D)
+    blk = (shape.H, shape.n, shape.D)
+    _check("ress_block_pool", LIB.ress_block_pool(
+        _ptr(q, "q", ref.dtype, tok), _ptr(k, "k", ref.dtype, tok), _ptr(v, "v", ref.dtype, tok),
+        dt, shape.c(),
+        _ptr(qpool, "qpool", torch.float64, blk), _ptr(kpool, "kpool", torch.float64, blk),
+        _ptr(vpool, "vpool", torch.float64, blk), _stream(stream)))
+
+
+def ress_block_score(qpool, kpool, vpool, M, shape: Shape, mode: int, scale: float,
+                     eps: float, P, key, vout, vmv, stream=None):
+    H, n, D = shape.H, shape.n, shape.D
+    f64 = torch.float64
+    _check("ress_block_score", LIB.ress_block_score(
+        _ptr(qpool, "qpool", f64, (H, n, D)), _ptr(kpool, "kpool", f64, (H, n, D)),
+        _ptr(vpool, "vpool", f64, (H, n, D)), _ptr(M, "M", f64, (H, D, D)),
+        shape.c(), int(mode), float(scale), float(eps),
+        _ptr(P, "P", f64, (H, n, n)), _ptr(key, "key", f64, (H, n, n)),
+        _ptr(vout, "vout", f64, (H, n, D)), _ptr(vmv, "vmv", f64, (H, n)),
+        _stream(stream)))
+
+
+def ress_select_topk(key, shape: Shape, keep: Sequence[int], always_keep, k_max: int,
+                     kept_idx, kept_cnt, stream=None):
+    H, n = shape.H, shape.n
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (n,):
+        raise ValueError(f"always_keep must have shape ({n},)")
+    _check("ress_select_topk", LIB.ress_select_topk(
+        _ptr(key, "key", torch.float64, (H, n, n)), shape.c(), keep_p, alw_p,
+        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
+
+
+def ress_refine_dropset(P, vpool, vout, vmv, M, shape: Shape, keep, always_keep,
+                        rounds: int, rho: float, k_max: int, kept_idx, kept_cnt,
+                        J_init=None, J_final=None, stream=None):
+    H, n, D = shape.H, shape.n, shape.D
+    f64 = torch.float64
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (n,):
+        raise ValueError(f"always_keep must have shape ({n},)")
+    _check("ress_refine_dropset", LIB.ress_refine_dropset(
+        _ptr(P, "P", f64, (H, n, n)), _ptr(vpool, "vpool", f64, (H, n, D)),
+        _ptr(vout, "vout", f64, (H, n, D)), _ptr(vmv, "vmv", f64, (H, n)),
+        _ptr(M, "M", f64, (H, D, D)), shape.c(), keep_p, alw_p, int(rounds), float(rho),
+        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)),
+        _ptr(J_init, "J_init", f64, (H, n)), _ptr(J_final, "J_final", f64, (H, n)),
+        _stream(stream)))
+
+
+def ress_sparse_attn_fwd(q, k, v, shape: Shape, kept_idx, kept_cnt, k_max: int,
+                         scale: float, out, lse=None, stream=None):
+    dt = _dtype_code(q)
+    tok = (shape.H, shape.N_pad, shape.D)
+    H, n = shape.H, shape.n
+    _check("ress_sparse_attn_fwd", LIB.ress_sparse_attn_fwd(
+        _ptr(q, "q", q.dtype, tok), _ptr(k, "k", q.dtype, tok), _ptr(v, "v", q.dtype, tok),
+        dt, shape.c(),
+        _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)) if kept_idx is not None else None,
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)) if kept_cnt is not None else None,
+        int(k_max), float(scale), _ptr(out, "out", q.dtype, tok),
+        _ptr(lse, "lse", torch.float32, (H, shape.N_pad)), _stream(stream)))

@@ -1,0 +1,70 @@
+"""Builds libress.so in-tree with hipcc for gfx950.
+
+    python -m block_sparse_global_amd.build
+
+Every HIP source under csrc/ is compiled and linked into one shared library
+next to this file. Packed float32 VALU instructions are disabled for the
+device code (-packed-fp32-ops); the host pass prints a harmless warning that
+it does not know that feature.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libress.so")
+ROOT = os.path.dirname(HERE)
+
+SOURCES = ["api.hip", "pool.hip", "score.hip", "select.hip", "attn.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def command(out: str = LIB):
+    return [
+        hipcc(),
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-Wall",
+        "-Wno-unused-function",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"),
+        "-o", out,
+    ] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles the library (always) and returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(
+        ln for ln in (res.stderr or "").splitlines()
+        if "packed-fp32-ops" not in ln
+    )
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+    if verbose and errs.strip():
+        print(errs, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

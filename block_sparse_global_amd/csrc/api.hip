@@ -1,0 +1,277 @@
+// libress host layer: argument validation, then kernel launches on the
+// caller's stream. Validation runs before any HIP call, so every invalid
+// argument is reported without touching the device; nothing is launched on
+// error. No exception leaves this file.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "ress_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return RESS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                   \
+  do {                                                                   \
+    if ((p) == nullptr) return fail(RESS_ERR_INVALID_ARG, #p " is NULL"); \
+    if (!aligned16(p))                                                   \
+      return fail(RESS_ERR_INVALID_ARG, #p " is not 16-byte aligned");   \
+  } while (0)
+
+#define OPTIONAL_PTR(p)                                                  \
+  do {                                                                   \
+    if ((p) != nullptr && !aligned16(p))                                 \
+      return fail(RESS_ERR_INVALID_ARG, #p " is not 16-byte aligned");   \
+  } while (0)
+
+int check_shape(const ress_shape& s) {
+  if (s.H < 1) return fail(RESS_ERR_INVALID_ARG, "H=%d must be >= 1", s.H);
+  if (s.D != 64)
+    return fail(RESS_ERR_UNSUPPORTED, "D=%d: only head dimension 64", s.D);
+  if (s.B != 64 && s.B != 128)
+    return fail(RESS_ERR_UNSUPPORTED, "B=%d: block size must be 64 or 128",
+                s.B);
+  if (s.N_pad < 1 || s.N_pad % s.B != 0)
+    return fail(RESS_ERR_INVALID_ARG, "N_pad=%d is not a positive multiple of B=%d",
+                s.N_pad, s.B);
+  if (s.N < 1 || s.N > s.N_pad || s.N_pad - s.N >= s.B)
+    return fail(RESS_ERR_INVALID_ARG,
+                "N=%d must satisfy N_pad-B < N <= N_pad (N_pad=%d, B=%d)", s.N,
+                s.N_pad, s.B);
+  const int n = s.N_pad / s.B;
+  if (n > RESS_MAX_BLOCKS)
+    return fail(RESS_ERR_UNSUPPORTED, "n=%d blocks exceeds the cap of %d", n,
+                RESS_MAX_BLOCKS);
+  // element counts of the largest tensors must fit the 64-bit offsets used
+  // in the kernels; [H][n][n] maps with H*n*n < 2^40 are far inside that.
+  if ((double)s.H * n * n > 1e12)
+    return fail(RESS_ERR_UNSUPPORTED, "H*n*n too large");
+  return RESS_OK;
+}
+
+int check_dtype(int dtype) {
+  if (dtype != RESS_DTYPE_BF16 && dtype != RESS_DTYPE_F32)
+    return fail(RESS_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  return RESS_OK;
+}
+
+// Budgets and always-kept flags (host arrays) -> kernel-argument config.
+int make_sel_config(const ress_shape& s, const int32_t* keep,
+                    const uint8_t* always_keep, int32_t k_max,
+                    ress::SelConfig* cfg) {
+  if (keep == nullptr) return fail(RESS_ERR_INVALID_ARG, "keep is NULL");
+  if (s.H > RESS_MAX_SEL_HEADS)
+    return fail(RESS_ERR_UNSUPPORTED, "H=%d exceeds %d heads for selection",
+                s.H, RESS_MAX_SEL_HEADS);
+  const int n = s.N_pad / s.B;
+  memset(cfg, 0, sizeof *cfg);
+  int n_always = 0;
+  if (always_keep != nullptr) {
+    for (int j = 0; j < n; ++j) {
+      if (always_keep[j] > 1)
+        return fail(RESS_ERR_INVALID_ARG, "always_keep[%d]=%d is not 0 or 1",
+                    j, always_keep[j]);
+      if (always_keep[j]) {
+        cfg->always_bits[j >> 6] |= 1ull << (j & 63);
+        ++n_always;
+      }
+    }
+  }
+  cfg->n_always = n_always;
+  int kmax_needed = 0;
+  for (int h = 0; h < s.H; ++h) {
+    const int k = keep[h];
+    if (k < 2 || k > n)
+      return fail(RESS_ERR_INVALID_ARG, "keep[%d]=%d must lie in [2, n=%d]", h,
+                  k, n);
+    if (k <= n_always)
+      return fail(RESS_ERR_INVALID_ARG,
+                  "keep[%d]=%d must exceed the %d always-kept blocks", h, k,
+                  n_always);
+    cfg->keep[h] = k;
+    if (k > kmax_needed) kmax_needed = k;
+  }
+  if (k_max < kmax_needed || k_max > n)
+    return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [max keep=%d, n=%d]",
+                k_max, kmax_needed, n);
+  return RESS_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(RESS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ress_version(void) { return RESS_VERSION; }
+
+const char* ress_last_error(void) { return g_err.c_str(); }
+
+int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
+                    ress_shape shape, double* qpool, double* kpool,
+                    double* vpool, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_dtype(dtype)) != RESS_OK) return rc;
+  const void* in[3] = {q, k, v};
+  double* out[3] = {qpool, kpool, vpool};
+  const char* names[3] = {"q/qpool", "k/kpool", "v/vpool"};
+  int given = 0;
+  for (int a = 0; a < 3; ++a) {
+    if ((in[a] == nullptr) != (out[a] == nullptr))
+      return fail(RESS_ERR_INVALID_ARG, "%s: input and output must both be given or both be NULL",
+                  names[a]);
+    if (in[a] != nullptr) {
+      if (!aligned16(in[a]) || !aligned16(out[a]))
+        return fail(RESS_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", names[a]);
+      ++given;
+    }
+  }
+  if (given == 0) return fail(RESS_ERR_INVALID_ARG, "nothing to pool");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int a = 0; a < 3; ++a) {
+    if (in[a] == nullptr) continue;
+    hipError_t e = ress::launch_block_pool(in[a], dtype, shape, out[a], st);
+    if (e != hipSuccess) return hip_status(e, "block_pool launch");
+  }
+  return ok();
+}
+
+int ress_block_score(const double* qpool, const double* kpool,
+                     const double* vpool, const double* M, ress_shape shape,
+                     int mode, double scale, double eps, double* P,
+                     double* key, double* vout, double* vmv, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if (mode != RESS_SCORE_PROB && mode != RESS_SCORE_DRIFT)
+    return fail(RESS_ERR_INVALID_ARG, "bad score mode %d", mode);
+  if (!(scale > 0.0) || !isfinite(scale))
+    return fail(RESS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE_PTR(qpool);
+  REQUIRE_PTR(kpool);
+  REQUIRE_PTR(P);
+  OPTIONAL_PTR(key);
+  if (mode == RESS_SCORE_DRIFT) {
+    if (!(eps > 0.0) || !isfinite(eps))
+      return fail(RESS_ERR_INVALID_ARG, "eps must be finite and > 0");
+    REQUIRE_PTR(vpool);
+    REQUIRE_PTR(key);
+    REQUIRE_PTR(vout);
+    REQUIRE_PTR(vmv);
+    OPTIONAL_PTR(M);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ress::launch_block_map(qpool, kpool, shape, scale, P, st);
+  if (e != hipSuccess) return hip_status(e, "block_map launch");
+  const int n = shape.N_pad / shape.B;
+  if (mode == RESS_SCORE_PROB) {
+    if (key != nullptr && key != P) {
+      e = ress::launch_copy(P, key, (size_t)shape.H * n * n, st);
+      if (e != hipSuccess) return hip_status(e, "copy launch");
+    }
+    return ok();
+  }
+  e = ress::launch_vmv(vpool, M, shape, vmv, st);
+  if (e != hipSuccess) return hip_status(e, "vmv launch");
+  e = ress::launch_drift(P, vpool, M, vmv, shape, eps, key, vout, st);
+  if (e != hipSuccess) return hip_status(e, "drift launch");
+  return ok();
+}
+
+int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
+                     const uint8_t* always_keep, int32_t k_max,
+                     int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  REQUIRE_PTR(key);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK)
+    return rc;
+  hipError_t e = ress::launch_topk(key, shape, cfg, k_max, kept_idx, kept_cnt,
+                                   static_cast<hipStream_t>(stream));
+  return hip_status(e, "topk launch");
+}
+
+int ress_refine_dropset(const double* P, const double* vpool,
+                        const double* vout, const double* vmv, const double* M,
+                        ress_shape shape, const int32_t* keep,
+                        const uint8_t* always_keep, int32_t rounds, double rho,
+                        int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
+                        double* J_init, double* J_final, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(vpool);
+  REQUIRE_PTR(vout);
+  REQUIRE_PTR(vmv);
+  OPTIONAL_PTR(M);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  OPTIONAL_PTR(J_init);
+  OPTIONAL_PTR(J_final);
+  if (rounds < 0) return fail(RESS_ERR_INVALID_ARG, "rounds=%d < 0", rounds);
+  if (!(rho > 0.0 && rho <= 1.0))
+    return fail(RESS_ERR_INVALID_ARG, "rho must lie in (0, 1]");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK)
+    return rc;
+  hipError_t e = ress::launch_refine(P, vpool, vout, vmv, M, shape, cfg, rounds,
+                                     rho, k_max, kept_idx, kept_cnt, J_init,
+                                     J_final, static_cast<hipStream_t>(stream));
+  return hip_status(e, "refine launch");
+}
+
+int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                         int dtype, ress_shape shape, const int32_t* kept_idx,
+                         const int32_t* kept_cnt, int32_t k_max, float scale,
+                         void* out, float* lse, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_dtype(dtype)) != RESS_OK) return rc;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  OPTIONAL_PTR(lse);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RESS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (kept_idx != nullptr) {
+    REQUIRE_PTR(kept_cnt);
+    const int n = shape.N_pad / shape.B;
+    if (k_max < 1 || k_max > n)
+      return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [1, n=%d]", k_max, n);
+  }
+  hipError_t e = ress::launch_attn(q, k, v, dtype, shape, kept_idx, kept_cnt,
+                                   k_max, scale, out, lse,
+                                   static_cast<hipStream_t>(stream));
+  return hip_status(e, "attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the libress kernels and its host layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ress.h"
+
+namespace ress {
+
+// Always-kept key blocks as a bitmask (n <= 4096 -> 64 words) and per-head
+// keep budgets; small enough to travel in the kernel arguments, so the
+// selection kernels need no extra device memory.
+struct SelConfig {
+  uint64_t always_bits[RESS_MAX_BLOCKS / 64];
+  int32_t keep[RESS_MAX_SEL_HEADS];
+  int32_t n_always;
+};
+
+__host__ __device__ inline bool sel_always(const SelConfig& c, int j) {
+  return (c.always_bits[j >> 6] >> (j & 63)) & 1ull;
+}
+
+// Launchers (defined next to their kernels). Each returns hipGetLastError()
+// of its launches.
+hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
+                             double* out, hipStream_t st);
+
+hipError_t launch_block_map(const double* qpool, const double* kpool,
+                            const ress_shape& s, double scale, double* P,
+                            hipStream_t st);
+
+hipError_t launch_copy(const double* src, double* dst, size_t count,
+                       hipStream_t st);
+
+hipError_t launch_vmv(const double* vpool, const double* M,
+                      const ress_shape& s, double* vmv, hipStream_t st);
+
+hipError_t launch_drift(const double* P, const double* vpool, const double* M,
+                        const double* vmv, const ress_shape& s, double eps,
+                        double* key, double* vout, hipStream_t st);
+
+hipError_t launch_topk(const double* key, const ress_shape& s,
+                       const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,
+                       int32_t* kept_cnt, hipStream_t st);
+
+hipError_t launch_refine(const double* P, const double* vpool,
+                         const double* vout, const double* vmv,
+                         const double* M, const ress_shape& s,
+                         const SelConfig& cfg, int32_t rounds, double rho,
+                         int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
+                         double* J_init, double* J_final, hipStream_t st);
+
+hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
+                       const ress_shape& s, const int32_t* kept_idx,
+                       const int32_t* kept_cnt, int32_t k_max, float scale,
+                       void* out, float* lse, hipStream_t st);
+
+}  // namespace ress

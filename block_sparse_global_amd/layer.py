@@ -1,0 +1,113 @@
+"""The whole block-sparse global-attention step over the C ABI.
+
+``BlockSparseGlobalAttention`` owns the device buffers of one workload shape
+(allocated once with torch) and runs pool -> score -> top-k -> [refine] ->
+sparse attention as five library calls on one stream. It only allocates and
+sequences; every step is a libress kernel.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._lib import (
+    RESS_SCORE_DRIFT,
+    RESS_SCORE_PROB,
+    Shape,
+    ress_block_pool,
+    ress_block_score,
+    ress_refine_dropset,
+    ress_select_topk,
+    ress_sparse_attn_fwd,
+)
+
+
+class BlockSparseGlobalAttention:
+    def __init__(self, shape: Shape, keep, always_keep, mode: str = "prob",
+                 rounds: int = 0, rho: float = 0.5, eps: float = 1e-4,
+                 scale: Optional[float] = None, M: Optional[torch.Tensor] = None,
+                 device="cuda", with_lse: bool = False):
+        if mode not in ("prob", "drift"):
+            raise ValueError(mode)
+        if rounds > 0 and mode != "drift":
+            raise ValueError("refinement rounds need the drift-mode score outputs")
+        self.shape = shape
+        self.keep = np.ascontiguousarray(np.asarray(keep, dtype=np.int32))
+        self.always = (None if always_keep is None
+                       else np.ascontiguousarray(np.asarray(always_keep, dtype=np.uint8)))
+        self.mode = mode
+        self.rounds = int(rounds)
+        self.rho = float(rho)
+        self.eps = float(eps)
+        self.scale = float(scale if scale is not None else 1.0 / math.sqrt(shape.D))
+        self.M = M
+        self.k_max = int(self.keep.max())
+        H, n, D, Np = shape.H, shape.n, shape.D, shape.N_pad
+        f64 = dict(dtype=torch.float64, device=device)
+        self.qpool = torch.empty((H, n, D), **f64)
+        self.kpool = torch.empty((H, n, D), **f64)
+        need_v = mode == "drift"
+        self.vpool = torch.empty((H, n, D), **f64) if need_v else None
+        self.P = torch.empty((H, n, n), **f64)
+        self.key = torch.empty((H, n, n), **f64) if mode == "drift" else None
+        self.vout = torch.empty((H, n, D), **f64) if need_v else None
+        self.vmv = torch.empty((H, n), **f64) if need_v else None
+        self.kept_idx = torch.empty((H, n, self.k_max), dtype=torch.int32, device=device)
+        self.kept_cnt = torch.empty((H, n), dtype=torch.int32, device=device)
+        self.J_init = torch.empty((H, n), **f64) if rounds > 0 else None
+        self.J_final = torch.empty((H, n), **f64) if rounds > 0 else None
+        self.lse = (torch.empty((H, Np), dtype=torch.float32, device=device)
+                    if with_lse else None)
+        self.out = None
+
+    # -- the five steps -------------------------------------------------------
+    def pool(self, q, k, v, stream=None):
+        ress_block_pool(q, k, v if self.vpool is not None else None, self.shape,
+                        self.qpool, self.kpool, self.vpool, stream)
+
+    def score(self, stream=None):
+        mode = RESS_SCORE_DRIFT if self.mode == "drift" else RESS_SCORE_PROB
+        ress_block_score(self.qpool, self.kpool, self.vpool, self.M, self.shape, mode,
+                         self.scale, self.eps, self.P, self.key, self.vout, self.vmv,
+                         stream)
+
+    def select(self, stream=None):
+        key = self.key if self.key is not None else self.P
+        ress_select_topk(key, self.shape, self.keep, self.always, self.k_max,
+                         self.kept_idx, self.kept_cnt, stream)
+
+    def refine(self, stream=None):
+        if self.rounds <= 0:
+            return
+        ress_refine_dropset(self.P, self.vpool, self.vout, self.vmv, self.M, self.shape,
+                            self.keep, self.always, self.rounds, self.rho, self.k_max,
+                            self.kept_idx, self.kept_cnt, self.J_init, self.J_final,
+                            stream)
+
+    def attend(self, q, k, v, out, stream=None):
+        ress_sparse_attn_fwd(q, k, v, self.shape, self.kept_idx, self.kept_cnt,
+                             self.k_max, self.scale, out, self.lse, stream)
+
+    def __call__(self, q, k, v, out=None, stream=None):
+        if out is None:
+            if self.out is None or self.out.dtype != q.dtype:
+                self.out = torch.empty_like(q)
+            out = self.out
+        self.pool(q, k, v, stream)
+        self.score(stream)
+        self.select(stream)
+        self.refine(stream)
+        self.attend(q, k, v, out, stream)
+        return out
+
+
+def dense_attention(q, k, v, shape: Shape, out, scale: Optional[float] = None,
+                    lse=None, stream=None):
+    """Dense global attention through the same kernel (every block kept)."""
+    s = float(scale if scale is not None else 1.0 / math.sqrt(shape.D))
+    ress_sparse_attn_fwd(q, k, v, shape, None, None, 1, s, out, lse, stream)
+    return out

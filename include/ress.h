@@ -1,0 +1,200 @@
+/*
+ * ress.h — C ABI of libress, block-sparse global attention for MI355X (gfx950).
+ *
+ * The operation is the three-step block-sparse attention of multi-view
+ * geometry transformers as described in "ReSS: Residual-Restoring Sparse
+ * Attention for 3D Vision Transformers", §3 "Block-Sparse Attention for 3D
+ * ViTs": (1) Q and K are mean pooled per block into a coarse block-level
+ * attention map; (2) per (query block, head) key blocks are selected up to a
+ * per-head budget, blocks holding special tokens always kept; (3) exact
+ * attention runs over the selected blocks only, with the softmax
+ * renormalised among them. The subject of those pages, "Block-Sparse Global
+ * Attention for Efficient Multi-View Geometry Transformers" (abstract), is
+ * the training-free form of this with probability-based selection; the ReSS
+ * page adds the drift score (§4.2) and drop-set refinement (§4.3).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor layout: head-major, row-major, contiguous. Token tensors are
+ *    [H][N_pad][D]; block tensors [H][n][D]; block maps [H][n][n], where
+ *    n = N_pad / B and tokens t >= N are padding (ignored as keys, written
+ *    as zero rows of the attention output).
+ *  - D must be 64; B must be 64 or 128; n must be <= 4096.
+ *  - Pointers named "device" are caller-owned device memory on the current
+ *    HIP device, 16-byte aligned, and must not alias one another. Arrays
+ *    named "host" are read on the host during the call and not retained.
+ *  - stream: a hipStream_t (NULL = the null stream). Every call only
+ *    enqueues work on it and returns; outputs are valid once the stream has
+ *    been synchronised. The library never synchronises and allocates no
+ *    memory; it keeps no state between calls except a cached record of the
+ *    device properties.
+ *  - Errors: every argument is validated on the host before any HIP call.
+ *    On error nothing is launched, a negative status is returned and a
+ *    message is available from ress_last_error() (thread-local). No C++
+ *    exception crosses this interface. NaN or Inf inputs give unspecified
+ *    (but memory-safe) outputs.
+ */
+#ifndef RESS_H
+#define RESS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RESS_VERSION 1
+
+/* Status codes. */
+#define RESS_OK 0
+#define RESS_ERR_INVALID_ARG -1 /* a bad pointer, size, budget or enum   */
+#define RESS_ERR_UNSUPPORTED -2 /* valid but outside what is implemented */
+#define RESS_ERR_HIP -3         /* a HIP runtime or launch error         */
+
+/* Element types of Q, K, V (and of the attention output). */
+#define RESS_DTYPE_BF16 0
+#define RESS_DTYPE_F32 1
+
+/* Block scores. */
+#define RESS_SCORE_PROB 0  /* pooled attention probability             */
+#define RESS_SCORE_DRIFT 1 /* ReSS drift key, Eq. 7 of the ReSS page   */
+
+/* Largest supported number of blocks per row (n). */
+#define RESS_MAX_BLOCKS 4096
+/* Largest number of heads accepted by the selection calls, whose per-head
+ * budgets travel in the kernel arguments. */
+#define RESS_MAX_SEL_HEADS 64
+
+typedef struct ress_shape {
+  int32_t H;     /* heads                                     */
+  int32_t N;     /* valid tokens, 1 <= N <= N_pad             */
+  int32_t N_pad; /* padded length, a multiple of B, N_pad-N<B */
+  int32_t D;     /* head dimension, must be 64                */
+  int32_t B;     /* block size (query and key), 64 or 128     */
+} ress_shape;
+
+/*
+ * ress_block_pool — mean pooling per block ("ReSS" page, §3 step (1)).
+ *
+ *   xpool[h][b][:] = mean of x[h][t][:] over the valid tokens t < N of block b
+ *
+ * q, k, v: device [H][N_pad][D] of `dtype`. Each of the three (input,
+ * output) pairs is either both non-NULL or both NULL; at least one pair is
+ * given. qpool, kpool, vpool: device float64 [H][n][D]. Accumulation is in
+ * float64.
+ */
+int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
+                    ress_shape shape, double* qpool, double* kpool,
+                    double* vpool, void* stream);
+
+/*
+ * ress_block_score — pooled block map and per-block ranking key.
+ *
+ *   P[h][i][j] = softmax over all j of scale * qpool[h][i] . kpool[h][j]
+ *     ("ReSS" page §4.1: the map is normalised over all key blocks).
+ *
+ * mode RESS_SCORE_PROB: the ranking key is P itself (SparseVGGT/HeSS as
+ *   described on the ReSS page, §3). `key` may be NULL (then rank by P);
+ *   vpool, M, vout and vmv are ignored.
+ * mode RESS_SCORE_DRIFT (ReSS page §4.2, Eq. 1 and 5-9):
+ *   vout[h][i]  = sum_j P[h][i][j] vpool[h][j]                      (Eq. 1)
+ *   vmv[h][j]   = vpool[h][j]^T M_h vpool[h][j]
+ *   q_ij        = vout_i^T M vout_i - 2 vout_i^T M V_j + vmv_j      (Eq. 9)
+ *   key[h][i][j] = P_ij sqrt(max(q_ij, 0)) / max(1 - P_ij, eps)     (Eq. 6-7)
+ *   with M_h = I when M is NULL, else M: device float64 [H][D][D], symmetric
+ *   (a Gram matrix W_O^T W_O, Eq. 8). vpool, key, vout, vmv are required.
+ *
+ * qpool, kpool, vpool: device float64 [H][n][D]. P, key: device float64
+ * [H][n][n]. vout: device float64 [H][n][D]. vmv: device float64 [H][n].
+ * scale > 0 (1/sqrt(D) is the usual value); eps > 0 (1e-4 on the page).
+ */
+int ress_block_score(const double* qpool, const double* kpool,
+                     const double* vpool, const double* M, ress_shape shape,
+                     int mode, double scale, double eps, double* P,
+                     double* key, double* vout, double* vmv, void* stream);
+
+/*
+ * ress_select_topk — per (head, query-block row) keep set (ReSS page §3 step
+ * (2), §4.1 Eq. 2 with |S| = c_h, §4.4 "Sparsity control").
+ *
+ * Candidates are the key blocks j with always_keep[j] == 0. Per row of head
+ * h, the c_h = keep[h] - |always| candidates with the largest key are kept
+ * (equal keys: the lower block index wins), together with every always-kept
+ * block. kept_idx[h][i][0 .. keep[h]-1] receives the kept block indices in
+ * ascending order and the rest of the row (up to k_max) is set to -1;
+ * kept_cnt[h][i] = keep[h].
+ *
+ * key: device float64 [H][n][n]. keep: HOST int32 [H], each
+ * 2 <= keep[h] <= n and keep[h] > |always|. always_keep: HOST uint8 [n] or
+ * NULL (no always-kept blocks). k_max >= max_h keep[h]. kept_idx: device
+ * int32 [H][n][k_max]. kept_cnt: device int32 [H][n]. H <= 64.
+ */
+int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
+                     const uint8_t* always_keep, int32_t k_max,
+                     int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
+ * ress_refine_dropset — ReSS iterative residual restoration (ReSS page
+ * §4.3, Eq. 10-17), applied to the keep sets from ress_select_topk.
+ *
+ * Per row, with D = candidates not kept: g = sum_{j in D} P_j (vout - V_j),
+ * K = 1 - sum_{j in D} P_j, G = g^T M g, J = G / K^2 (Eq. 10, 12). Round r
+ * (r < rounds) swaps m_r = floor(rho c / 2^(r+1)) blocks (Eq. 17): from the
+ * round-start g, K, G it computes the exact objective decrease (Eq. 16) of
+ * restoring each k in D (Eq. 13-14) and of dropping each kept candidate
+ * (Eq. 15; a drop with K + u <= 0 counts as -inf), restores the m_r best
+ * restores and drops the m_r best drops (ties: lower index), then recomputes
+ * g, K, G. The set with the smallest J seen (strictly smaller replaces) is
+ * written back to kept_idx / kept_cnt in the same format as the top-k call.
+ *
+ * P: device float64 [H][n][n]; vpool, vout: device float64 [H][n][D];
+ * vmv: device float64 [H][n] (all three as written by ress_block_score in
+ * drift mode with the same M). M: device float64 [H][D][D] or NULL (= I).
+ * keep, always_keep: HOST, as for ress_select_topk. rounds >= 0,
+ * 0 < rho <= 1. kept_idx, kept_cnt: device, in/out. J_init, J_final: device
+ * float64 [H][n] or NULL. H <= 64.
+ */
+int ress_refine_dropset(const double* P, const double* vpool,
+                        const double* vout, const double* vmv, const double* M,
+                        ress_shape shape, const int32_t* keep,
+                        const uint8_t* always_keep, int32_t rounds, double rho,
+                        int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
+                        double* J_init, double* J_final, void* stream);
+
+/*
+ * ress_sparse_attn_fwd — exact attention over the kept key blocks (ReSS page
+ * §3 step (3): softmax renormalised among the selected blocks, "as if the
+ * unselected blocks never existed"; dense global attention when kept_idx is
+ * NULL).
+ *
+ *   out[h][t] = sum_u softmax_u(scale q[h][t] . k[h][u]) v[h][u]
+ *
+ * over the valid keys u < N of the blocks kept_idx[h][i][0 .. kept_cnt-1]
+ * of t's query block i. QK^T and PV run on bf16 matrix cores with float32
+ * accumulation and a float32 online softmax; float32 inputs are rounded to
+ * bf16 (nearest-even) when staged. Rows t >= N are written as zeros.
+ *
+ * q, k, v: device [H][N_pad][D] of `dtype`. kept_idx: device int32
+ * [H][n][k_max] or NULL (dense); entries outside [0, n) are skipped.
+ * kept_cnt: device int32 [H][n], required with kept_idx (values are clamped
+ * to [0, k_max]; a row with nothing kept is written as zeros). out: device
+ * [H][N_pad][D] of `dtype`. lse: device float32 [H][N_pad] or NULL; it
+ * receives log sum_u exp(scale q . k_u) (natural log; -inf for an empty
+ * row, 0 for padded rows). scale > 0.
+ */
+int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                         int dtype, ress_shape shape, const int32_t* kept_idx,
+                         const int32_t* kept_cnt, int32_t k_max, float scale,
+                         void* out, float* lse, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* ress_last_error(void);
+
+/* RESS_VERSION of the built library. */
+int ress_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RESS_H */

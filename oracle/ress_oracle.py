@@ -107,7 +107,8 @@ def drift_key(P: np.ndarray, vpool: np.ndarray, M: Optional[np.ndarray],
         for i0 in range(0, n, row_chunk):
             i1 = min(n, i0 + row_chunk)
             e = vout[h, i0:i1, None, :] - vpool[h, None, :, :]  # [ci][n][D]
-            q[h, i0:i1] = np.sum(np.matmul(e, Mh) * e, axis=-1)
+            Me = e if M is None else np.matmul(e, Mh)          # M_h = I: e itself
+            q[h, i0:i1] = np.sum(Me * e, axis=-1)
     q = np.maximum(q, 0.0)
     s = P * np.sqrt(q)
     key = s / np.maximum(1.0 - P, eps)

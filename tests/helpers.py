@@ -1,0 +1,99 @@
+"""Shared helpers of the parity tests: inputs on both sides, comparisons."""
+
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+
+import synth
+
+
+def to_torch_tokens(x: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(x)
+    return t.to(device).contiguous()
+
+
+@functools.lru_cache(maxsize=2)
+def case_inputs(name: str):
+    w = synth.get_workload(name)
+    x = synth.make_inputs(w)
+    return w, x
+
+
+def f64(x, w):
+    return synth.as_f64(x, w.dtype)
+
+
+def kept_mask_from_lists(idx: np.ndarray, cnt: np.ndarray, n: int) -> np.ndarray:
+    H, nq, _ = idx.shape
+    m = np.zeros((H, nq, n), dtype=bool)
+    for h in range(H):
+        for i in range(nq):
+            js = idx[h, i, : cnt[h, i]]
+            m[h, i, js] = True
+    return m
+
+
+def check_lists_wellformed(idx: np.ndarray, cnt: np.ndarray, keep, always, n: int):
+    """Counts equal the budgets, lists ascending and in range, -1 padded,
+    always-kept blocks present."""
+    H, nq, kmax = idx.shape
+    alw = np.nonzero(np.asarray(always))[0] if always is not None else np.array([], int)
+    for h in range(H):
+        assert np.all(cnt[h] == keep[h]), f"head {h}: counts {np.unique(cnt[h])} != {keep[h]}"
+        rows = idx[h, :, : keep[h]]
+        assert np.all(rows >= 0) and np.all(rows < n)
+        assert np.all(np.diff(rows, axis=1) > 0), "lists must be strictly ascending"
+        assert np.all(idx[h, :, keep[h]:] == -1)
+        for j in alw:
+            assert np.all(np.any(rows == j, axis=1)), f"always-kept block {j} missing"
+
+
+def compare_masks(gpu: np.ndarray, ref: np.ndarray, key: np.ndarray, always,
+                  keep, rel: float = 1e-6):
+    """Keep sets must be equal; where a row differs, every block in the
+    symmetric difference must carry an oracle key within `rel` (relative) of
+    the oracle's cut value (the c-th largest candidate key) — a near-tie.
+    Returns the number of rows that differ (all of them near-ties)."""
+    H, nq, n = gpu.shape
+    cand = (np.asarray(always) == 0) if always is not None else np.ones(n, bool)
+    n_alw = n - int(cand.sum())
+    differ = np.nonzero(np.any(gpu != ref, axis=-1))
+    for h, i in zip(*differ):
+        c = int(keep[h]) - n_alw
+        kv = key[h, i, cand]
+        cut = np.sort(kv)[::-1][c - 1]
+        sym = np.nonzero(gpu[h, i] != ref[h, i])[0]
+        for j in sym:
+            assert cand[j], f"row ({h},{i}): always-kept block {j} differs"
+            gap = abs(key[h, i, j] - cut) / max(abs(cut), 1e-300)
+            assert gap <= rel, (f"row ({h},{i}) block {j}: key {key[h, i, j]!r} vs cut "
+                                f"{cut!r} (rel gap {gap:.3e}) is not a near-tie")
+    return len(differ[0])
+
+
+def attn_errors(gpu: np.ndarray, ref: np.ndarray):
+    d = np.abs(gpu.astype(np.float64) - ref)
+    return float(d.max()), float(d.mean()), float(np.abs(ref).max())
+
+
+def sample_blocks(H: int, n: int, count: int, seed: int = 0, must=()):
+    """Distinct (h, i) query blocks: the listed ones, the last block of each
+    head (holds the padding), then random ones."""
+    rng = np.random.default_rng(seed)
+    picks = set(tuple(m) for m in must)
+    for h in range(H):
+        picks.add((h, n - 1))
+    while len(picks) < min(count, H * n):
+        picks.add((int(rng.integers(H)), int(rng.integers(n))))
+    return sorted(picks)
+
+
+def row_rms(x: np.ndarray) -> float:
+    return float(math.sqrt(np.mean(np.square(x))))

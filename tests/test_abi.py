@@ -1,0 +1,159 @@
+"""The C-ABI library on the CPU host: it loads, exports every entry point the
+header declares, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ress.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ress_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
+              "ress_refine_dropset", "ress_sparse_attn_fwd", "ress_last_error",
+              "ress_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    import block_sparse_global_amd as b
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), f"{f} declared in ress.h but not exported"
+    assert b.ress_version() == 1
+    assert set(b.ENTRY_POINTS) == set(declared_functions())
+
+
+def _shape(H=2, N=256, N_pad=256, D=64, B=64):
+    import block_sparse_global_amd as b
+    return b.Shape(H, N, N_pad, D, B).c()
+
+
+FAKE = ctypes.c_void_p(0x1000)        # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x1008)
+
+
+@pytest.mark.parametrize("shape,code,msg", [
+    (dict(D=32), -2, "head dimension"),
+    (dict(B=32), -2, "block size"),
+    (dict(H=0), -1, "H="),
+    (dict(N_pad=250), -1, "multiple"),
+    (dict(N=100), -1, "N="),
+    (dict(N=300), -1, "N="),
+    (dict(N=4097 * 64, N_pad=4097 * 64), -2, "cap"),
+])
+def test_attention_rejects_bad_shapes(shape, code, msg):
+    import block_sparse_global_amd as b
+    rc = b.LIB.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, _shape(**shape), None, None, 1,
+                                    ctypes.c_float(0.125), FAKE, None, None)
+    assert rc == code
+    assert msg in b.ress_last_error()
+
+
+def test_attention_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape()
+    f = ctypes.c_float(0.125)
+    assert L.ress_sparse_attn_fwd(None, FAKE, FAKE, 0, s, None, None, 1, f, FAKE, None, None) == -1
+    assert L.ress_sparse_attn_fwd(MISALIGNED, FAKE, FAKE, 0, s, None, None, 1, f, FAKE, None, None) == -1
+    assert "aligned" in b.ress_last_error()
+    assert L.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 7, s, None, None, 1, f, FAKE, None, None) == -1
+    assert L.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, s, None, None, 1, ctypes.c_float(0.0),
+                                  FAKE, None, None) == -1
+    # kept lists need counts and a sane k_max
+    assert L.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, s, FAKE, None, 1, f, FAKE, None, None) == -1
+    assert L.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, s, FAKE, FAKE, 0, f, FAKE, None, None) == -1
+    assert L.ress_sparse_attn_fwd(FAKE, FAKE, FAKE, 0, s, FAKE, FAKE, 5, f, FAKE, None, None) == -1
+
+
+def test_pool_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape()
+    assert L.ress_block_pool(None, None, None, 0, s, None, None, None, None) == -1
+    assert L.ress_block_pool(FAKE, None, None, 0, s, None, None, None, None) == -1
+    assert "both" in b.ress_last_error()
+    assert L.ress_block_pool(FAKE, None, None, 3, s, FAKE, None, None, None) == -1
+
+
+def test_score_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape()
+    d = ctypes.c_double
+    assert L.ress_block_score(FAKE, FAKE, None, None, s, 2, d(0.1), d(1e-4), FAKE, None, None,
+                              None, None) == -1
+    assert L.ress_block_score(FAKE, FAKE, None, None, s, 0, d(-1), d(1e-4), FAKE, None, None,
+                              None, None) == -1
+    # drift needs vpool, key, vout, vmv and eps > 0
+    assert L.ress_block_score(FAKE, FAKE, None, None, s, 1, d(0.1), d(1e-4), FAKE, FAKE, FAKE,
+                              FAKE, None) == -1
+    assert L.ress_block_score(FAKE, FAKE, FAKE, None, s, 1, d(0.1), d(0.0), FAKE, FAKE, FAKE,
+                              FAKE, None) == -1
+    assert L.ress_block_score(FAKE, FAKE, FAKE, MISALIGNED, s, 1, d(0.1), d(1e-4), FAKE, FAKE,
+                              FAKE, FAKE, None) == -1
+
+
+def _arr(a, t):
+    a = np.ascontiguousarray(np.asarray(a, dtype=t))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_selection_budget_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape(H=2)           # n = 4
+    _, ok_keep = _arr([2, 3], np.int32)
+    _, alw = _arr([0, 0, 0, 1], np.uint8)
+    assert L.ress_select_topk(FAKE, s, None, None, 3, FAKE, FAKE, None) == -1      # keep NULL
+    _, low = _arr([1, 3], np.int32)
+    assert L.ress_select_topk(FAKE, s, low, None, 3, FAKE, FAKE, None) == -1       # keep < 2
+    _, high = _arr([2, 5], np.int32)
+    assert L.ress_select_topk(FAKE, s, high, None, 5, FAKE, FAKE, None) == -1      # keep > n
+    assert L.ress_select_topk(FAKE, s, ok_keep, None, 2, FAKE, FAKE, None) == -1   # k_max < keep
+    _, alw3 = _arr([1, 1, 1, 0], np.uint8)
+    assert L.ress_select_topk(FAKE, s, ok_keep, alw3, 3, FAKE, FAKE, None) == -1   # keep <= always
+    _, bad = _arr([0, 2, 0, 0], np.uint8)
+    assert L.ress_select_topk(FAKE, s, ok_keep, bad, 3, FAKE, FAKE, None) == -1    # flag not 0/1
+    big = _shape(H=65)
+    _, k65 = _arr([2] * 65, np.int32)
+    assert L.ress_select_topk(FAKE, big, k65, None, 2, FAKE, FAKE, None) == -2     # too many heads
+    d = ctypes.c_double
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, -1, d(0.5), 3,
+                                 FAKE, FAKE, None, None, None) == -1               # rounds < 0
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(1.5), 3,
+                                 FAKE, FAKE, None, None, None) == -1               # rho > 1
+    assert L.ress_refine_dropset(FAKE, FAKE, None, FAKE, None, s, ok_keep, alw, 2, d(0.5), 3,
+                                 FAKE, FAKE, None, None, None) == -1               # vout NULL
+
+
+def test_error_string_is_cleared_per_thread():
+    import threading
+    import block_sparse_global_amd as b
+    b.LIB.ress_block_pool(None, None, None, 0, _shape(D=32), None, None, None, None)
+    assert b.ress_last_error()
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(b.ress_last_error()))
+    th.start(); th.join()
+    assert seen == [""]
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    import block_sparse_global_amd as b
+    shape = b.Shape(1, 128, 128, 64, 64)
+    x = torch.zeros((1, 128, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        b.ress_sparse_attn_fwd(x, x, x, shape, None, None, 1, 0.125, x)

@@ -1,0 +1,338 @@
+"""GPU parity: every libress entry point against the CPU oracle.
+
+Run on an MI355X: ``python -m pytest tests -m gpu``. Each workload runs the
+whole path on the GPU once (pool -> score -> top-k -> [refine] -> attention),
+and each stage is compared with the oracle on the same seeded inputs:
+
+* pooled blocks, pooled map P, drift keys and pooled outputs: float64,
+  relative 1e-12 (1e-10 for the drift key, whose GPU form is the Eq. 9
+  expansion while the oracle uses the direct form);
+* keep sets: bit-exact except near-ties (oracle keys within 1e-6 relative of
+  the row's cut);
+* refinement: started from the GPU's top-k sets; sets equal unless the
+  oracle logged a near-tie (< 1e-6 relative) on the row's trajectory, in
+  which case the GPU's J_final must equal the oracle's J of the GPU's set;
+* attention: with the GPU's kept lists, max-abs <= 2e-2 and mean-abs <= 2e-3
+  (bf16 inputs, float32 accumulation), and rms error <= 2^-7 of the rms output.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import custom
+from tests.helpers import (
+    attn_errors,
+    case_inputs,
+    check_lists_wellformed,
+    compare_masks,
+    f64,
+    kept_mask_from_lists,
+    sample_blocks,
+    to_torch_tokens,
+)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, REL_RMS = 2e-2, 2e-3, 2.0 ** -7
+
+
+def _lib():
+    import block_sparse_global_amd as b
+    return b
+
+
+def run_gpu(w, x, mode, M=None, stream=None, blocks_out=True):
+    """The whole step on the GPU; every intermediate copied to the host."""
+    b = _lib()
+    shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+    rounds = w.rounds if mode == "drift" else 0
+    Mt = torch.from_numpy(M).cuda() if M is not None else None
+    layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
+                                         rounds=rounds, rho=w.rho, M=Mt, with_lse=True)
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    layer.pool(q, k, v, stream)
+    layer.score(stream)
+    layer.select(stream)
+    torch.cuda.synchronize()
+    res = {
+        "qpool": layer.qpool.cpu().numpy(), "kpool": layer.kpool.cpu().numpy(),
+        "P": layer.P.cpu().numpy(),
+        "topk_idx": layer.kept_idx.cpu().numpy(), "topk_cnt": layer.kept_cnt.cpu().numpy(),
+    }
+    if mode == "drift":
+        res.update(vpool=layer.vpool.cpu().numpy(), key=layer.key.cpu().numpy(),
+                   vout=layer.vout.cpu().numpy(), vmv=layer.vmv.cpu().numpy())
+    layer.refine(stream)
+    layer.attend(q, k, v, out, stream)
+    torch.cuda.synchronize()
+    res["idx"] = layer.kept_idx.cpu().numpy()
+    res["cnt"] = layer.kept_cnt.cpu().numpy()
+    if rounds:
+        res["J_init"] = layer.J_init.cpu().numpy()
+        res["J_final"] = layer.J_final.cpu().numpy()
+    res["out"] = out.float().cpu().numpy()
+    res["lse"] = layer.lse.cpu().numpy()
+    res["k_max"] = layer.k_max
+    return res
+
+
+CASES = [("tiny", "prob"), ("views8", "prob"), ("views32", "drift"),
+         ("views100", "drift"), ("views200", "prob"), ("views200", "drift")]
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[f"{a}-{b}" for a, b in CASES])
+def case(request):
+    name, mode = request.param
+    print(f"\n[case] {name} mode={mode}", flush=True)
+    w, x = case_inputs(name)
+    g = run_gpu(w, x, mode)
+    qf, kf = f64(x["q"], w), f64(x["k"], w)
+    N, B = w.N, w.block
+    ref = {"qpool": oracle.block_pool(qf, N, B), "kpool": oracle.block_pool(kf, N, B)}
+    del qf, kf
+    scale = 1.0 / math.sqrt(w.head_dim)
+    ref["P"] = oracle.block_map(ref["qpool"], ref["kpool"], scale)
+    if mode == "drift":
+        ref["vpool"] = oracle.block_pool(f64(x["v"], w), N, B)
+        ref["key"], ref["vout"], _ = oracle.drift_key(ref["P"], ref["vpool"], None, 1e-4)
+    else:
+        ref["key"] = ref["P"]
+    ref["kept"], ref["margin"] = oracle.select_topk(ref["key"], x["keep"], x["always"])
+    return name, mode, w, x, g, ref
+
+
+def _close(a, b, rel, what):
+    scale = np.maximum(np.abs(b), np.abs(b).max() * 1e-300 + 1e-300)
+    err = np.abs(a - b) / scale
+    assert err.max() <= rel, f"{what}: max relative error {err.max():.3e} > {rel}"
+
+
+def test_pool(case):
+    name, mode, w, x, g, ref = case
+    for t in ("qpool", "kpool") + (("vpool",) if mode == "drift" else ()):
+        # sums of bf16 values are exact in float64, so this is usually exact
+        d = np.abs(g[t] - ref[t])
+        tol = 1e-12 * np.maximum(np.abs(ref[t]), 1e-3 * np.abs(ref[t]).max())
+        assert np.all(d <= tol), f"{t}: max abs diff {d.max():.3e}"
+
+
+def test_block_map(case):
+    name, mode, w, x, g, ref = case
+    _close(g["P"], ref["P"], 1e-12, "P")
+    assert np.allclose(g["P"].sum(-1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_drift_key(case):
+    name, mode, w, x, g, ref = case
+    if mode != "drift":
+        pytest.skip("probability scoring")
+    _close(g["key"], ref["key"], 1e-10, "drift key")
+    d = np.abs(g["vout"] - ref["vout"])
+    assert d.max() <= 1e-12 * np.abs(ref["vpool"]).max(), f"vout diff {d.max():.3e}"
+    vmv = np.einsum("hjd,hjd->hj", ref["vpool"], ref["vpool"])
+    _close(g["vmv"], vmv, 1e-12, "V^T V")
+
+
+def test_topk(case):
+    name, mode, w, x, g, ref = case
+    n = w.n_blocks
+    check_lists_wellformed(g["topk_idx"], g["topk_cnt"], x["keep"], x["always"], n)
+    gm = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
+    nd = compare_masks(gm, ref["kept"], ref["key"], x["always"], x["keep"])
+    print(f"[topk] {name}/{mode}: {nd} near-tie rows of {w.heads * n}")
+
+
+def test_refine(case):
+    name, mode, w, x, g, ref = case
+    if mode != "drift" or w.rounds == 0:
+        pytest.skip("no refinement rounds in this workload")
+    n = w.n_blocks
+    check_lists_wellformed(g["idx"], g["cnt"], x["keep"], x["always"], n)
+    start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
+    rows = [(h, i) for h, i in sample_blocks(w.heads, n, 512, seed=3)]
+    kr, J0, J1, mg = oracle.refine_dropset(ref["P"], ref["vpool"], ref["vout"], None,
+                                           x["keep"], x["always"], start, w.rounds, w.rho,
+                                           rows=rows)
+    gm = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    cand = x["always"] == 0
+    flagged = 0
+    for h, i in rows:
+        assert g["J_init"][h, i] == pytest.approx(J0[h, i], rel=1e-9)
+        if np.array_equal(gm[h, i], kr[h, i]):
+            assert g["J_final"][h, i] == pytest.approx(J1[h, i], rel=1e-9)
+            continue
+        assert mg[h, i] < 1e-6, f"row ({h},{i}) differs without a near-tie (margin {mg[h, i]:.3e})"
+        flagged += 1
+        Dm = cand & ~gm[h, i]
+        e = ref["vout"][h, i][None] - ref["vpool"][h]
+        d = ref["P"][h, i][:, None] * e
+        Jg = oracle.drop_objective(ref["P"][h, i], d, np.eye(w.head_dim), Dm)[3]
+        assert g["J_final"][h, i] == pytest.approx(Jg, rel=1e-9)
+        assert g["J_final"][h, i] <= g["J_init"][h, i]
+    assert np.all(g["J_final"] <= g["J_init"])
+    print(f"[refine] {name}: {len(rows)} rows checked, {flagged} near-tie rows; "
+          f"mean J_final/J_init = {np.mean(g['J_final'] / g['J_init']):.4f}")
+
+
+def test_attention(case):
+    name, mode, w, x, g, ref = case
+    n, B, N = w.n_blocks, w.block, w.N
+    kept = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    count = w.heads * n if w.heads * n <= 64 else 48
+    blocks = sample_blocks(w.heads, n, count, seed=5)
+    qf, kf, vf = (f64(x[t], w) for t in ("q", "k", "v"))
+    O, lse = oracle.masked_attention(qf, kf, vf, kept, N, B, 1.0 / math.sqrt(w.head_dim),
+                                     blocks=blocks)
+    got, want, gl, wl = [], [], [], []
+    for h, i in blocks:
+        r0, r1 = i * B, min((i + 1) * B, N)
+        got.append(g["out"][h, r0:r1]); want.append(O[h, r0:r1])
+        gl.append(g["lse"][h, r0:r1]); wl.append(lse[h, r0:r1])
+        assert np.all(g["out"][h, r1:(i + 1) * B] == 0), "padded rows must be zero"
+    got, want = np.concatenate(got), np.concatenate(want)
+    mx, mean, scale = attn_errors(got, want)
+    rel = math.sqrt(np.mean((got - want) ** 2) / np.mean(want ** 2))
+    print(f"[attn] {name}/{mode}: max-abs {mx:.3e} mean-abs {mean:.3e} rel-rms {rel:.3e}")
+    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_RMS
+    assert np.allclose(np.concatenate(gl), np.concatenate(wl), rtol=0, atol=1e-3)
+
+
+# ---------------------------------------------------------------------------
+# Dense mode, determinism and edge cases
+# ---------------------------------------------------------------------------
+
+def _small(**kw):
+    w = custom(**kw)
+    return w, synth.make_inputs(w)
+
+
+def test_dense_mode_matches_dense_oracle():
+    b = _lib()
+    for w, x in (case_inputs("tiny"), _small(name="d", views=3, patches_per_view=300,
+                                              specials_per_view=5, heads=3, block=128)):
+        shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+        q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        lse = torch.empty((w.heads, w.N_pad), dtype=torch.float32, device="cuda")
+        b.dense_attention(q, k, v, shape, out, lse=lse)
+        torch.cuda.synchronize()
+        O, L = oracle.dense_attention(*(f64(x[t], w) for t in ("q", "k", "v")), w.N, w.block,
+                                      1.0 / math.sqrt(w.head_dim))
+        got = out.float().cpu().numpy()
+        mx, mean, _ = attn_errors(got[:, : w.N], O[:, : w.N])
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+        assert np.all(got[:, w.N:] == 0)
+        assert np.allclose(lse.cpu().numpy()[:, : w.N], L[:, : w.N], atol=1e-3, rtol=0)
+
+
+def test_single_kept_block_is_restricted_softmax():
+    b = _lib()
+    w, x = _small(name="s", views=2, patches_per_view=250, specials_per_view=0, heads=2,
+                  block=64)
+    shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+    n = w.n_blocks
+    rng = np.random.default_rng(7)
+    idx = rng.integers(0, n, size=(w.heads, n, 1)).astype(np.int32)
+    cnt = np.ones((w.heads, n), np.int32)
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    b.ress_sparse_attn_fwd(q, k, v, shape, torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(cnt).cuda(), 1, 0.125, out)
+    torch.cuda.synchronize()
+    kept = kept_mask_from_lists(idx, cnt, n)
+    O, _ = oracle.masked_attention(*(f64(x[t], w) for t in ("q", "k", "v")), kept, w.N,
+                                   w.block, 0.125)
+    mx, mean, _ = attn_errors(out.float().cpu().numpy()[:, : w.N], O[:, : w.N])
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
+def test_invalid_list_entries_are_skipped_and_empty_rows_are_zero():
+    b = _lib()
+    w, x = _small(name="e", views=2, patches_per_view=256, specials_per_view=0, heads=1,
+                  block=128)
+    shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+    n = w.n_blocks  # 4
+    idx = np.array([[[1, -3, 99, 2], [0, 1, 2, 3], [3, -1, -1, -1], [2, 0, 0, 0]]], np.int32)
+    cnt = np.array([[4, 4, 1, 0]], np.int32)
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    out = torch.full_like(q, 7.0)
+    lse = torch.empty((1, w.N_pad), dtype=torch.float32, device="cuda")
+    b.ress_sparse_attn_fwd(q, k, v, shape, torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(cnt).cuda(), 4, 0.125, out, lse)
+    torch.cuda.synchronize()
+    kept = np.zeros((1, n, n), bool)
+    kept[0, 0, [1, 2]] = True
+    kept[0, 1, :] = True
+    kept[0, 2, 3] = True
+    O, _ = oracle.masked_attention(*(f64(x[t], w) for t in ("q", "k", "v")), kept, w.N,
+                                   w.block, 0.125, blocks=[(0, 0), (0, 1), (0, 2)])
+    got = out.float().cpu().numpy()
+    mx, mean, _ = attn_errors(got[0, : 3 * 128], O[0, : 3 * 128])
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+    assert np.all(got[0, 3 * 128:] == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()[0, 3 * 128:]))
+
+
+def test_padding_garbage_is_ignored():
+    b = _lib()
+    w, x = _small(name="p", views=3, patches_per_view=290, specials_per_view=5, heads=2,
+                  block=128, sparsity=(0.5, 0.5))
+    assert w.N < w.N_pad
+    ref = run_gpu(w, x, "drift")
+    y = dict(x)
+    for t in ("q", "k", "v"):
+        a = x[t].copy()
+        a[:, w.N:, :] = synth.f32_to_bf16_bits(np.full(a[:, w.N:, :].shape, np.nan, np.float32))
+        y[t] = a
+    got = run_gpu(w, y, "drift")
+    for key in ("qpool", "kpool", "vpool", "P", "key", "idx", "cnt"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.array_equal(got["out"][:, : w.N], ref["out"][:, : w.N])
+    assert np.all(got["out"][:, w.N:] == 0)
+
+
+def test_block64_bf16_drift_with_gram_and_refine():
+    w, x = _small(name="g", views=4, patches_per_view=300, specials_per_view=5, heads=2,
+                  block=64, sparsity=(0.5, 0.5), score="drift", rounds=4, rho=1.0)
+    M = synth.make_gram(w.heads, w.head_dim)
+    g = run_gpu(w, x, "drift", M=M)
+    N, B, n = w.N, w.block, w.n_blocks
+    qp = oracle.block_pool(f64(x["q"], w), N, B)
+    kp = oracle.block_pool(f64(x["k"], w), N, B)
+    vp = oracle.block_pool(f64(x["v"], w), N, B)
+    P = oracle.block_map(qp, kp, 0.125)
+    key, vout, _ = oracle.drift_key(P, vp, M, 1e-4)
+    _close(g["key"], key, 1e-10, "drift key with M")
+    _close(g["vmv"], np.einsum("hjd,hde,hje->hj", vp, M, vp), 1e-12, "V^T M V")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    compare_masks(kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n), kept, key,
+                  x["always"], x["keep"])
+    start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
+    kr, J0, J1, mg = oracle.refine_dropset(P, vp, vout, M, x["keep"], x["always"], start,
+                                           w.rounds, w.rho)
+    gm = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    same = np.all(gm == kr, axis=-1)
+    assert np.all(same | (mg < 1e-6))
+    assert np.allclose(g["J_init"], J0, rtol=1e-9, atol=0)
+    assert np.allclose(g["J_final"][same], J1[same], rtol=1e-9, atol=0)
+    assert np.mean(g["J_final"] / g["J_init"]) < 1.0
+
+
+def test_reruns_are_bit_identical_on_a_side_stream():
+    w, x = _small(name="r", views=6, patches_per_view=400, specials_per_view=5, heads=4,
+                  block=128, sparsity=(0.8, 0.8), score="drift", rounds=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = run_gpu(w, x, "drift", stream=s)
+        b = run_gpu(w, x, "drift", stream=s)
+    for k in a:
+        if isinstance(a[k], np.ndarray):
+            assert np.array_equal(a[k], b[k], equal_nan=True), k
