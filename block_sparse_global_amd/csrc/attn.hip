@@ -225,8 +225,12 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dim = 32 * dt + 8 * g + 4 * half;
-      const float x0 = o[dt][4 * g] * inv, x1 = o[dt][4 * g + 1] * inv;
-      const float x2 = o[dt][4 * g + 2] * inv, x3 = o[dt][4 * g + 3] * inv;
+      // padded rows may hold garbage (even NaN) in their accumulators:
+      // select zero rather than scale by it
+      const float x0 = inv != 0.f ? o[dt][4 * g] * inv : 0.f;
+      const float x1 = inv != 0.f ? o[dt][4 * g + 1] * inv : 0.f;
+      const float x2 = inv != 0.f ? o[dt][4 * g + 2] * inv : 0.f;
+      const float x3 = inv != 0.f ? o[dt][4 * g + 3] * inv : 0.f;
       if constexpr (sizeof(Tout) == 2) {
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);

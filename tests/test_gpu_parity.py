@@ -202,7 +202,11 @@ def test_attention(case):
     rel = math.sqrt(np.mean((got - want) ** 2) / np.mean(want ** 2))
     print(f"[attn] {name}/{mode}: max-abs {mx:.3e} mean-abs {mean:.3e} rel-rms {rel:.3e}")
     assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_RMS
-    assert np.allclose(np.concatenate(gl), np.concatenate(wl), rtol=0, atol=1e-3)
+    # bf16 inputs: the logits are exact products summed in float32, so the
+    # log-sum-exp agrees closely; float32 inputs are rounded to bf16 when
+    # staged, which moves each logit by up to ~2^-8 |q||k| * scale
+    lse_tol = 1e-3 if w.dtype == "bf16" else 3e-2
+    assert np.allclose(np.concatenate(gl), np.concatenate(wl), rtol=0, atol=lse_tol)
 
 
 # ---------------------------------------------------------------------------
@@ -230,7 +234,8 @@ def test_dense_mode_matches_dense_oracle():
         mx, mean, _ = attn_errors(got[:, : w.N], O[:, : w.N])
         assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
         assert np.all(got[:, w.N:] == 0)
-        assert np.allclose(lse.cpu().numpy()[:, : w.N], L[:, : w.N], atol=1e-3, rtol=0)
+        lse_tol = 1e-3 if w.dtype == "bf16" else 3e-2
+        assert np.allclose(lse.cpu().numpy()[:, : w.N], L[:, : w.N], atol=lse_tol, rtol=0)
 
 
 def test_single_kept_block_is_restricted_softmax():
