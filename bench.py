@@ -145,6 +145,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 8/32-view layer-vs-dense lines")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-attention timing (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run one device-to-device copy of BYTES bytes, whose "
+                         "HBM counters calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -173,15 +178,27 @@ def main():
     attn_ms = time_events(lambda: layer.attend(q, k, v, out), args.steps)
 
     import block_sparse_global_amd as bsg
-    dense_out = torch.empty_like(q)
-    dense_reps = max(2, min(args.steps, 5))
-    dense_ms = time_events(lambda: bsg.dense_attention(q, k, v, shape, dense_out), dense_reps)
     df = dense_flops(w)
+    dense_ms = float("nan")
+    if not args.no_dense:
+        dense_out = torch.empty_like(q)
+        dense_reps = max(2, min(args.steps, 5))
+        dense_ms = time_events(lambda: bsg.dense_attention(q, k, v, shape, dense_out),
+                               dense_reps)
+        del dense_out
+    if args.copy_calibration > 0:
+        nb = int(args.copy_calibration)
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     sweep = {}
     if not args.no_sweep:
         for name in ("views8", "views32", "views100"):
-            if name == args.workload:
+            if name == args.workload and not args.no_dense:
                 sweep[name] = {"layer_ms": ms_step, "dense_ms": dense_ms}
             else:
                 w2, x2, shape2, layer2, (q2, k2, v2), out2 = setup(name)
@@ -223,10 +240,10 @@ def main():
         },
         "layer_ms": ms_step,
         "layer_ms_wall": t_wall,
-        "dense_ms": dense_ms,
-        "dense_tflops": df / (dense_ms * 1e-3) / 1e12,
-        "speedup_vs_dense": dense_ms / ms_step,
-        "sparse_vs_dense_per_flop": (kf / attn_ms) / (df / dense_ms),
+        "dense_ms": None if args.no_dense else dense_ms,
+        "dense_tflops": None if args.no_dense else df / (dense_ms * 1e-3) / 1e12,
+        "speedup_vs_dense": None if args.no_dense else dense_ms / ms_step,
+        "sparse_vs_dense_per_flop": None if args.no_dense else (kf / attn_ms) / (df / dense_ms),
         "attn_tflops": achieved,
         "kept_flop": kf,
         "realised_sparsity": 1.0 - float(cnt.sum()) / (w.heads * w.n_blocks ** 2),

@@ -84,7 +84,8 @@ def _load():
                                      ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, vp]
     lib.ress_select_topk.argtypes = [dp, ress_shape, ip, vp, i32, ip, ip, vp]
     lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
-                                        ctypes.c_double, i32, ip, ip, dp, dp, vp]
+                                        ctypes.c_double, ctypes.c_double, i32, ip, ip,
+                                        dp, dp, vp]
     lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
                                          ctypes.c_float, vp, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
@@ -205,9 +206,9 @@ def ress_select_topk(key, shape: Shape, keep: Sequence[int], always_keep, k_max:
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
 
 
-def ress_refine_dropset(P, vpool, vout, vmv, M, shape: Shape, keep, always_keep,
-                        rounds: int, rho: float, k_max: int, kept_idx, kept_cnt,
-                        J_init=None, J_final=None, stream=None):
+def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
+                        rounds: int, rho: float, eps: float, k_max: int, kept_idx,
+                        kept_cnt, J_init=None, J_final=None, stream=None):
     H, n, D = shape.H, shape.n, shape.D
     f64 = torch.float64
     keep_arr, keep_p = _host_i32(keep, "keep")
@@ -217,10 +218,10 @@ def ress_refine_dropset(P, vpool, vout, vmv, M, shape: Shape, keep, always_keep,
     if alw_arr is not None and alw_arr.shape != (n,):
         raise ValueError(f"always_keep must have shape ({n},)")
     _check("ress_refine_dropset", LIB.ress_refine_dropset(
-        _ptr(P, "P", f64, (H, n, n)), _ptr(vpool, "vpool", f64, (H, n, D)),
-        _ptr(vout, "vout", f64, (H, n, D)), _ptr(vmv, "vmv", f64, (H, n)),
+        _ptr(P, "P", f64, (H, n, n)), _ptr(key, "key", f64, (H, n, n)),
+        _ptr(vpool, "vpool", f64, (H, n, D)), _ptr(vout, "vout", f64, (H, n, D)),
         _ptr(M, "M", f64, (H, D, D)), shape.c(), keep_p, alw_p, int(rounds), float(rho),
-        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
+        float(eps), int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)),
         _ptr(J_init, "J_init", f64, (H, n)), _ptr(J_final, "J_final", f64, (H, n)),
         _stream(stream)))

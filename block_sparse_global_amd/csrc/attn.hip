@@ -5,11 +5,13 @@
 // float32 accumulation, for gfx950.
 //
 // Work decomposition: one workgroup per (query block, head); BLK/32 waves,
-// each owning 32 query rows. Per kept key block the K tile and the V tile
-// are staged in LDS and every wave computes
+// each owning 32 query rows. Per kept key block the K and V tiles are copied
+// straight from HBM into LDS (global_load_lds, double-buffered: the next kept
+// block streams in while the current one is computed) and every wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T held in
 //                  registers for the whole kernel)
-//   O^T += V^T P^T (A = V^T from LDS, B = P^T taken directly from the S^T
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with LDS
+//                  transpose reads, B = P^T taken directly from the S^T
 //                  accumulators after the softmax)
 // so that each lane owns one query column: the running max, the running sum
 // and the rescaling of O are per-lane scalars (the two lane halves holding
@@ -21,6 +23,8 @@
 // D[8*(r/4) + 4*(l/32) + r%4][l % 32]. Only this output mapping and the
 // equal k-slot mapping of A and B matter for correctness; the parity tests
 // check them end to end.
+#include <type_traits>
+
 #include "ress_internal.h"
 
 namespace ress {
@@ -28,6 +32,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;
 
@@ -56,29 +61,65 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Position of key kk (0..15) inside its 16-key group of the V^T tile: the
-// 8 keys a lane half feeds to one MFMA k-step are made contiguous
-// (lane half 0: keys 0-3, 8-11; lane half 1: keys 4-7, 12-15).
-__device__ inline int vt_pos(int kk) {
-  return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+// LDS layout: K and V tiles are both row-major ([key][64 dims], 128-byte
+// rows of eight 16-byte chunks), with the chunk index XORed by a
+// row-dependent value so that the MFMA operand reads are bank-conflict free.
+// gfx950's LDS serves a 128-bit access in passes of 16 lanes over 64
+// four-byte banks; the bank group of (row, chunk) is (8 * row + chunk) mod 16.
+//  * K (128-bit reads of 16 consecutive rows at one logical chunk):
+//    XOR with (row >> 1) & 7 gives 16 distinct groups.
+//  * V (transposed 64-bit reads, below): XOR with (row & 3) << 1 makes each
+//    32-lane pass hit distinct banks.
+__device__ inline int k_swz(int row) { return (row >> 1) & 7; }
+__device__ inline int v_swz(int row) { return (row & 3) << 1; }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives
+// element i % 4 of the 8-byte words addressed by source lanes 4k + i / 4,
+// k = 0..3. With source lane 4k + q pointing at V[key0 + k][d0 + 4q ..], lane
+// i gets V[key0 .. key0 + 3][d0 + i]: four consecutive keys of one dim, the
+// k-major operand layout the PV product needs, straight from row-major V.
+__device__ inline v4i16 tr_read(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
 }
 
+// 16 bytes global -> LDS without registers; lane l of the wave writes the
+// 16 bytes at `window` + 16 * l (window is wave-uniform).
+__device__ inline void gload_lds16(const uint16_t* g, uint16_t* window) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)window, 16, 0, 0);
+}
+
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Running-max slack before O is rescaled (log2 units of the scaled scores):
+// a new block whose row max exceeds the one in use by less than this keeps
+// the old max, so p may reach 2^kRescaleSlack; float32 and bf16 hold that
+// exactly as well as values below 1, and the final O / l uses the same max
+// for numerator and denominator.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int BLK, typename Tin, typename Tout>
-__global__ __launch_bounds__(BLK * 2) void attn_kernel(
+__global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
     const Tin* __restrict__ Q, const Tin* __restrict__ Kx,
     const Tin* __restrict__ Vx, const int32_t* __restrict__ kept_idx,
     const int32_t* __restrict__ kept_cnt, int k_max, int n, int N, int N_pad,
     float scale, Tout* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kThreads = BLK * 2;     // BLK/32 waves of 64
-  constexpr int kKT = BLK / 32;         // 32-key tiles per block
-  constexpr int kChunksPerRowV = BLK / 8;  // 16-byte chunks per V^T row
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * BLK];
+  constexpr int kThreads = BLK * 2;  // BLK/32 waves of 64
+  constexpr int kKT = BLK / 32;      // 32-key tiles per block
+  constexpr int kTile = BLK * kD;    // elements per K or V tile
+  // Double-buffered tiles: block kb is consumed from buffer kb&1 while block
+  // kb+1 is loaded into the other one.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTile];
 
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
@@ -99,9 +140,10 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;
+  float m_use = -INFINITY;  // running max in use, in scaled log2 units
   float l_run = 0.f;
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e)
+  const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   int cnt = n;
   const int32_t* list = nullptr;
@@ -111,108 +153,164 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(
     cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
     list = kept_idx + row * k_max;
   }
+  // next list position holding a valid block index (entries outside [0, n)
+  // are skipped); uniform across the workgroup
+  auto next_valid = [&](int kb) {
+    if (list == nullptr) return kb;
+    while (kb < cnt) {
+      const int j = list[kb];
+      if (j >= 0 && j < n) break;
+      ++kb;
+    }
+    return kb;
+  };
+  auto block_of = [&](int kb) { return list ? list[kb] : kb; };
 
-  for (int kb = 0; kb < cnt; ++kb) {
-    const int j = list ? list[kb] : kb;
-    if (j < 0 || j >= n) continue;  // uniform across the workgroup
-    __syncthreads();  // previous tiles fully consumed
-    // ---- stage K (row-major, XOR-swizzled 16-byte chunks) and V^T
-    {
-      const Tin* kp = Kx + head_off + (size_t)j * BLK * kD;
-      const Tin* vp = Vx + head_off + (size_t)j * BLK * kD;
+  // ---- staging of block j into buffer b. Rows past N (last block only)
+  // are read from row N-1: finite data whose scores are masked to -inf, so
+  // p = 0 multiplies a finite V row.
+  auto issue_loads = [&](int j, int b) {
+    if constexpr (sizeof(Tin) == 2) {
+      // 4 windows of 8 rows per wave and tensor; lane l fills row
+      // 8*win + l/8, physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row)
+      const bool full = (j + 1) * BLK <= N;
 #pragma unroll
-      for (int it = 0; it < (BLK * 8) / kThreads; ++it) {
-        const int c = tid + it * kThreads;
-        const int key = c >> 3, ch = c & 7;
-        // padded keys (last block only) are staged as zeros: their scores
-        // are masked below, and a zero V row keeps 0 * garbage out of O
-        const bool live = j * BLK + key < N;
-        uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-        if (live) {
-          kv = load_row8(kp + (size_t)key * kD + ch * 8);
-          vv = load_row8(vp + (size_t)key * kD + ch * 8);
-        }
-        *reinterpret_cast<uint4*>(&Ks[key * kD + ((ch ^ (key & 7)) * 8)]) = kv;
-        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
-        const int pos = (key & ~15) + vt_pos(key & 15);
-        const int pch = pos >> 3, pin = pos & 7;
+      for (int it = 0; it < 4; ++it) {
+        const int win = 4 * w + it;
+        const int r = 8 * win + (lane >> 3);
+        const int grow = full ? j * BLK + r : min(j * BLK + r, N - 1);
+        const Tin* base = Kx + head_off + (size_t)grow * kD;
+        gload_lds16(base + (((lane & 7) ^ k_swz(r)) * 8), &Ks[b][win * 512]);
+        const Tin* vbase = Vx + head_off + (size_t)grow * kD;
+        gload_lds16(vbase + (((lane & 7) ^ v_swz(r)) * 8), &Vs[b][win * 512]);
+      }
+    } else {
+      // float32 inputs: rounded to bf16 (nearest even) through registers
 #pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const int dim = ch * 8 + dd;
-          const int phys = (pch ^ (dim & (kChunksPerRowV - 1))) * 8 + pin;
-          Vt[dim * BLK + phys] = (uint16_t)(vw[dd >> 1] >> ((dd & 1) * 16));
-        }
+      for (int it = 0; it < 4; ++it) {
+        const int idx = tid + it * kThreads;
+        const int r = idx >> 3, c = idx & 7;
+        const int grow = min(j * BLK + r, N - 1);
+        const size_t off = head_off + (size_t)grow * kD + c * 8;
+        *reinterpret_cast<uint4*>(&Ks[b][r * kD + ((c ^ k_swz(r)) * 8)]) = load_row8(Kx + off);
+        *reinterpret_cast<uint4*>(&Vs[b][r * kD + ((c ^ v_swz(r)) * 8)]) = load_row8(Vx + off);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T
+  // Per-lane LDS element offsets of the MFMA operands (the buffer, the
+  // 32-key tile and the 16-key step only add compile-time constants).
+  int koff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    koff[ks] = l32 * kD + (((2 * ks + half) ^ k_swz(l32)) * 8);
+  int voff[2];
+  {
+    const int kk = (lane & 15) >> 2, q = lane & 3, G = (lane & 31) >> 4;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      voff[dt] = (4 * half + kk) * kD + (((4 * dt + 2 * G + (q >> 1)) ^ (2 * kk)) * 8) +
+                 (q & 1) * 4;
+  }
+
+  // ---- one kept block from buffer B (compile-time, so all LDS offsets are
+  // immediates); returns the next list position
+  auto process = [&](auto bufc, int kb) {
+    constexpr int B = decltype(bufc)::value;
+    const int j = block_of(kb);
+    const int kb_next = next_valid(kb + 1);
+    if (kb_next < cnt) issue_loads(block_of(kb_next), B ^ 1);
+
+    // S^T = K Q^T
     f32x16 s[kKT];
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
+      bf16x8 ka[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[B][kt * 32 * kD + koff[ks]]));
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const int krow = 32 * kt + l32;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ch = 2 * ks + half;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &Ks[krow * kD + ((ch ^ (krow & 7)) * 8)]));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kt], 0, 0, 0);
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s[kt], 0, 0, 0);
     }
-    // ---- mask padded keys of the last block
-    if (j == n - 1 && N < N_pad) {
-      const int base = j * BLK;
+    // mask padded keys (only the last block has any). Branching on the
+    // block's valid-key count, which changes with j, keeps the compiler from
+    // hoisting loop-invariant compare masks; the lane-half term is folded
+    // into the limit so that the compares use immediate key offsets only.
+    const int live_keys = N - j * BLK;
+    if (live_keys < BLK) {
+      const int lim = live_keys - 4 * half;
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (base + key >= N) s[kt][r] = -INFINITY;
+          const int kc = 32 * kt + 8 * (r >> 2) + (r & 3);
+          if (kc >= lim) s[kt][r] = -INFINITY;
         }
     }
-    // ---- online softmax (per lane = per query)
+    // online softmax (per lane = per query), lazy rescaling
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f((m_run - m_new) * sl2);
-    const float mb = m_new * sl2;
-    float psum = 0.f;
-    bf16x8 pb[kKT][2];
+    const float m_blk = mloc * sl2;
+    if (__any(m_blk > m_use + kRescaleSlack)) {
+      const float m_new = fmaxf(m_use, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kt][r], sl2, -mb));
-        psum += p;
-        pb[kt][r >> 3][r & 7] = (__bf16)p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const int dim = 32 * dt + l32;
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int ch = 2 * (2 * kt + hf) + half;
-          const int phys = (ch ^ (dim & (kChunksPerRowV - 1))) * 8;
-          const bf16x8 a =
-              as_bf16x8(*reinterpret_cast<const uint4*>(&Vt[dim * BLK + phys]));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][hf], o[dt], 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_use = m_new;
     }
+    // per 16-key step: P = exp2(S*scale*log2e - m) as bf16, then
+    // O^T += V^T P^T with the V^T operand read transposed from LDS
+    float psum = 0.f;
+#pragma unroll
+    for (int step = 0; step < 2 * kKT; ++step) {
+      const int kt = step >> 1, hf = step & 1;
+      bf16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        pb[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
+      // row sum of the very bf16 weights the PV product uses, two per
+      // instruction (bf16 dot product with (1, 1), float32 accumulation)
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const bf16x2 pp = {pb[r], pb[r + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vp = &Vs[B][step * 16 * kD + voff[dt]];
+        const v4i16 lo = tr_read(vp);           // keys 16*step + 4*half + 0..3
+        const v4i16 hi = tr_read(vp + 8 * kD);  // keys 16*step + 8 + 4*half + 0..3
+        const v8i16 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, lohi);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+      }
+    }
+    l_run += psum;
+    wait_vmem();  // this wave's loads of the next block have landed in LDS
+    __syncthreads();
+    return kb_next;
+  };
+
+  int kb = next_valid(0);
+  if (kb < cnt) {
+    issue_loads(block_of(kb), 0);
+    wait_vmem();
+  }
+  __syncthreads();
+  while (kb < cnt) {
+    kb = process(std::integral_constant<int, 0>{}, kb);
+    if (kb >= cnt) break;
+    kb = process(std::integral_constant<int, 1>{}, kb);
   }
 
   // ---- epilogue
@@ -242,7 +340,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(
     }
   if (lse != nullptr && half == 0) {
     float v = 0.f;
-    if (valid) v = (l_tot > 0.f) ? m_run * scale + logf(l_tot) : -INFINITY;
+    // m_use is in log2 units of scale*s; ln(2) converts it back
+    if (valid) v = (l_tot > 0.f) ? m_use * 0.6931471805599453f + logf(l_tot) : -INFINITY;
     lse[(size_t)h * N_pad + qrow] = v;
   }
 }

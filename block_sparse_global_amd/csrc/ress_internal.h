@@ -21,6 +21,33 @@ __host__ __device__ inline bool sel_always(const SelConfig& c, int j) {
   return (c.always_bits[j >> 6] >> (j & 63)) & 1ull;
 }
 
+// 64-bit key whose unsigned order is the float64 order (-0 counted as +0).
+__device__ inline uint64_t order_key(double x) {
+  if (x == 0.0) x = 0.0;
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Fixed-order (butterfly) sums over one wave of 64 lanes; every lane gets
+// the result.
+__device__ inline double wave_sum64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline int wave_isum64(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Orders the LDS accesses of one wave (all lanes) before the ones after it.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Launchers (defined next to their kernels). Each returns hipGetLastError()
 // of its launches.
 hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
@@ -44,12 +71,13 @@ hipError_t launch_topk(const double* key, const ress_shape& s,
                        const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,
                        int32_t* kept_cnt, hipStream_t st);
 
-hipError_t launch_refine(const double* P, const double* vpool,
-                         const double* vout, const double* vmv,
+hipError_t launch_refine(const double* P, const double* key,
+                         const double* vpool, const double* vout,
                          const double* M, const ress_shape& s,
                          const SelConfig& cfg, int32_t rounds, double rho,
-                         int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
-                         double* J_init, double* J_final, hipStream_t st);
+                         double eps, int32_t k_max, int32_t* kept_idx,
+                         int32_t* kept_cnt, double* J_init, double* J_final,
+                         hipStream_t st);
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
                        const ress_shape& s, const int32_t* kept_idx,

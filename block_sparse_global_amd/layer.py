@@ -83,10 +83,10 @@ class BlockSparseGlobalAttention:
     def refine(self, stream=None):
         if self.rounds <= 0:
             return
-        ress_refine_dropset(self.P, self.vpool, self.vout, self.vmv, self.M, self.shape,
-                            self.keep, self.always, self.rounds, self.rho, self.k_max,
-                            self.kept_idx, self.kept_cnt, self.J_init, self.J_final,
-                            stream)
+        ress_refine_dropset(self.P, self.key, self.vpool, self.vout, self.M, self.shape,
+                            self.keep, self.always, self.rounds, self.rho, self.eps,
+                            self.k_max, self.kept_idx, self.kept_cnt, self.J_init,
+                            self.J_final, stream)
 
     def attend(self, q, k, v, out, stream=None):
         ress_sparse_attn_fwd(q, k, v, self.shape, self.kept_idx, self.kept_cnt,

@@ -98,7 +98,7 @@ int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
  *   vpool, M, vout and vmv are ignored.
  * mode RESS_SCORE_DRIFT (ReSS page §4.2, Eq. 1 and 5-9):
  *   vout[h][i]  = sum_j P[h][i][j] vpool[h][j]                      (Eq. 1)
- *   vmv[h][j]   = vpool[h][j]^T M_h vpool[h][j]
+ *   vmv[h][j]   = vpool[h][j]^T M_h vpool[h][j]  (Eq. 9's last term)
  *   q_ij        = vout_i^T M vout_i - 2 vout_i^T M V_j + vmv_j      (Eq. 9)
  *   key[h][i][j] = P_ij sqrt(max(q_ij, 0)) / max(1 - P_ij, eps)     (Eq. 6-7)
  *   with M_h = I when M is NULL, else M: device float64 [H][D][D], symmetric
@@ -135,31 +135,36 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
 
 /*
  * ress_refine_dropset — ReSS iterative residual restoration (ReSS page
- * §4.3, Eq. 10-17), applied to the keep sets from ress_select_topk.
+ * §4.3, Eq. 10-17, Appendix E), applied to the keep sets from
+ * ress_select_topk.
  *
- * Per row, with D = candidates not kept: g = sum_{j in D} P_j (vout - V_j),
- * K = 1 - sum_{j in D} P_j, G = g^T M g, J = G / K^2 (Eq. 10, 12). Round r
- * (r < rounds) swaps m_r = floor(rho c / 2^(r+1)) blocks (Eq. 17): from the
+ * Per row, with D = candidates not kept, d_j = P_j (vout - V_j) (Eq. 5):
+ * g = sum_{j in D} d_j, K = 1 - sum_{j in D} P_j, G = g^T M g, J = G / K^2
+ * (Eq. 10, 12). Round r (r < rounds) swaps m_r = floor(rho c / 2^(r+1))
+ * blocks (Eq. 17), clamped to |D| and to the kept candidates: from the
  * round-start g, K, G it computes the exact objective decrease (Eq. 16) of
  * restoring each k in D (Eq. 13-14) and of dropping each kept candidate
- * (Eq. 15; a drop with K + u <= 0 counts as -inf), restores the m_r best
- * restores and drops the m_r best drops (ties: lower index), then recomputes
- * g, K, G. The set with the smallest J seen (strictly smaller replaces) is
- * written back to kept_idx / kept_cnt in the same format as the top-k call.
+ * (Eq. 15; a drop with K + u <= 0 counts as -inf), with s_k^2 = (key_k *
+ * max(1 - P_k, eps))^2 (Eq. 6-7); restores the m_r best restores and drops
+ * the m_r best drops (ties: lower index); then moves g and K by the swapped
+ * blocks (Eq. 13) and recomputes G and J. The set with the smallest J seen
+ * (strictly smaller replaces) is written back to kept_idx / kept_cnt in the
+ * same format as the top-k call.
  *
- * P: device float64 [H][n][n]; vpool, vout: device float64 [H][n][D];
- * vmv: device float64 [H][n] (all three as written by ress_block_score in
- * drift mode with the same M). M: device float64 [H][D][D] or NULL (= I).
- * keep, always_keep: HOST, as for ress_select_topk. rounds >= 0,
- * 0 < rho <= 1. kept_idx, kept_cnt: device, in/out. J_init, J_final: device
- * float64 [H][n] or NULL. H <= 64.
+ * P, key: device float64 [H][n][n] (key = the drift key of ress_block_score
+ * with the same eps and M). vpool, vout: device float64 [H][n][D] as written
+ * by ress_block_score in drift mode. M: device float64 [H][D][D] or NULL
+ * (= I). keep, always_keep: HOST, as for ress_select_topk. rounds >= 0,
+ * 0 < rho <= 1, eps > 0. kept_idx, kept_cnt: device, in/out. J_init,
+ * J_final: device float64 [H][n] or NULL. H <= 64.
  */
-int ress_refine_dropset(const double* P, const double* vpool,
-                        const double* vout, const double* vmv, const double* M,
-                        ress_shape shape, const int32_t* keep,
+int ress_refine_dropset(const double* P, const double* key,
+                        const double* vpool, const double* vout,
+                        const double* M, ress_shape shape, const int32_t* keep,
                         const uint8_t* always_keep, int32_t rounds, double rho,
-                        int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
-                        double* J_init, double* J_final, void* stream);
+                        double eps, int32_t k_max, int32_t* kept_idx,
+                        int32_t* kept_cnt, double* J_init, double* J_final,
+                        void* stream);
 
 /*
  * ress_sparse_attn_fwd — exact attention over the kept key blocks (ReSS page

@@ -131,12 +131,17 @@ def test_selection_budget_checks():
     _, k65 = _arr([2] * 65, np.int32)
     assert L.ress_select_topk(FAKE, big, k65, None, 2, FAKE, FAKE, None) == -2     # too many heads
     d = ctypes.c_double
-    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, -1, d(0.5), 3,
-                                 FAKE, FAKE, None, None, None) == -1               # rounds < 0
-    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(1.5), 3,
-                                 FAKE, FAKE, None, None, None) == -1               # rho > 1
-    assert L.ress_refine_dropset(FAKE, FAKE, None, FAKE, None, s, ok_keep, alw, 2, d(0.5), 3,
-                                 FAKE, FAKE, None, None, None) == -1               # vout NULL
+    e = d(1e-4)
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, -1, d(0.5), e,
+                                 3, FAKE, FAKE, None, None, None) == -1            # rounds < 0
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(1.5), e,
+                                 3, FAKE, FAKE, None, None, None) == -1            # rho > 1
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, None, None, s, ok_keep, alw, 2, d(0.5), e,
+                                 3, FAKE, FAKE, None, None, None) == -1            # vout NULL
+    assert L.ress_refine_dropset(FAKE, None, FAKE, FAKE, None, s, ok_keep, alw, 2, d(0.5), e,
+                                 3, FAKE, FAKE, None, None, None) == -1            # key NULL
+    assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(0.5),
+                                 d(0.0), 3, FAKE, FAKE, None, None, None) == -1    # eps <= 0
 
 
 def test_error_string_is_cleared_per_thread():
