@@ -32,6 +32,18 @@ METRIC = "kept-block attention TFLOP/s + layer latency (ms) vs dense at 8/32/100
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes of one attention launch on the 100-view workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, median over dispatches), scaled by what the same counters read for
+# a 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0). The figures hold only
+# for the kernel source they were taken on; any other source reports null.
+ATTN_TRAFFIC = {
+    "workload": "views100",
+    "source_sha256": "29619b6aef27ed59c110c48fa62af72501df52e2e11d07dd48f32df7e60febe7",
+    "read_bytes": 7943460635,
+    "write_bytes": 281542656,
+}
+
 
 def kept_flops(w, idx, cnt):
     """4 * D * sum over kept (query block, key block) pairs of valid q * valid k."""
@@ -67,6 +79,18 @@ def setup(name):
                                            rho=w.rho)
     out = torch.empty_like(q)
     return w, x, shape, layer, (q, k, v), out
+
+
+def attn_traffic(workload):
+    """Counter-measured bytes of one attention launch, or None when the kernel
+    source or the workload differs from the ones the counters were taken on."""
+    import hashlib
+    src = os.path.join(ROOT, "block_sparse_global_amd", "csrc", "attn.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != ATTN_TRAFFIC["source_sha256"] or workload != ATTN_TRAFFIC["workload"]:
+        return None
+    return ATTN_TRAFFIC["read_bytes"] + ATTN_TRAFFIC["write_bytes"]
 
 
 def time_events(fn, reps):
@@ -234,7 +258,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": attn_traffic(w.name), "traffic_unit": "bytes per launch (HBM, counters)",
             "kernel": "attn_kernel<128, bf16> (ress_sparse_attn_fwd)",
             "flop_per_launch": kf, "avg_launch_ms": attn_ms,
         },

@@ -95,6 +95,20 @@ __device__ inline void gload_lds16(const uint16_t* g, uint16_t* window) {
 
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// Workgroup barrier for the LDS tiles: waits for this wave's LDS operations
+// (not for tile copies still in flight, which wait_vmem covers) and keeps the
+// compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// max of a lane's value and the one of lane l ^ 32 (v_permlane32_swap)
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Running-max slack before O is rescaled (log2 units of the scaled scores):
 // a new block whose row max exceeds the one in use by less than this keeps
 // the old max, so p may reach 2^kRescaleSlack; float32 and bf16 hold that
@@ -103,7 +117,7 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // v
 constexpr float kRescaleSlack = 8.0f;
 
 template <int BLK, typename Tin, typename Tout>
-__global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
+__global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     const Tin* __restrict__ Q, const Tin* __restrict__ Kx,
     const Tin* __restrict__ Vx, const int32_t* __restrict__ kept_idx,
     const int32_t* __restrict__ kept_cnt, int k_max, int n, int N, int N_pad,
@@ -111,9 +125,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
   constexpr int kThreads = BLK * 2;  // BLK/32 waves of 64
   constexpr int kKT = BLK / 32;      // 32-key tiles per block
   constexpr int kTile = BLK * kD;    // elements per K or V tile
-  // Double-buffered tiles: block kb is consumed from buffer kb&1 while block
-  // kb+1 is loaded into the other one.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kTile];
+  // One K buffer and two V buffers (48 KB at BLK = 128, so three workgroups
+  // share a CU): V of the next kept block streams in during the whole of the
+  // current block, K of the next block once every wave has finished its
+  // S = K Q^T product.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTile];
 
   const int i = blockIdx.x;
@@ -145,13 +161,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e)
   const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // The keep list is read through the constant address space so that its
+  // (workgroup-uniform) entries come in by scalar loads: vector loads would
+  // share the vmcnt counter with the tile copies and a wait for a block index
+  // would also wait for the copies in flight.
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
   int cnt = n;
-  const int32_t* list = nullptr;
+  const_i32p list = nullptr;
   if (kept_idx != nullptr) {
     const size_t row = (size_t)h * n + i;
-    cnt = kept_cnt[row];
+    cnt = ((const_i32p)kept_cnt)[row];
     cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
-    list = kept_idx + row * k_max;
+    list = (const_i32p)(kept_idx + row * k_max);
   }
   // next list position holding a valid block index (entries outside [0, n)
   // are skipped); uniform across the workgroup
@@ -166,34 +187,54 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
   };
   auto block_of = [&](int kb) { return list ? list[kb] : kb; };
 
-  // ---- staging of block j into buffer b. Rows past N (last block only)
-  // are read from row N-1: finite data whose scores are masked to -inf, so
-  // p = 0 multiplies a finite V row.
-  auto issue_loads = [&](int j, int b) {
+  // ---- staging of the K or V tile of block j into an LDS buffer. Each wave
+  // copies 4 windows of 8 rows; in window it, lane l fills row
+  // r = 32*w + 8*it + l/8 at physical chunk l%8, i.e. logical chunk
+  // (l%8) ^ swz(r). For V, swz(r) = 2*((l/8)&3) does not depend on it; for
+  // K, swz(r) = (l/16) ^ (4*(it&1)). So two per-lane offsets (windows 0 and
+  // 1) plus compile-time row steps cover all windows. Rows past N (last
+  // block only) are read from row N-1: finite data whose scores are masked
+  // to -inf, so p = 0 multiplies a finite V row.
+  const int row0 = 32 * w + (lane >> 3);
+  const int kgo0 = row0 * kD + (((lane & 7) ^ (lane >> 4)) * 8);
+  const int kgo1 = (row0 + 8) * kD + (((lane & 7) ^ (lane >> 4) ^ 4) * 8);
+  const int vgo0 = row0 * kD + (((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 8);
+  auto tile_off = [&](int it, bool is_v) {
+    return is_v ? vgo0 + 8 * it * kD : ((it & 1) ? kgo1 : kgo0) + 16 * (it >> 1) * kD;
+  };
+  auto issue_tile = [&](const Tin* X, uint16_t* dst, int j, bool is_v) {
     if constexpr (sizeof(Tin) == 2) {
-      // 4 windows of 8 rows per wave and tensor; lane l fills row
-      // 8*win + l/8, physical chunk l%8, i.e. logical chunk (l%8) ^ swz(row)
+      // block base (uniform) + 32-bit per-lane byte offset: the copies use
+      // the scalar-base addressing form
+      const char* base = reinterpret_cast<const char*>(
+          X + head_off + (size_t)__builtin_amdgcn_readfirstlane(j) * BLK * kD);
       const bool full = (j + 1) * BLK <= N;
+      if (full) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int win = 4 * w + it;
-        const int r = 8 * win + (lane >> 3);
-        const int grow = full ? j * BLK + r : min(j * BLK + r, N - 1);
-        const Tin* base = Kx + head_off + (size_t)grow * kD;
-        gload_lds16(base + (((lane & 7) ^ k_swz(r)) * 8), &Ks[b][win * 512]);
-        const Tin* vbase = Vx + head_off + (size_t)grow * kD;
-        gload_lds16(vbase + (((lane & 7) ^ v_swz(r)) * 8), &Vs[b][win * 512]);
+        for (int it = 0; it < 4; ++it) {
+          const uint32_t off = 2u * (uint32_t)tile_off(it, is_v);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
+        }
+      } else {
+        const int last = N - 1 - j * BLK;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = row0 + 8 * it;
+          const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) + (min(r, last) - r) * kD);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
+        }
       }
     } else {
       // float32 inputs: rounded to bf16 (nearest even) through registers
+      const Tin* base = X + head_off + (size_t)j * BLK * kD;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
+      for (int it = 0; it < BLK * 8 / kThreads; ++it) {
         const int idx = tid + it * kThreads;
         const int r = idx >> 3, c = idx & 7;
-        const int grow = min(j * BLK + r, N - 1);
-        const size_t off = head_off + (size_t)grow * kD + c * 8;
-        *reinterpret_cast<uint4*>(&Ks[b][r * kD + ((c ^ k_swz(r)) * 8)]) = load_row8(Kx + off);
-        *reinterpret_cast<uint4*>(&Vs[b][r * kD + ((c ^ v_swz(r)) * 8)]) = load_row8(Vx + off);
+        const int rr = min(r, N - 1 - j * BLK);
+        const int sw = is_v ? v_swz(r) : k_swz(r);
+        *reinterpret_cast<uint4*>(&dst[r * kD + ((c ^ sw) * 8)]) =
+            load_row8(base + (size_t)rr * kD + c * 8);
       }
     }
   };
@@ -213,13 +254,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
                  (q & 1) * 4;
   }
 
-  // ---- one kept block from buffer B (compile-time, so all LDS offsets are
-  // immediates); returns the next list position
+  // ---- one kept block, V from buffer B (compile-time, so all LDS offsets
+  // are immediates); returns the next list position
   auto process = [&](auto bufc, int kb) {
     constexpr int B = decltype(bufc)::value;
     const int j = block_of(kb);
     const int kb_next = next_valid(kb + 1);
-    if (kb_next < cnt) issue_loads(block_of(kb_next), B ^ 1);
+    const bool more = kb_next < cnt;
+    const int j_next = more ? block_of(kb_next) : 0;
+    if (more) issue_tile(Vx, Vs[B ^ 1], j_next, true);
 
     // S^T = K Q^T
     f32x16 s[kKT];
@@ -228,13 +271,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
       bf16x8 ka[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[B][kt * 32 * kD + koff[ks]]));
+        ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[kt * 32 * kD + koff[ks]]));
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s[kt], 0, 0, 0);
     }
+    // every wave has read its K operands: the K tile of the next block may
+    // replace this one
+    lds_barrier();
+    if (more) issue_tile(Kx, Ks, j_next, false);
     // mask padded keys (only the last block has any). Branching on the
     // block's valid-key count, which changes with j, keeps the compiler from
     // hoisting loop-invariant compare masks; the lane-half term is folded
@@ -256,7 +303,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = max_halves(mloc);
     const float m_blk = mloc * sl2;
     if (__any(m_blk > m_use + kRescaleSlack)) {
       const float m_new = fmaxf(m_use, m_blk);
@@ -296,17 +343,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_kernel(
       }
     }
     l_run += psum;
-    wait_vmem();  // this wave's loads of the next block have landed in LDS
-    __syncthreads();
+    wait_vmem();  // this wave's copies of the next block's tiles have landed
+    lds_barrier();
     return kb_next;
   };
 
   int kb = next_valid(0);
   if (kb < cnt) {
-    issue_loads(block_of(kb), 0);
+    issue_tile(Kx, Ks, block_of(kb), false);
+    issue_tile(Vx, Vs[0], block_of(kb), true);
     wait_vmem();
   }
-  __syncthreads();
+  lds_barrier();
   while (kb < cnt) {
     kb = process(std::integral_constant<int, 0>{}, kb);
     if (kb >= cnt) break;
