@@ -3,7 +3,8 @@
 Python side of the C-ABI library built from ``csrc/``: the five entry points
 under their C names, plus ``BlockSparseGlobalAttention`` which sequences them
 for one workload shape. Importing this package loads ``libress.so`` and
-raises if it has not been built (``python -m block_sparse_global_amd.build``).
+raises if it has not been built (``python block_sparse_global_amd/build.py``
+or ``python __graft_entry__.py build``).
 """
 
 from ._lib import (  # noqa: F401
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     ress_block_score,
     ress_last_error,
     ress_refine_dropset,
+    ress_refine_workspace_size,
     ress_select_topk,
     ress_sparse_attn_fwd,
     ress_version,

@@ -37,6 +37,7 @@ ENTRY_POINTS = (
     "ress_block_score",
     "ress_select_topk",
     "ress_refine_dropset",
+    "ress_refine_workspace_size",
     "ress_sparse_attn_fwd",
     "ress_last_error",
     "ress_version",
@@ -75,7 +76,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libress is not built ({LIB_PATH} missing); run "
-            "`python -m block_sparse_global_amd.build` first")
+            "`python block_sparse_global_amd/build.py` first")
     lib = ctypes.CDLL(LIB_PATH)
     vp, dp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     i32 = ctypes.c_int32
@@ -85,7 +86,9 @@ def _load():
     lib.ress_select_topk.argtypes = [dp, ress_shape, ip, vp, i32, ip, ip, vp]
     lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
                                         ctypes.c_double, ctypes.c_double, i32, ip, ip,
-                                        dp, dp, vp]
+                                        dp, dp, vp, ctypes.c_size_t, vp]
+    lib.ress_refine_workspace_size.argtypes = [ress_shape]
+    lib.ress_refine_workspace_size.restype = ctypes.c_size_t
     lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
                                          ctypes.c_float, vp, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
@@ -206,10 +209,25 @@ def ress_select_topk(key, shape: Shape, keep: Sequence[int], always_keep, k_max:
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
 
 
+def ress_refine_workspace_size(shape: Shape) -> int:
+    nb = LIB.ress_refine_workspace_size(shape.c())
+    if nb == 0:
+        raise RessError("ress_refine_workspace_size", RESS_ERR_INVALID_ARG,
+                        LIB.ress_last_error().decode(errors="replace"))
+    return int(nb)
+
+
 def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
                         rounds: int, rho: float, eps: float, k_max: int, kept_idx,
-                        kept_cnt, J_init=None, J_final=None, stream=None):
+                        kept_cnt, J_init=None, J_final=None, workspace=None, stream=None):
+    """workspace: a device uint8 tensor of at least ress_refine_workspace_size
+    bytes (allocated here when None)."""
     H, n, D = shape.H, shape.n, shape.D
+    if workspace is None:
+        workspace = torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
+                                device=kept_idx.device if isinstance(kept_idx, torch.Tensor)
+                                else "cuda")
+    ws_ptr = _ptr(workspace, "workspace", torch.uint8)
     f64 = torch.float64
     keep_arr, keep_p = _host_i32(keep, "keep")
     if keep_arr is not None and keep_arr.shape != (H,):
@@ -224,7 +242,7 @@ def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
         float(eps), int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)),
         _ptr(J_init, "J_init", f64, (H, n)), _ptr(J_final, "J_final", f64, (H, n)),
-        _stream(stream)))
+        ws_ptr, workspace.numel(), _stream(stream)))
 
 
 def ress_sparse_attn_fwd(q, k, v, shape: Shape, kept_idx, kept_cnt, k_max: int,

@@ -1,6 +1,6 @@
 """Builds libress.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_global_amd.build
+    python block_sparse_global_amd/build.py
 
 Every HIP source under csrc/ is compiled and linked into one shared library
 next to this file. Packed float32 VALU instructions are disabled for the

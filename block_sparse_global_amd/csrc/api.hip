@@ -225,9 +225,15 @@ int ress_refine_dropset(const double* P, const double* key,
                         const uint8_t* always_keep, int32_t rounds, double rho,
                         double eps, int32_t k_max, int32_t* kept_idx,
                         int32_t* kept_cnt, double* J_init, double* J_final,
-                        void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if (workspace == nullptr) return fail(RESS_ERR_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(RESS_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (workspace_bytes < ress::refine_workspace_bytes(shape))
+    return fail(RESS_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace_bytes, ress::refine_workspace_bytes(shape));
   REQUIRE_PTR(P);
   REQUIRE_PTR(key);
   REQUIRE_PTR(vpool);
@@ -247,9 +253,15 @@ int ress_refine_dropset(const double* P, const double* key,
     return rc;
   hipError_t e = ress::launch_refine(P, key, vpool, vout, M, shape, cfg, rounds,
                                      rho, eps, k_max, kept_idx, kept_cnt,
-                                     J_init, J_final,
+                                     J_init, J_final, workspace,
                                      static_cast<hipStream_t>(stream));
   return hip_status(e, "refine launch");
+}
+
+size_t ress_refine_workspace_size(ress_shape shape) {
+  if (check_shape(shape) != RESS_OK) return 0;
+  ok();
+  return ress::refine_workspace_bytes(shape);
 }
 
 int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,

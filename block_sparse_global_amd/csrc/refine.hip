@@ -2,48 +2,367 @@
 // Vision Transformers", §4.3 "Iterative Residual Restoration", Eq. 10-17,
 // and Appendix E "Fused Kernel Implementation").
 //
-// One workgroup refines TR consecutive query-block rows of one head, with all
-// rounds inside the kernel:
-//   * gains: every thread owns one key block j per pass, streams V_j once
-//     and forms V_j . (M g_r) for all TR rows, then the exact objective
-//     decrease of Eq. 16 for restoring (j in D, Eq. 14) or dropping (j kept,
-//     Eq. 15) j; gains are kept in LDS as 64-bit order keys;
-//   * selection: wave r selects the m_r best restores and the m_r best drops
-//     of row r by an exact radix select (ties: lower block index), with no
-//     workgroup barrier;
-//   * update: g and K move by the swapped blocks only (Eq. 13); G = g^T M g
-//     and J = G / K^2 (Eq. 12) are recomputed; the drop set with the smallest
-//     J seen is kept (track-best).
+// The per-row state (g, M g, K, G, J, the current and the best drop set) lives
+// in a caller-provided workspace in HBM, and each round is two kernels over
+// all rows of all heads:
+//   * gains: for every head, the products V_j . (M g_i) of all key blocks j
+//     and query-block rows i form one n x n x 64 float64 product, computed
+//     as a tiled matrix product (64 x 64 tiles, the dims staged through
+//     LDS); its epilogue turns each product into the exact objective
+//     decrease of Eq. 16 for restoring (j in D_i, Eq. 14) or dropping (j
+//     kept, Eq. 15) j, stored as a 64-bit order key;
+//   * select: one wave per row selects the m_r best restores and the m_r
+//     best drops by an exact radix select (ties: lower block index), moves g
+//     and K by the swapped blocks (Eq. 13), recomputes G = g^T M g and
+//     J = G / K^2 (Eq. 12) and keeps the drop set with the smallest J seen
+//     (track-best).
+// An init kernel builds the starting state from the top-k keep lists and a
+// final kernel writes the best sets back as keep lists.
 // s_j (Eq. 6) comes from the drift key of Eq. 7: s = key * max(1 - P, eps).
-// All reductions have a fixed order, so results are bit-reproducible.
+// Every sum has a fixed order, so results are bit-reproducible.
 #include "ress_internal.h"
 
 namespace ress {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kD = 64;
 
-struct RowScal {
+// Per-row scalars of the refinement state.
+struct alignas(64) RowState {
   double K, G, J, Jbest, J0, vu;  // vu = vout . (M g)
-  int nD, nS, nchg, pad;
+  int32_t nD, nS;                 // sizes of D and of the kept candidates
+};
+
+// Workspace regions (each 256-byte aligned).
+struct RefineWs {
+  uint64_t* gains;  // [H][n][n] order keys of the gains
+  uint8_t* fcur;    // [H][n][fs] 1 = block in the current drop set D
+  uint8_t* fbest;   // [H][n][fs] 1 = block in the best drop set
+  double* g;        // [H][n][64]
+  double* u;        // [H][n][64] M g
+  RowState* rs;     // [H][n]
+};
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Row stride of the flag maps: n rounded up to 16 bytes, so that a row is
+// read with aligned 16-byte loads.
+__host__ __device__ inline int flag_stride(int n) { return (n + 15) & ~15; }
+
+struct WsLayout {
+  size_t gains, fcur, fbest, g, u, rs, total;
+  explicit WsLayout(const ress_shape& s) {
+    const size_t n = (size_t)(s.N_pad / s.B), H = (size_t)s.H;
+    size_t off = 0;
+    gains = off; off += align256(H * n * n * 8);
+    const size_t fs = (size_t)flag_stride((int)n);
+    fcur = off;  off += align256(H * n * fs);
+    fbest = off; off += align256(H * n * fs);
+    g = off;     off += align256(H * n * kD * 8);
+    u = off;     off += align256(H * n * kD * 8);
+    rs = off;    off += align256(H * n * sizeof(RowState));
+    total = off;
+  }
+  RefineWs at(void* base) const {
+    unsigned char* b = static_cast<unsigned char*>(base);
+    return RefineWs{reinterpret_cast<uint64_t*>(b + gains), b + fcur, b + fbest,
+                    reinterpret_cast<double*>(b + g), reinterpret_cast<double*>(b + u),
+                    reinterpret_cast<RowState*>(b + rs)};
+  }
+};
+
+// Swaps of round r for head h: m_r = floor(rho c / 2^(r+1)) (Eq. 17).
+__host__ __device__ inline int swaps_of(const SelConfig& cfg, int h, int round, double rho) {
+  const int c = cfg.keep[h] - cfg.n_always;
+  return (int)floor(rho * (double)c / ldexp(1.0, round + 1));
+}
+
+// u = M g (lane d computes dim d; g in LDS), then G = g^T M g and
+// vu = vout^T M g, every lane holding the totals.
+__device__ inline double gram_apply(const double* __restrict__ Mh, const double* gl,
+                                    double gd, double vod, double* G, double* vu) {
+  const int d = threadIdx.x & 63;
+  double u = gd;
+  if (Mh != nullptr) {
+    const double* Mrow = Mh + (size_t)d * kD;
+    u = 0.0;
+#pragma unroll 8
+    for (int e = 0; e < kD; ++e) u = fma(Mrow[e], gl[e], u);
+  }
+  *G = wave_sum64(gd * u);
+  *vu = wave_sum64(vod * u);
+  return u;
+}
+
+// ---------------------------------------------------------------- init
+// One wave per (row i, head h): D_i = candidates not in the keep list,
+// K = 1 - sum_{j in D} P_ij, and g_i = sum_{j in D} P_ij (vout_i - V_j)
+// (Eq. 5, 10) formed from the kept blocks S_i instead: sum over all j of
+// P_ij (vout_i - V_j) is zero (the row of P sums to one and vout_i is
+// sum_j P_ij V_j), so g_i = sum_{j in S_i} P_ij (V_j - vout_i), about an
+// order of magnitude fewer terms at high sparsity; the two agree to rounding.
+__global__ __launch_bounds__(64) void refine_init_kernel(
+    const double* __restrict__ P, const double* __restrict__ vpool,
+    const double* __restrict__ vout, const double* __restrict__ M, int n,
+    SelConfig cfg, int k_max, const int32_t* __restrict__ kept_idx,
+    const int32_t* __restrict__ kept_cnt, RefineWs ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint8_t* flags = smem;                                                 // [n]
+  int32_t* slist = reinterpret_cast<int32_t*>(smem + ((n + 15) & ~15));  // [n]
+  double* gl = reinterpret_cast<double*>(slist + ((n + 3) & ~3));        // [64]
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const size_t row = (size_t)h * n + i;
+  const double* Prow = P + row * n;
+  const double* Vh = vpool + (size_t)h * n * kD;
+
+  for (int j = lane; j < n; j += 64) flags[j] = sel_always(cfg, j) ? 0 : 1;
+  wave_lds_sync();
+  int cnt = kept_cnt[row];
+  cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
+  for (int q = lane; q < cnt; q += 64) {
+    const int j = kept_idx[row * k_max + q];
+    if (j >= 0 && j < n) flags[j] = 0;
+  }
+  wave_lds_sync();
+
+  uint8_t* fc = ws.fcur + row * flag_stride(n);
+  uint8_t* fb = ws.fbest + row * flag_stride(n);
+  const uint64_t below = (1ull << lane) - 1ull;
+  double ks = 0.0;
+  int nD = 0, nS = 0, pos = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const bool in = j < n;
+    const uint8_t f = in ? flags[j] : 0;
+    if (in) {
+      fc[j] = f;
+      fb[j] = f;
+    }
+    const bool inD = in && f != 0, kept = in && f == 0;
+    if (inD) ks += Prow[j];
+    nD += inD;
+    nS += kept && !sel_always(cfg, j);
+    const uint64_t msk = __ballot(kept);
+    if (kept) slist[pos + __popcll(msk & below)] = j;
+    pos += __popcll(msk);
+  }
+  const double K = 1.0 - wave_sum64(ks);
+  nD = wave_isum64(nD);
+  nS = wave_isum64(nS);
+  wave_lds_sync();
+
+  const int d = lane;
+  const double vod = vout[row * kD + d];
+  double acc = 0.0;
+#pragma unroll 8
+  for (int q = 0; q < pos; ++q) {
+    const int j = slist[q];
+    acc += Prow[j] * (Vh[(size_t)j * kD + d] - vod);
+  }
+  gl[d] = acc;
+  wave_lds_sync();
+  double G, vu;
+  const double u = gram_apply(M ? M + (size_t)h * kD * kD : nullptr, gl, acc, vod, &G, &vu);
+  ws.g[row * kD + d] = acc;
+  ws.u[row * kD + d] = u;
+  if (lane == 0) {
+    RowState st;
+    st.K = K;
+    st.G = G;
+    st.J = (K > 0.0) ? G / (K * K) : INFINITY;
+    st.J0 = st.J;
+    st.Jbest = st.J;
+    st.vu = vu;
+    st.nD = nD;
+    st.nS = nS;
+    ws.rs[row] = st;
+  }
+}
+
+// ---------------------------------------------------------------- gains
+// C[i][j] = u_i . V_j over a 64 x 64 tile (rows i, key blocks j) of one head,
+// the 64 dims staged through LDS in two halves, transposed. Thread (ti, tj)
+// owns rows i0 + ti + 16a and key blocks j0 + tj + 16b (a, b < 4), so that
+// the sixteen lanes of a row group read sixteen consecutive key blocks, in
+// LDS and in the epilogue's loads and stores. Every product is one fma chain
+// over the dims in ascending order. The epilogue issues all its loads first,
+// then forms the gain of each (i, j).
+constexpr int kGT = 64;    // tile edge
+constexpr int kGK = 32;    // dims per LDS stage
+constexpr int kGPad = 66;  // padded row of a transposed stage
+
+__global__ __launch_bounds__(256) void refine_gains_kernel(
+    const double* __restrict__ P, const double* __restrict__ key,
+    const double* __restrict__ vpool, int n, SelConfig cfg, int round, double rho,
+    double eps, RefineWs ws) {
+  const int h = blockIdx.z;
+  if (swaps_of(cfg, h, round, rho) <= 0) return;  // no swaps for this head
+  __shared__ double Ut[kGK][kGPad];
+  __shared__ double Vt[kGK][kGPad];
+  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
+  const int ti = tid >> 4, tj = tid & 15;
+  const double* Uh = ws.u + (size_t)h * n * kD;
+  const double* Vh = vpool + (size_t)h * n * kD;
+
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+
+  // staging: thread t copies row t/4 (clamped to n-1), dims (t%4)*8 .. +7
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const int ri = min(i0 + lr, n - 1), rj = min(j0 + lr, n - 1);
+#pragma unroll
+  for (int kc = 0; kc < kD; kc += kGK) {
+    const double2* us = reinterpret_cast<const double2*>(Uh + (size_t)ri * kD + kc + lc);
+    const double2* vs = reinterpret_cast<const double2*>(Vh + (size_t)rj * kD + kc + lc);
+    double2 xu[4], xv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xu[e] = us[e];
+      xv[e] = vs[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Ut[lc + 2 * e][lr] = xu[e].x;
+      Ut[lc + 2 * e + 1][lr] = xu[e].y;
+      Vt[lc + 2 * e][lr] = xv[e].x;
+      Vt[lc + 2 * e + 1][lr] = xv[e].y;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < kGK; ++k) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = Ut[k][ti + 16 * a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = Vt[k][tj + 16 * b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(bv[b], av[a], acc[a][b]);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: the exact objective decrease of each swap (Eq. 13-16). Out
+  // of range rows and blocks load from a clamped valid address and are not
+  // stored.
+  const int fs = flag_stride(n);
+  double pv[4][4], kv[4][4];
+  uint8_t fv[4][4];
+  double sK[4], sG[4], sJ[4], svu[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const size_t row = (size_t)h * n + min(i0 + ti + 16 * a, n - 1);
+    const RowState* st = ws.rs + row;
+    sK[a] = st->K;
+    sG[a] = st->G;
+    sJ[a] = st->J;
+    svu[a] = st->vu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = min(j0 + tj + 16 * b, n - 1);
+      pv[a][b] = P[row * n + j];
+      kv[a][b] = key[row * n + j];
+      fv[a][b] = ws.fcur[row * fs + j];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ti + 16 * a;
+    const size_t row = (size_t)h * n + i;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tj + 16 * b;
+      const double p = pv[a][b];
+      const double sv = kv[a][b] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
+      const double s2 = sv * sv;
+      const double dMg = p * (svu[a] - acc[a][b]);      // d_j^T M g_i
+      double dJ;
+      if (fv[a][b]) {  // restore (Eq. 13-14), u = +P_j
+        const double dG = -2.0 * dMg + s2;
+        const double Ku = sK[a] + p;
+        dJ = sJ[a] - (sG[a] + dG) / (Ku * Ku);
+      } else {  // drop (Eq. 15), u = -P_j
+        const double dG = 2.0 * dMg + s2;
+        const double Ku = sK[a] - p;
+        dJ = (Ku > 0.0) ? sJ[a] - (sG[a] + dG) / (Ku * Ku) : -INFINITY;
+      }
+      if (i < n && j < n) ws.gains[row * n + j] = order_key(dJ);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- select
+// Bitwise AND / OR of a 64-bit value over the wave.
+__device__ inline uint64_t wave_and64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v &= (uint64_t)__shfl_xor((long long)v, o, 64);
+  return v;
+}
+__device__ inline uint64_t wave_or64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= (uint64_t)__shfl_xor((long long)v, o, 64);
+  return v;
+}
+
+template <int KPL>
+struct SelKeys {  // the lane's keys (block j = lane + 64k), in registers
+  uint64_t v[KPL];
+  __device__ SelKeys(const uint64_t* g, int n, int lane) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int j = lane + 64 * k;
+      v[k] = j < n ? g[j] : 0ull;
+    }
+  }
+  __device__ uint64_t operator()(int k) const { return v[k]; }
+};
+template <>
+struct SelKeys<0> {  // long rows: the keys are read from LDS as needed
+  const uint64_t* g;
+  int lane;
+  __device__ SelKeys(const uint64_t* g_, int, int lane_) : g(g_), lane(lane_) {}
+  __device__ uint64_t operator()(int k) const { return g[lane + 64 * k]; }
 };
 
 // Exact top-m of one row's gains within one wave. Lane l owns key blocks
-// j = l + 64k; bit k of `member` marks membership. Returns the selected
-// elements of this lane as a bitmask over k.
-__device__ uint64_t wave_select(const uint64_t* __restrict__ g, uint64_t member,
-                                int n, int m, uint32_t* __restrict__ whist) {
+// j = l + 64k; bit k of `member` marks membership (members have j < n).
+// Returns the selected elements of this lane as a bitmask over k. Radix
+// select on 8-bit digits; each pass first finds the bits that every key
+// still in play shares and takes its digit just below that common prefix,
+// so no pass is spent on digits that cannot separate the keys (the leading
+// bits of the gains are mostly equal) and the histogram counts spread over
+// many bins. KPL > 0: the lane's KPL >= ceil(n / 64) keys are in registers;
+// KPL = 0: up to 64 per lane, read from LDS.
+template <int KPL>
+__device__ uint64_t wave_select(const SelKeys<KPL>& key, uint64_t member, int n, int m,
+                                uint32_t* __restrict__ whist) {
   const int lane = threadIdx.x & 63;
-  uint64_t selected = 0, inplay = member;
   if (m <= 0) return 0;
+  constexpr int kK = KPL > 0 ? KPL : 64;
+  uint64_t selected = 0, inplay = member;
   int need = m;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (;;) {
+    uint64_t all1 = ~0ull, any1 = 0ull;
+#pragma unroll(KPL > 0 ? KPL : 1)
+    for (int k = 0; k < kK; ++k)
+      if ((inplay >> k) & 1ull) {
+        all1 &= key(k);
+        any1 |= key(k);
+      }
+    const uint64_t diff = wave_and64(all1) ^ wave_or64(any1);
+    if (diff == 0ull) break;  // the keys in play are all equal
+    const int top = 63 - __clzll((long long)diff);
+    const int shift = top >= 7 ? top - 7 : 0;
     for (int b = lane; b < 256; b += 64) whist[b] = 0u;
     wave_lds_sync();
-    for (int k = 0, j = lane; j < n; ++k, j += 64)
-      if ((inplay >> k) & 1ull) atomicAdd(&whist[(uint32_t)(g[j] >> shift) & 255u], 1u);
+#pragma unroll(KPL > 0 ? KPL : 1)
+    for (int k = 0; k < kK; ++k)
+      if ((inplay >> k) & 1ull) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
     wave_lds_sync();
     int c[4];
     int s = 0;
@@ -79,9 +398,10 @@ __device__ uint64_t wave_select(const uint64_t* __restrict__ g, uint64_t member,
     above = __shfl(above, src, 64);
     atd = __shfl(atd, src, 64);
     wave_lds_sync();
-    for (int k = 0, j = lane; j < n; ++k, j += 64) {
+#pragma unroll(KPL > 0 ? KPL : 1)
+    for (int k = 0; k < kK; ++k) {
       if ((inplay >> k) & 1ull) {
-        const int dig = (int)((uint32_t)(g[j] >> shift) & 255u);
+        const int dig = (int)((uint32_t)(key(k) >> shift) & 255u);
         if (dig > dsel) selected |= 1ull << k;
         if (dig != dsel) inplay &= ~(1ull << k);
       }
@@ -101,301 +421,145 @@ __device__ uint64_t wave_select(const uint64_t* __restrict__ g, uint64_t member,
   return selected;
 }
 
-template <int TR>
-__global__ __launch_bounds__(kThreads) void refine_kernel(
-    const double* __restrict__ P, const double* __restrict__ key,
-    const double* __restrict__ vpool, const double* __restrict__ vout,
-    const double* __restrict__ M, int n, SelConfig cfg, int rounds, double rho,
-    double eps, int k_max, int32_t* __restrict__ kept_idx,
-    int32_t* __restrict__ kept_cnt, double* __restrict__ J_init,
-    double* __restrict__ J_final) {
+// One wave per (row i, head h): the swaps of one round and the state update.
+template <int KPL>
+__global__ __launch_bounds__(64) void refine_select_kernel(
+    const double* __restrict__ P, const double* __restrict__ vpool,
+    const double* __restrict__ vout, const double* __restrict__ M, int n,
+    SelConfig cfg, int round, double rho, RefineWs ws) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int m_base = swaps_of(cfg, h, round, rho);
+  if (m_base <= 0) return;  // no swaps for this head
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int n_even = (n + 1) & ~1;  // keeps the regions below 16-byte aligned
-  uint64_t* gains = reinterpret_cast<uint64_t*>(smem);    // [TR][n] (stride n)
-  double* vo = reinterpret_cast<double*>(gains + TR * n_even);  // [TR][64] vout_r
-  double* gv = vo + TR * kD;                               // [TR][64] g_r
-  double* uv = gv + TR * kD;                               // [TR][64] M g_r
-  RowScal* rs = reinterpret_cast<RowScal*>(uv + TR * kD);  // [TR]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(rs + TR);   // [kWaves][256]
-  uint8_t* fcur = reinterpret_cast<uint8_t*>(hist + kWaves * 256);  // [TR][n]
-  uint8_t* fbest = fcur + TR * n;                                   // [TR][n]
+  uint32_t* whist = reinterpret_cast<uint32_t*>(smem);                      // [256]
+  double* gl = reinterpret_cast<double*>(smem + 1024);                      // [64]
+  int32_t* chg = reinterpret_cast<int32_t*>(smem + 1536);                   // [n]
+  uint8_t* flags = smem + 1536 + 4 * ((n + 3) & ~3);                        // [fs]
+  uint64_t* gkeys = reinterpret_cast<uint64_t*>(flags + flag_stride(n));    // [n] (KPL = 0)
 
-  const int h = blockIdx.y;
-  const int i0 = blockIdx.x * TR;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int nrow = min(TR, n - i0);
-  const double* Ph = P + (size_t)h * n * n;
-  const double* Kh = key + (size_t)h * n * n;
+  const size_t row = (size_t)h * n + i;
+  const RowState st = ws.rs[row];
+  const int m = min(m_base, min(st.nD, st.nS));
+  const int fs = flag_stride(n);
+  const uint4* fc = reinterpret_cast<const uint4*>(ws.fcur + row * fs);
+  const uint64_t* grow = ws.gains + row * n;
+  for (int c = lane; c < fs / 16; c += 64) reinterpret_cast<uint4*>(flags)[c] = fc[c];
+  if constexpr (KPL == 0)
+    for (int j = lane; j < n; j += 64) gkeys[j] = grow[j];
+  wave_lds_sync();
+  const SelKeys<KPL> keys(KPL > 0 ? grow : gkeys, n, lane);
+
+  uint64_t memD = 0, memS = 0;
+  for (int k = 0, j = lane; j < n; ++k, j += 64) {
+    if (sel_always(cfg, j)) continue;
+    if (flags[j]) memD |= 1ull << k; else memS |= 1ull << k;
+  }
+  const uint64_t restore = wave_select<KPL>(keys, memD, n, m, whist);
+  const uint64_t drop = wave_select<KPL>(keys, memS, n, m, whist);
+  // change list in ascending block index (sign: +1 for a drop)
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nchg = 0;
+  for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
+    const int j = j0 + lane;
+    const bool rb = (restore >> k) & 1ull, db = (drop >> k) & 1ull;
+    const uint64_t msk = __ballot(rb || db);
+    if (rb || db) {
+      chg[nchg + __popcll(msk & below)] = db ? (j + 1) : -(j + 1);
+      flags[j] = db ? 1 : 0;
+    }
+    nchg += __popcll(msk);
+  }
+  wave_lds_sync();
+
+  // g and K move by the swapped blocks (Eq. 13), in ascending order
+  const int d = lane;
+  const double* Prow = P + row * n;
   const double* Vh = vpool + (size_t)h * n * kD;
-  const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;
-  const int c = cfg.keep[h] - cfg.n_always;
-
-  // ---- initial drop sets D_r = candidates not in the input keep lists
-  for (int idx = tid; idx < TR * kD; idx += kThreads) {
-    const int r = idx / kD;
-    vo[idx] = (r < nrow) ? vout[((size_t)h * n + i0 + r) * kD + idx % kD] : 0.0;
-  }
-  for (int idx = tid; idx < TR * n; idx += kThreads) {
-    const int r = idx / n, j = idx % n;
-    fcur[idx] = (r < nrow && !sel_always(cfg, j)) ? 1 : 0;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < TR * k_max; idx += kThreads) {
-    const int r = idx / k_max, q = idx % k_max;
-    if (r >= nrow) continue;
-    const size_t row = (size_t)h * n + i0 + r;
-    int cnt = kept_cnt[row];
-    cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
-    if (q >= cnt) continue;
-    const int j = kept_idx[row * k_max + q];
-    if (j >= 0 && j < n) fcur[r * n + j] = 0;
-  }
-  __syncthreads();
-
-  // ---- initial g_r = sum_{j in D_r} P_rj (vout_r - V_j) (Eq. 5, 10).
-  // Thread (d, q): row q % TR, slice q / TR of the key blocks; the slices
-  // are then added in ascending order.
-  {
-    double* part = reinterpret_cast<double*>(hist);  // 4 x 64 doubles
-    const int d = tid & 63, q = tid >> 6;
-    const int r = q % TR, sl = q / TR, nsl = kWaves / TR;
-    double acc = 0.0;
-    if (r < nrow) {
-      const double vod = vo[r * kD + d];
-      const double* Prow = Ph + (size_t)(i0 + r) * n;
-      const int per = (n + nsl - 1) / nsl;
-      const int j0 = sl * per, j1 = min(n, j0 + per);
-      // unconditional (predicated) loads so that the unrolled iterations
-      // keep many loads in flight; adding +0 for j outside D leaves acc as is
-#pragma unroll 16
-      for (int j = j0; j < j1; ++j) {
-        const double t = Prow[j] * (vod - Vh[(size_t)j * kD + d]);
-        acc += fcur[r * n + j] ? t : 0.0;
-      }
-    }
-    part[q * kD + d] = acc;
-    __syncthreads();
-    if (tid < TR * kD) {
-      const int rr = tid / kD, dd = tid % kD;
-      double s = 0.0;
-      for (int s2 = 0; s2 < nsl; ++s2) s += part[(s2 * TR + rr) * kD + dd];
-      gv[tid] = s;
-    }
-    __syncthreads();
-  }
-
-  // ---- per-row scalars: wave r owns row r
-  auto row_state = [&](int r, bool first) {
-    double u = gv[r * kD + lane];
-    if (Mh != nullptr) {
-      const double* Mrow = Mh + (size_t)lane * kD;
-      u = 0.0;
-#pragma unroll 8
-      for (int e = 0; e < kD; ++e) u = fma(Mrow[e], gv[r * kD + e], u);
-    }
-    uv[r * kD + lane] = u;
-    const double G = wave_sum64(gv[r * kD + lane] * u);
-    const double vu = wave_sum64(vo[r * kD + lane] * u);
-    if (lane == 0) {
-      RowScal& st = rs[r];
-      st.G = G;
-      st.vu = vu;
-      st.J = (st.K > 0.0) ? G / (st.K * st.K) : INFINITY;
-      if (first) {
-        st.J0 = st.J;
-        st.Jbest = st.J;
-      }
-    }
-  };
-  if (wave < nrow) {
-    const int r = wave;
-    const double* Prow = Ph + (size_t)(i0 + r) * n;
-    double ks = 0.0;
-    int nD = 0, nS = 0;
-    for (int j = lane; j < n; j += 64) {
-      const bool cand = !sel_always(cfg, j);
-      const bool inD = fcur[r * n + j] != 0;
-      if (inD) ks += Prow[j];
-      nD += inD;
-      nS += cand && !inD;
-    }
-    const double K = 1.0 - wave_sum64(ks);
-    nD = wave_isum64(nD);
-    nS = wave_isum64(nS);
-    if (lane == 0) {
-      rs[r].K = K;
-      rs[r].nD = nD;
-      rs[r].nS = nS;
-    }
-    wave_lds_sync();
-    row_state(r, true);
-    for (int j = lane; j < n; j += 64) fbest[r * n + j] = fcur[r * n + j];
-  }
-  __syncthreads();
-
-  for (int round = 0; round < rounds; ++round) {
-    const int m_base = (int)floor(rho * (double)c / ldexp(1.0, round + 1));
-    if (m_base <= 0) continue;  // uniform: every row of the head shares c
-
-    // ---- gains of every (row, key block) from the round-start state
-    double sK[TR], sG[TR], sJ[TR], svu[TR];
+  const double vod = vout[row * kD + d];
+  double g = ws.g[row * kD + d];
+  double dk = 0.0;
+  // batches of 16 changes: all loads of a batch are issued before its sums
+  for (int q0 = 0; q0 < nchg; q0 += 16) {
+    int ev[16];
+    double pv[16], vv[16];
 #pragma unroll
-    for (int r = 0; r < TR; ++r) {
-      sK[r] = rs[r].K; sG[r] = rs[r].G; sJ[r] = rs[r].J; svu[r] = rs[r].vu;
+    for (int t = 0; t < 16; ++t) {
+      const int q = min(q0 + t, nchg - 1);
+      ev[t] = chg[q];
+      const int j = (ev[t] > 0 ? ev[t] : -ev[t]) - 1;
+      pv[t] = Prow[j];
+      vv[t] = Vh[(size_t)j * kD + d];
     }
-    for (int jb = 0; jb < n; jb += kThreads) {
-      // keeps the (loop-invariant) M g reads below inside the loop: hoisting
-      // all TR x 64 of them would not fit in registers
-      asm volatile("" ::: "memory");
-      const int j = jb + tid;
-      if (j >= n || sel_always(cfg, j)) continue;
-      double acc[TR];
 #pragma unroll
-      for (int r = 0; r < TR; ++r) acc[r] = 0.0;
-      const double2* vj = reinterpret_cast<const double2*>(Vh + (size_t)j * kD);
-#pragma unroll 1
-      for (int ch = 0; ch < kD / 16; ++ch) {
-        double2 x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = vj[ch * 8 + e];
-#pragma unroll
-        for (int r = 0; r < TR; ++r) {
-          const double2* ur = reinterpret_cast<const double2*>(uv + r * kD) + ch * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double2 uu = ur[e];
-            acc[r] = fma(x[e].x, uu.x, acc[r]);
-            acc[r] = fma(x[e].y, uu.y, acc[r]);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < TR; ++r) {
-        if (r >= nrow) break;
-        const size_t off = (size_t)(i0 + r) * n + j;
-        const double p = Ph[off];
-        const double s = Kh[off] * fmax(1.0 - p, eps);  // s_rj (Eq. 6)
-        const double s2 = s * s;
-        const double dMg = p * (svu[r] - acc[r]);       // d_j^T M g
-        double dJ;
-        if (fcur[r * n + j]) {  // restore (Eq. 13-14), u = +P_j
-          const double dG = -2.0 * dMg + s2;
-          const double Ku = sK[r] + p;
-          dJ = sJ[r] - (sG[r] + dG) / (Ku * Ku);
-        } else {  // drop (Eq. 15), u = -P_j
-          const double dG = 2.0 * dMg + s2;
-          const double Ku = sK[r] - p;
-          dJ = (Ku > 0.0) ? sJ[r] - (sG[r] + dG) / (Ku * Ku) : -INFINITY;
-        }
-        gains[r * n + j] = order_key(dJ);
-      }
+    for (int t = 0; t < 16; ++t) {
+      if (q0 + t >= nchg) break;
+      const double dj = pv[t] * (vod - vv[t]);
+      g = (ev[t] > 0) ? g + dj : g - dj;
+      dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
     }
-    __syncthreads();
-
-    // ---- selection and set update: wave r owns row r
-    if (wave < nrow) {
-      const int r = wave;
-      RowScal& st = rs[r];
-      const int m = min(m_base, min(st.nD, st.nS));
-      uint64_t memD = 0, memS = 0;
-      for (int k = 0, j = lane; j < n; ++k, j += 64) {
-        if (sel_always(cfg, j)) continue;
-        if (fcur[r * n + j]) memD |= 1ull << k; else memS |= 1ull << k;
-      }
-      uint32_t* whist = hist + wave * 256;
-      const uint64_t restore = wave_select(gains + r * n, memD, n, m, whist);
-      const uint64_t drop = wave_select(gains + r * n, memS, n, m, whist);
-      // change list (ascending block index, sign = +1 for a drop), stored
-      // over this row's gains, which are no longer needed
-      int32_t* chg = reinterpret_cast<int32_t*>(gains + r * n);
-      const double* Prow = Ph + (size_t)(i0 + r) * n;
-      const uint64_t below = (1ull << lane) - 1ull;
-      int pos = 0;
-      double dk = 0.0;
-      for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
-        const int j = j0 + lane;
-        const bool rb = (restore >> k) & 1ull, db = (drop >> k) & 1ull;
-        const uint64_t msk = __ballot(rb || db);
-        if (rb || db) {
-          chg[pos + __popcll(msk & below)] = db ? (j + 1) : -(j + 1);
-          fcur[r * n + j] = db ? 1 : 0;
-          dk += rb ? Prow[j] : -Prow[j];
-        }
-        pos += __popcll(msk);
-      }
-      dk = wave_sum64(dk);
-      if (lane == 0) {
-        st.K += dk;  // Eq. 13: K moves by +P for a restore, -P for a drop
-        st.nchg = pos;
-      }
-    }
-    __syncthreads();
-
-    // ---- g moves by the swapped blocks (Eq. 13), in ascending order
-    if (tid < TR * kD) {
-      const int r = tid / kD, d = tid % kD;
-      if (r < nrow) {
-        const int nchg = rs[r].nchg;
-        const int32_t* chg = reinterpret_cast<const int32_t*>(gains + r * n);
-        const double* Prow = Ph + (size_t)(i0 + r) * n;
-        const double vod = vo[r * kD + d];
-        double g = gv[r * kD + d];
-#pragma unroll 8
-        for (int q = 0; q < nchg; ++q) {
-          const int e = chg[q];
-          const int j = (e > 0 ? e : -e) - 1;
-          const double dj = Prow[j] * (vod - Vh[(size_t)j * kD + d]);
-          g = (e > 0) ? g + dj : g - dj;
-        }
-        gv[r * kD + d] = g;
-      }
-    }
-    __syncthreads();
-    if (wave < nrow) {
-      const int r = wave;
-      row_state(r, false);
-      wave_lds_sync();
-      if (rs[r].J < rs[r].Jbest) {  // track-best, strict
-        for (int j = lane; j < n; j += 64) fbest[r * n + j] = fcur[r * n + j];
-        wave_lds_sync();
-        if (lane == 0) rs[r].Jbest = rs[r].J;
-      }
-    }
-    __syncthreads();
   }
-
-  // ---- keep lists from the best drop sets, ascending, -1 padded
-  if (wave < nrow) {
-    const int r = wave;
-    const size_t row = (size_t)h * n + i0 + r;
-    int32_t* out = kept_idx + row * k_max;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int pos = 0;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-      const int j = j0 + lane;
-      const bool kept = j < n && (sel_always(cfg, j) || !fbest[r * n + j]);
-      const uint64_t msk = __ballot(kept);
-      const int p = pos + __popcll(msk & below);
-      if (kept && p < k_max) out[p] = j;
-      pos += __popcll(msk);
-    }
-    for (int p = pos + lane; p < k_max; p += 64) out[p] = -1;
-    if (lane == 0) {
-      kept_cnt[row] = pos < k_max ? pos : k_max;
-      if (J_init) J_init[row] = rs[r].J0;
-      if (J_final) J_final[row] = rs[r].Jbest;
-    }
+  gl[d] = g;
+  wave_lds_sync();
+  double G, vu;
+  const double u = gram_apply(M ? M + (size_t)h * kD * kD : nullptr, gl, g, vod, &G, &vu);
+  const double K = st.K + dk;
+  const double J = (K > 0.0) ? G / (K * K) : INFINITY;
+  const bool better = J < st.Jbest;  // track-best, strict
+  uint8_t* fcw = ws.fcur + row * fs;
+  uint8_t* fbw = ws.fbest + row * fs;
+  for (int q = lane; q < nchg; q += 64) {
+    const int e = chg[q];
+    const int j = (e > 0 ? e : -e) - 1;
+    fcw[j] = e > 0 ? 1 : 0;
+  }
+  if (better)
+    for (int c = lane; c < fs / 16; c += 64)
+      reinterpret_cast<uint4*>(fbw)[c] = reinterpret_cast<const uint4*>(flags)[c];
+  ws.g[row * kD + d] = g;
+  ws.u[row * kD + d] = u;
+  if (lane == 0) {
+    RowState s2 = st;
+    s2.K = K;
+    s2.G = G;
+    s2.J = J;
+    s2.vu = vu;
+    if (better) s2.Jbest = J;
+    ws.rs[row] = s2;
   }
 }
 
-size_t lds_bytes(int TR, int n) {
-  const size_t n_even = (size_t)((n + 1) & ~1);
-  return (size_t)TR * n_even * 8 + 3 * (size_t)TR * kD * 8 + TR * sizeof(RowScal) +
-         kWaves * 256 * 4 + 2 * (size_t)TR * n;
+// ---------------------------------------------------------------- final
+// Keep lists from the best drop sets, ascending, -1 padded.
+__global__ __launch_bounds__(64) void refine_final_kernel(
+    int n, SelConfig cfg, int k_max, RefineWs ws, int32_t* __restrict__ kept_idx,
+    int32_t* __restrict__ kept_cnt, double* __restrict__ J_init,
+    double* __restrict__ J_final) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const size_t row = (size_t)h * n + i;
+  const uint8_t* fb = ws.fbest + row * flag_stride(n);
+  int32_t* out = kept_idx + row * k_max;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const bool kept = j < n && (sel_always(cfg, j) || !fb[j]);
+    const uint64_t msk = __ballot(kept);
+    const int p = pos + __popcll(msk & below);
+    if (kept && p < k_max) out[p] = j;
+    pos += __popcll(msk);
+  }
+  for (int p = pos + lane; p < k_max; p += 64) out[p] = -1;
+  if (lane == 0) {
+    kept_cnt[row] = pos < k_max ? pos : k_max;
+    const RowState st = ws.rs[row];
+    if (J_init) J_init[row] = st.J0;
+    if (J_final) J_final[row] = st.Jbest;
+  }
 }
 
 }  // namespace
+
+size_t refine_workspace_bytes(const ress_shape& s) { return WsLayout(s).total; }
 
 hipError_t launch_refine(const double* P, const double* key,
                          const double* vpool, const double* vout,
@@ -403,27 +567,32 @@ hipError_t launch_refine(const double* P, const double* key,
                          const SelConfig& cfg, int32_t rounds, double rho,
                          double eps, int32_t k_max, int32_t* kept_idx,
                          int32_t* kept_cnt, double* J_init, double* J_final,
-                         hipStream_t st) {
+                         void* workspace, hipStream_t st) {
   const int n = s.N_pad / s.B;
-  // rows per workgroup: as many as keep the LDS footprint within 64 KB
-  int TR = 4;
-  while (TR > 1 && lds_bytes(TR, n) > 65536) TR >>= 1;
-  dim3 grid((n + TR - 1) / TR, s.H);
-  const size_t lds = lds_bytes(TR, n);
-  switch (TR) {
-#define RESS_CASE(T)                                                          \
-  case T:                                                                     \
-    hipLaunchKernelGGL((refine_kernel<T>), grid, dim3(kThreads), lds, st, P,  \
-                       key, vpool, vout, M, n, cfg, rounds, rho, eps, k_max,  \
-                       kept_idx, kept_cnt, J_init, J_final);                  \
-    break;
-    RESS_CASE(4)
-    RESS_CASE(2)
-    RESS_CASE(1)
-#undef RESS_CASE
-    default:
-      return hipErrorInvalidValue;
+  const RefineWs ws = WsLayout(s).at(workspace);
+  const dim3 rows(n, s.H);
+  const size_t lds_init = (size_t)((n + 15) & ~15) + 4 * (size_t)((n + 3) & ~3) + 512;
+  hipLaunchKernelGGL(refine_init_kernel, rows, dim3(64), lds_init, st, P, vpool, vout, M, n,
+                     cfg, k_max, kept_idx, kept_cnt, ws);
+  const bool keys_in_regs = n <= 17 * 64;
+  const size_t lds_sel = 1536 + 4 * (size_t)((n + 3) & ~3) + (size_t)((n + 15) & ~15) +
+                         (keys_in_regs ? 0 : 8 * (size_t)n);
+  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
+  for (int r = 0; r < rounds; ++r) {
+    int m_max = 0;
+    for (int h = 0; h < s.H; ++h) m_max = max(m_max, swaps_of(cfg, h, r, rho));
+    if (m_max <= 0) continue;  // no head swaps in this round
+    hipLaunchKernelGGL(refine_gains_kernel, tiles, dim3(256), 0, st, P, key, vpool, n, cfg,
+                       r, rho, eps, ws);
+    if (keys_in_regs)
+      hipLaunchKernelGGL((refine_select_kernel<17>), rows, dim3(64), lds_sel, st, P, vpool,
+                         vout, M, n, cfg, r, rho, ws);
+    else
+      hipLaunchKernelGGL((refine_select_kernel<0>), rows, dim3(64), lds_sel, st, P, vpool,
+                         vout, M, n, cfg, r, rho, ws);
   }
+  hipLaunchKernelGGL(refine_final_kernel, rows, dim3(64), 0, st, n, cfg, k_max, ws, kept_idx,
+                     kept_cnt, J_init, J_final);
   return hipGetLastError();
 }
 

@@ -77,7 +77,11 @@ hipError_t launch_refine(const double* P, const double* key,
                          const SelConfig& cfg, int32_t rounds, double rho,
                          double eps, int32_t k_max, int32_t* kept_idx,
                          int32_t* kept_cnt, double* J_init, double* J_final,
-                         hipStream_t st);
+                         void* workspace, hipStream_t st);
+
+// Bytes of the refinement workspace for a shape (the per-row state of all
+// rows of all heads, in HBM).
+size_t refine_workspace_bytes(const ress_shape& s);
 
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
                        const ress_shape& s, const int32_t* kept_idx,

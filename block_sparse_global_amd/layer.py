@@ -21,6 +21,7 @@ from ._lib import (
     ress_block_pool,
     ress_block_score,
     ress_refine_dropset,
+    ress_refine_workspace_size,
     ress_select_topk,
     ress_sparse_attn_fwd,
 )
@@ -60,6 +61,8 @@ class BlockSparseGlobalAttention:
         self.kept_cnt = torch.empty((H, n), dtype=torch.int32, device=device)
         self.J_init = torch.empty((H, n), **f64) if rounds > 0 else None
         self.J_final = torch.empty((H, n), **f64) if rounds > 0 else None
+        self.workspace = (torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
+                                      device=device) if rounds > 0 else None)
         self.lse = (torch.empty((H, Np), dtype=torch.float32, device=device)
                     if with_lse else None)
         self.out = None
@@ -86,7 +89,7 @@ class BlockSparseGlobalAttention:
         ress_refine_dropset(self.P, self.key, self.vpool, self.vout, self.M, self.shape,
                             self.keep, self.always, self.rounds, self.rho, self.eps,
                             self.k_max, self.kept_idx, self.kept_cnt, self.J_init,
-                            self.J_final, stream)
+                            self.J_final, self.workspace, stream)
 
     def attend(self, q, k, v, out, stream=None):
         ress_sparse_attn_fwd(q, k, v, self.shape, self.kept_idx, self.kept_cnt,

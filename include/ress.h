@@ -156,7 +156,11 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
  * by ress_block_score in drift mode. M: device float64 [H][D][D] or NULL
  * (= I). keep, always_keep: HOST, as for ress_select_topk. rounds >= 0,
  * 0 < rho <= 1, eps > 0. kept_idx, kept_cnt: device, in/out. J_init,
- * J_final: device float64 [H][n] or NULL. H <= 64.
+ * J_final: device float64 [H][n] or NULL. H <= 64. workspace: device,
+ * workspace_bytes >= ress_refine_workspace_size(shape), 256-byte aligned;
+ * calls that share one workspace must not overlap. The rounds run as
+ * kernels on `stream` (an init kernel, then a gains and a selection kernel
+ * per round with swaps, then a final kernel).
  */
 int ress_refine_dropset(const double* P, const double* key,
                         const double* vpool, const double* vout,
@@ -164,7 +168,18 @@ int ress_refine_dropset(const double* P, const double* key,
                         const uint8_t* always_keep, int32_t rounds, double rho,
                         double eps, int32_t k_max, int32_t* kept_idx,
                         int32_t* kept_cnt, double* J_init, double* J_final,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ress_refine_workspace_size — bytes of device workspace that
+ * ress_refine_dropset needs for `shape`: the refinement state of every
+ * (head, query-block) row, about 10 n^2 H + 1100 n H bytes (the gains, the
+ * current and best drop sets, g and M g per row). 0 for an invalid shape
+ * (ress_last_error says why). The caller allocates it (256-byte aligned, as
+ * hipMalloc returns) and may reuse it across calls on one stream; its
+ * contents need no initialisation and are garbage after a call.
+ */
+size_t ress_refine_workspace_size(ress_shape shape);
 
 /*
  * ress_sparse_attn_fwd — exact attention over the kept key blocks (ReSS page

@@ -21,8 +21,8 @@ def declared_functions():
 def test_header_declares_the_five_calls():
     names = declared_functions()
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
-              "ress_refine_dropset", "ress_sparse_attn_fwd", "ress_last_error",
-              "ress_version"):
+              "ress_refine_dropset", "ress_refine_workspace_size", "ress_sparse_attn_fwd",
+              "ress_last_error", "ress_version"):
         assert f in names
 
 
@@ -133,15 +133,40 @@ def test_selection_budget_checks():
     d = ctypes.c_double
     e = d(1e-4)
     assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, -1, d(0.5), e,
-                                 3, FAKE, FAKE, None, None, None) == -1            # rounds < 0
+                                 3, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == -1            # rounds < 0
     assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(1.5), e,
-                                 3, FAKE, FAKE, None, None, None) == -1            # rho > 1
+                                 3, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == -1            # rho > 1
     assert L.ress_refine_dropset(FAKE, FAKE, FAKE, None, None, s, ok_keep, alw, 2, d(0.5), e,
-                                 3, FAKE, FAKE, None, None, None) == -1            # vout NULL
+                                 3, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == -1            # vout NULL
     assert L.ress_refine_dropset(FAKE, None, FAKE, FAKE, None, s, ok_keep, alw, 2, d(0.5), e,
-                                 3, FAKE, FAKE, None, None, None) == -1            # key NULL
+                                 3, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == -1            # key NULL
     assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, 2, d(0.5),
-                                 d(0.0), 3, FAKE, FAKE, None, None, None) == -1    # eps <= 0
+                                 d(0.0), 3, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == -1    # eps <= 0
+
+
+def test_refine_workspace_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape(H=2)           # n = 4
+    _, keep = _arr([2, 3], np.int32)
+    _, alw = _arr([0, 0, 0, 1], np.uint8)
+    d = ctypes.c_double
+    need = L.ress_refine_workspace_size(s)
+    # gains (8 n^2 H), two flag maps (n^2 H each), g and M g (512 n H each),
+    # row state (64 n H), every region rounded up to 256 bytes
+    r256 = lambda x: -(-x // 256) * 256  # noqa: E731
+    n, H = 4, 2
+    assert need == r256(8 * n * n * H) + 2 * r256(n * n * H) + 2 * r256(512 * n * H) + \
+        r256(64 * n * H)
+    assert L.ress_refine_workspace_size(_shape(D=32)) == 0 and b.ress_last_error()
+    args = (FAKE, FAKE, FAKE, FAKE, None, s, keep, alw, 2, d(0.5), d(1e-4), 3, FAKE, FAKE,
+            None, None)
+    assert L.ress_refine_dropset(*args, None, need, None) == -1          # no workspace
+    assert "workspace is NULL" in b.ress_last_error()
+    assert L.ress_refine_dropset(*args, ctypes.c_void_p(0x1010), need, None) == -1
+    assert "256-byte" in b.ress_last_error()
+    assert L.ress_refine_dropset(*args, FAKE, need - 1, None) == -1      # too small
+    assert "smaller" in b.ress_last_error()
 
 
 def test_error_string_is_cleared_per_thread():
