@@ -344,11 +344,12 @@ __device__ uint64_t wave_select(const SelKeys<KPL>& key, uint64_t member, int n,
   const int lane = threadIdx.x & 63;
   if (m <= 0) return 0;
   constexpr int kK = KPL > 0 ? KPL : 64;
+  constexpr int kU = KPL > 0 ? KPL : 1;  // unroll factor of the per-key loops
   uint64_t selected = 0, inplay = member;
   int need = m;
   for (;;) {
     uint64_t all1 = ~0ull, any1 = 0ull;
-#pragma unroll(KPL > 0 ? KPL : 1)
+#pragma unroll kU
     for (int k = 0; k < kK; ++k)
       if ((inplay >> k) & 1ull) {
         all1 &= key(k);
@@ -360,7 +361,7 @@ __device__ uint64_t wave_select(const SelKeys<KPL>& key, uint64_t member, int n,
     const int shift = top >= 7 ? top - 7 : 0;
     for (int b = lane; b < 256; b += 64) whist[b] = 0u;
     wave_lds_sync();
-#pragma unroll(KPL > 0 ? KPL : 1)
+#pragma unroll kU
     for (int k = 0; k < kK; ++k)
       if ((inplay >> k) & 1ull) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
     wave_lds_sync();
@@ -398,7 +399,7 @@ __device__ uint64_t wave_select(const SelKeys<KPL>& key, uint64_t member, int n,
     above = __shfl(above, src, 64);
     atd = __shfl(atd, src, 64);
     wave_lds_sync();
-#pragma unroll(KPL > 0 ? KPL : 1)
+#pragma unroll kU
     for (int k = 0; k < kK; ++k) {
       if ((inplay >> k) & 1ull) {
         const int dig = (int)((uint32_t)(key(k) >> shift) & 255u);
@@ -438,19 +439,23 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
   uint64_t* gkeys = reinterpret_cast<uint64_t*>(flags + flag_stride(n));    // [n] (KPL = 0)
 
   const size_t row = (size_t)h * n + i;
-  const RowState st = ws.rs[row];
-  const int m = min(m_base, min(st.nD, st.nS));
   const int fs = flag_stride(n);
   const uint4* fc = reinterpret_cast<const uint4*>(ws.fcur + row * fs);
   const uint64_t* grow = ws.gains + row * n;
   for (int c = lane; c < fs / 16; c += 64) reinterpret_cast<uint4*>(flags)[c] = fc[c];
   if constexpr (KPL == 0)
     for (int j = lane; j < n; j += 64) gkeys[j] = grow[j];
-  wave_lds_sync();
   const SelKeys<KPL> keys(KPL > 0 ? grow : gkeys, n, lane);
+  const RowState st = ws.rs[row];
+  const int m = min(m_base, min(st.nD, st.nS));
+  wave_lds_sync();
 
   uint64_t memD = 0, memS = 0;
-  for (int k = 0, j = lane; j < n; ++k, j += 64) {
+  constexpr int kU = KPL > 0 ? KPL : 4;
+#pragma unroll kU
+  for (int k = 0; k < (KPL > 0 ? KPL : 64); ++k) {
+    const int j = lane + 64 * k;
+    if (j >= n) break;
     if (sel_always(cfg, j)) continue;
     if (flags[j]) memD |= 1ull << k; else memS |= 1ull << k;
   }
@@ -534,9 +539,14 @@ __global__ __launch_bounds__(64) void refine_final_kernel(
     int n, SelConfig cfg, int k_max, RefineWs ws, int32_t* __restrict__ kept_idx,
     int32_t* __restrict__ kept_cnt, double* __restrict__ J_init,
     double* __restrict__ J_final) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const size_t row = (size_t)h * n + i;
-  const uint8_t* fb = ws.fbest + row * flag_stride(n);
+  const int fs = flag_stride(n);
+  const uint4* fsrc = reinterpret_cast<const uint4*>(ws.fbest + row * fs);
+  for (int c = lane; c < fs / 16; c += 64) reinterpret_cast<uint4*>(smem)[c] = fsrc[c];
+  wave_lds_sync();
+  const uint8_t* fb = smem;
   int32_t* out = kept_idx + row * k_max;
   const uint64_t below = (1ull << lane) - 1ull;
   int pos = 0;
@@ -591,7 +601,8 @@ hipError_t launch_refine(const double* P, const double* key,
       hipLaunchKernelGGL((refine_select_kernel<0>), rows, dim3(64), lds_sel, st, P, vpool,
                          vout, M, n, cfg, r, rho, ws);
   }
-  hipLaunchKernelGGL(refine_final_kernel, rows, dim3(64), 0, st, n, cfg, k_max, ws, kept_idx,
+  hipLaunchKernelGGL(refine_final_kernel, rows, dim3(64), (size_t)flag_stride(n), st, n, cfg,
+                     k_max, ws, kept_idx,
                      kept_cnt, J_init, J_final);
   return hipGetLastError();
 }
