@@ -7,8 +7,11 @@
 // q_ij = vout^T M vout - 2 vout^T M V_j + V_j^T M V_j (the Eq. 9 expansion,
 // so no per-pair D-vector is formed), key = P sqrt(max(q,0)) / max(1-P, eps).
 //
-// All reductions run in a fixed order (no atomics), so repeated calls give
-// identical bits.
+// The three n x n x 64 products (logits, vout = P V, (M vout) . V_j) run as
+// tiled matrix products with their elementwise steps in the epilogues; the
+// row softmax is one wave per row. Every output element is one fma chain in
+// ascending index order and every reduction has a fixed order (no
+// atomics), so repeated calls give identical bits.
 #include "ress_internal.h"
 
 namespace ress {
@@ -16,20 +19,6 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kThreads = 256;
-constexpr int kRows = 8;    // query-block rows per workgroup
-constexpr int kJTile = 32;  // key blocks staged per LDS tile
-
-__device__ inline double half_wave_max(double v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 32));
-  return v;
-}
-
-__device__ inline double half_wave_sum(double v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, 32);
-  return v;
-}
 
 __device__ inline double wave_sum(double v) {
 #pragma unroll
@@ -37,64 +26,151 @@ __device__ inline double wave_sum(double v) {
   return v;
 }
 
-// Logits, row max, exponentials and normalisation of kRows map rows. Thread
-// t owns row r = t / 32 and key blocks j = jj, jj + 32, ... (jj = t % 32);
-// the P row itself holds the intermediate values, and each element is only
-// ever touched by its owning thread.
-__global__ __launch_bounds__(kThreads) void map_kernel(
-    const double* __restrict__ qpool, const double* __restrict__ kpool,
-    double scale, int n, double* __restrict__ P) {
-  const int h = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
-  const int t = threadIdx.x;
-  const int r = t >> 5;
-  const int jj = t & 31;
-  const int i = i0 + r;
-
-  __shared__ double qs[kRows][kD];
-  __shared__ double kt[kD][kJTile + 1];
-
-  for (int e = t; e < kRows * kD; e += kThreads) {
-    const int rr = e / kD, d = e % kD;
-    qs[rr][d] = (i0 + rr < n) ? qpool[((size_t)h * n + i0 + rr) * kD + d] : 0.0;
-  }
-  double* Prow = P + ((size_t)h * n + (i < n ? i : 0)) * n;
-  const double* kh = kpool + (size_t)h * n * kD;
-
-  double mx = -INFINITY;
-  for (int j0 = 0; j0 < n; j0 += kJTile) {
-    __syncthreads();
-    // stage 32 key blocks transposed: thread loads 8 dims of one key block
-    {
-      const int kk = t >> 3, d0 = (t & 7) * 8;
-      const int j = j0 + kk;
+__device__ inline double wave_max(double v) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
-        kt[d0 + d][kk] = (j < n) ? kh[(size_t)j * kD + d0 + d] : 0.0;
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---- 64 x 64 tile of A_i . B_j over the 64 dims (A, B row-major [.][64]),
+// the dims staged through LDS in two transposed halves. Thread (ti, tj) owns
+// rows i0 + ti + 16a and columns j0 + tj + 16b (a, b < 4): the sixteen lanes
+// of a row group touch sixteen consecutive columns. acc[a][b] is one fma
+// chain over the dims in ascending order. `stage_a` fills the A half (rows
+// clamped to n-1), so that callers can form A on the fly.
+constexpr int kGT = 64;    // tile edge
+constexpr int kGK = 32;    // dims per LDS stage
+constexpr int kGPad = 66;  // padded row of a transposed stage
+
+struct TileSmem {
+  double At[kGK][kGPad];
+  double Bt[kGK][kGPad];
+};
+
+template <typename StageA>
+__device__ inline void tile_dot(const double* __restrict__ B, int n, int j0, StageA stage_a,
+                                TileSmem& sm, double (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int ti = tid >> 4, tj = tid & 15;
+  const int lr = tid >> 2, lc = (tid & 3) * 8;
+  const int rj = min(j0 + lr, n - 1);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+#pragma unroll
+  for (int kc = 0; kc < kD; kc += kGK) {
+    double xa[8];
+    stage_a(lr, kc + lc, xa);
+    const double2* bs = reinterpret_cast<const double2*>(B + (size_t)rj * kD + kc + lc);
+    double2 xb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xb[e] = bs[e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sm.At[lc + 2 * e][lr] = xa[2 * e];
+      sm.At[lc + 2 * e + 1][lr] = xa[2 * e + 1];
+      sm.Bt[lc + 2 * e][lr] = xb[e].x;
+      sm.Bt[lc + 2 * e + 1][lr] = xb[e].y;
     }
     __syncthreads();
-    const int j = j0 + jj;
-    if (i < n && j < n) {
-      double dot = 0.0;
-#pragma unroll 16
-      for (int d = 0; d < kD; ++d) dot = fma(qs[r][d], kt[d][jj], dot);
-      const double l = scale * dot;
-      Prow[j] = l;
-      mx = fmax(mx, l);
+#pragma unroll 4
+    for (int k = 0; k < kGK; ++k) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = sm.At[k][ti + 16 * a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = sm.Bt[k][tj + 16 * b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+}
+
+// Logits scale * qpool_i . kpool_j of one 64 x 64 tile, written into P.
+__global__ __launch_bounds__(kThreads) void logits_kernel(
+    const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int n,
+    double* __restrict__ P) {
+  __shared__ TileSmem sm;
+  const int h = blockIdx.z;
+  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
+  const double* qh = qpool + (size_t)h * n * kD;
+  auto stage_q = [&](int r, int d0, double (&x)[8]) {
+    const double2* src = reinterpret_cast<const double2*>(qh + (size_t)min(i0 + r, n - 1) * kD + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double2 v = src[e];
+      x[2 * e] = v.x;
+      x[2 * e + 1] = v.y;
+    }
+  };
+  double acc[4][4];
+  tile_dot(kpool + (size_t)h * n * kD, n, j0, stage_q, sm, acc);
+  const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ti + 16 * a;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tj + 16 * b;
+      if (i < n && j < n) P[((size_t)h * n + i) * n + j] = scale * acc[a][b];
     }
   }
-  mx = half_wave_max(mx);
+}
+
+// Row softmax in place, one wave per row: max, exponentials and their sum,
+// normalisation. KPL > 0: the row (KPL >= ceil(n / 64) values per lane) is
+// held in registers; KPL = 0: in LDS (8 n bytes).
+template <int KPL>
+__global__ __launch_bounds__(64) void softmax_rows_kernel(int n, double* __restrict__ P) {
+  extern __shared__ double rowbuf[];
+  const int lane = threadIdx.x;
+  double* Prow = P + ((size_t)blockIdx.y * n + blockIdx.x) * n;
+  constexpr int kK = KPL > 0 ? KPL : 1;
+  double v[kK];
+  double mx = -INFINITY;
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int j = lane + 64 * k;
+      v[k] = j < n ? Prow[j] : -INFINITY;
+      mx = fmax(mx, v[k]);
+    }
+  } else {
+    for (int j = lane; j < n; j += 64) {
+      const double x = Prow[j];
+      rowbuf[j] = x;
+      mx = fmax(mx, x);
+    }
+  }
+  mx = wave_max(mx);
   double sum = 0.0;
-  if (i < n) {
-    for (int j = jj; j < n; j += kJTile) {
-      const double e = exp(Prow[j] - mx);
-      Prow[j] = e;
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int j = lane + 64 * k;
+      v[k] = j < n ? exp(v[k] - mx) : 0.0;
+      sum += v[k];
+    }
+  } else {
+    for (int j = lane; j < n; j += 64) {
+      const double e = exp(rowbuf[j] - mx);
+      rowbuf[j] = e;
       sum += e;
     }
   }
-  sum = half_wave_sum(sum);
-  if (i < n) {
-    for (int j = jj; j < n; j += kJTile) Prow[j] = Prow[j] / sum;
+  sum = wave_sum(sum);
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int j = lane + 64 * k;
+      if (j < n) Prow[j] = v[k] / sum;
+    }
+  } else {
+    for (int j = lane; j < n; j += 64) Prow[j] = rowbuf[j] / sum;
   }
 }
 
@@ -128,100 +204,125 @@ __global__ __launch_bounds__(kThreads) void vmv_kernel(
   if (j < n && lane == 0) vmv[(size_t)h * n + j] = s;
 }
 
-// Drift key of kRows map rows. Phase 1: vout = P V (thread owns dim t%64 of
-// rows t/64 and t/64 + 4). Phase 2: w = M vout and a = vout . w. Phase 3:
-// for every key block, q = a - 2 w . V_j + vmv_j and the key.
-__global__ __launch_bounds__(kThreads) void drift_kernel(
-    const double* __restrict__ P, const double* __restrict__ vpool,
-    const double* __restrict__ M, const double* __restrict__ vmv, int n,
-    double eps, double* __restrict__ key, double* __restrict__ vout) {
+// vout = P V for 32 rows (all 64 dims) per workgroup: thread (ti, tj) owns
+// rows ti and ti + 16 and dims tj + 16b (b < 4); the key blocks stream
+// through LDS 64 at a time. Each vout element is one fma chain over j in
+// ascending order.
+constexpr int kVR = 32;  // rows per workgroup
+constexpr int kVJ = 64;  // key blocks per LDS stage
+
+__global__ __launch_bounds__(kThreads) void vout_kernel(
+    const double* __restrict__ P, const double* __restrict__ vpool, int n,
+    double* __restrict__ vout) {
+  __shared__ double Ps[kVR][kVJ + 1];
+  __shared__ double Vs[kVJ][kD + 2];
   const int h = blockIdx.y;
-  const int i0 = blockIdx.x * kRows;
-  const int t = threadIdx.x;
-  const int d = t & 63;
-  const int rg = t >> 6;  // 0..3
-
-  __shared__ double ps[kRows][kJTile];
-  __shared__ double vt[kJTile][kD + 1];
-  __shared__ double vo[kRows][kD];
-  __shared__ double ws[kRows][kD];
-  __shared__ double as[kRows];
-
+  const int i0 = blockIdx.x * kVR;
+  const int tid = threadIdx.x;
+  const int ti = tid >> 4, tj = tid & 15;
   const double* Ph = P + (size_t)h * n * n;
   const double* Vh = vpool + (size_t)h * n * kD;
-
-  // ---- phase 1: vout rows
-  double acc0 = 0.0, acc1 = 0.0;
-  for (int j0 = 0; j0 < n; j0 += kJTile) {
+  double acc[2][4] = {};
+  for (int jc = 0; jc < n; jc += kVJ) {
+    // P: 32 rows x 64 blocks (8 per thread); V: 64 blocks x 64 dims (16 per thread)
+#pragma unroll
+    for (int e = 0; e < kVR * kVJ / kThreads; ++e) {
+      const int idx = tid + e * kThreads;
+      const int r = idx >> 6, c = idx & 63;
+      const int i = min(i0 + r, n - 1), j = jc + c;
+      Ps[r][c] = j < n ? Ph[(size_t)i * n + j] : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < kVJ * kD / (2 * kThreads); ++e) {
+      const int idx = tid + e * kThreads;
+      const int r = idx >> 5, c2 = idx & 31;
+      const int j = min(jc + r, n - 1);
+      const double2 x = reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[c2];
+      Vs[r][2 * c2] = x.x;
+      Vs[r][2 * c2 + 1] = x.y;
+    }
     __syncthreads();
-    {
-      const int rr = t >> 5, jj = t & 31;
-      const int i = i0 + rr, j = j0 + jj;
-      ps[rr][jj] = (i < n && j < n) ? Ph[(size_t)i * n + j] : 0.0;
-    }
-    for (int e = t; e < kJTile * kD; e += kThreads) {
-      const int jj = e >> 6, dd = e & 63;
-      const int j = j0 + jj;
-      vt[jj][dd] = (j < n) ? Vh[(size_t)j * kD + dd] : 0.0;
-    }
-    __syncthreads();
-    const int jmax = min(kJTile, n - j0);
-    for (int jj = 0; jj < jmax; ++jj) {
-      acc0 = fma(ps[rg][jj], vt[jj][d], acc0);
-      acc1 = fma(ps[rg + 4][jj], vt[jj][d], acc1);
-    }
-  }
-  vo[rg][d] = acc0;
-  vo[rg + 4][d] = acc1;
-  if (i0 + rg < n) vout[((size_t)h * n + i0 + rg) * kD + d] = acc0;
-  if (i0 + rg + 4 < n) vout[((size_t)h * n + i0 + rg + 4) * kD + d] = acc1;
-  __syncthreads();
-
-  // ---- phase 2: w = M vout, a = vout . w
-  {
-    double w0 = vo[rg][d], w1 = vo[rg + 4][d];
-    if (M != nullptr) {
-      const double* Mrow = M + ((size_t)h * kD + d) * kD;
-      w0 = 0.0;
-      w1 = 0.0;
-#pragma unroll 8
-      for (int e = 0; e < kD; ++e) {
-        const double m = Mrow[e];
-        w0 = fma(m, vo[rg][e], w0);
-        w1 = fma(m, vo[rg + 4][e], w1);
+    const int kmax = min(kVJ, n - jc);
+    for (int k = 0; k < kmax; ++k) {
+      const double p0 = Ps[ti][k], p1 = Ps[ti + 16][k];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const double vv = Vs[k][tj + 16 * b];
+        acc[0][b] = fma(p0, vv, acc[0][b]);
+        acc[1][b] = fma(p1, vv, acc[1][b]);
       }
     }
-    ws[rg][d] = w0;
-    ws[rg + 4][d] = w1;
-    const double a0 = wave_sum(vo[rg][d] * w0);
-    const double a1 = wave_sum(vo[rg + 4][d] * w1);
-    if (d == 0) {
-      as[rg] = a0;
-      as[rg + 4] = a1;
-    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int i = i0 + ti + 16 * a;
+    if (i < n)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) vout[((size_t)h * n + i) * kD + tj + 16 * b] = acc[a][b];
+  }
+}
 
-  // ---- phase 3: keys. Thread owns row t/32 and key blocks j0 + t%32.
-  const int r = t >> 5;
-  const int jj = t & 31;
-  const int i = i0 + r;
-  for (int j0 = 0; j0 < n; j0 += kJTile) {
-    __syncthreads();
-    for (int e = t; e < kJTile * kD; e += kThreads) {
-      const int kk = e >> 6, dd = e & 63;
-      const int j = j0 + kk;
-      vt[kk][dd] = (j < n) ? Vh[(size_t)j * kD + dd] : 0.0;
+// Drift key of one 64 x 64 tile: w_i = M vout_i (vout_i when M is NULL) is
+// formed while staging, a_i = vout_i . w_i, then per (i, j)
+// q = a_i - 2 w_i . V_j + vmv_j and key = P sqrt(max(q, 0)) / max(1 - P, eps).
+__global__ __launch_bounds__(kThreads) void key_kernel(
+    const double* __restrict__ P, const double* __restrict__ vpool,
+    const double* __restrict__ M, const double* __restrict__ vmv,
+    const double* __restrict__ vout, int n, double eps, double* __restrict__ key) {
+  __shared__ TileSmem sm;
+  __shared__ double apart[2][kGT][4];
+  const int h = blockIdx.z;
+  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
+  const int tid = threadIdx.x;
+  const double* voh = vout + (size_t)h * n * kD;
+  const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;
+  // stage w_i dims d0 .. d0+7 of row r; the partial vout . w over those
+  // dims goes to apart[half][r][thread's quarter]
+  auto stage_w = [&](int r, int d0, double (&x)[8]) {
+    const double* vr = voh + (size_t)min(i0 + r, n - 1) * kD;
+    double vo8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vo8[e] = vr[d0 + e];
+    if (Mh == nullptr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = vo8[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double* Mrow = Mh + (size_t)(d0 + e) * kD;
+        double w = 0.0;
+#pragma unroll 8
+        for (int f = 0; f < kD; ++f) w = fma(Mrow[f], vr[f], w);
+        x[e] = w;
+      }
     }
-    __syncthreads();
-    const int j = j0 + jj;
-    if (i < n && j < n) {
-      double wv = 0.0;
-#pragma unroll 16
-      for (int e = 0; e < kD; ++e) wv = fma(ws[r][e], vt[jj][e], wv);
-      double q = as[r] - 2.0 * wv + vmv[(size_t)h * n + j];
-      q = fmax(q, 0.0);
-      const double p = Ph[(size_t)i * n + j];
-      key[((size_t)h * n + i) * n + j] = p * sqrt(q) / fmax(1.0 - p, eps);
+    double pa = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pa = fma(vo8[e], x[e], pa);
+    apart[d0 >= kGK][r][(d0 % kGK) / 8] = pa;
+  };
+  double acc[4][4];
+  tile_dot(vpool + (size_t)h * n * kD, n, j0, stage_w, sm, acc);
+  const int ti = tid >> 4, tj = tid & 15;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int r = ti + 16 * a;
+    const int i = i0 + r;
+    double ai = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) ai += apart[hh][r][q4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tj + 16 * b;
+      if (i < n && j < n) {
+        const size_t off = ((size_t)h * n + i) * n + j;
+        const double q = fmax(ai - 2.0 * acc[a][b] + vmv[(size_t)h * n + j], 0.0);
+        const double p = P[off];
+        key[off] = p * sqrt(q) / fmax(1.0 - p, eps);
+      }
     }
   }
 }
@@ -232,9 +333,13 @@ hipError_t launch_block_map(const double* qpool, const double* kpool,
                             const ress_shape& s, double scale, double* P,
                             hipStream_t st) {
   const int n = s.N_pad / s.B;
-  dim3 grid((n + kRows - 1) / kRows, s.H);
-  hipLaunchKernelGGL(map_kernel, grid, dim3(kThreads), 0, st, qpool, kpool,
-                     scale, n, P);
+  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
+  hipLaunchKernelGGL(logits_kernel, tiles, dim3(kThreads), 0, st, qpool, kpool, scale, n, P);
+  const dim3 rows(n, s.H);
+  if (n <= 17 * 64)
+    hipLaunchKernelGGL((softmax_rows_kernel<17>), rows, dim3(64), 0, st, n, P);
+  else
+    hipLaunchKernelGGL((softmax_rows_kernel<0>), rows, dim3(64), (size_t)n * 8, st, n, P);
   return hipGetLastError();
 }
 
@@ -262,9 +367,11 @@ hipError_t launch_drift(const double* P, const double* vpool, const double* M,
                         const double* vmv, const ress_shape& s, double eps,
                         double* key, double* vout, hipStream_t st) {
   const int n = s.N_pad / s.B;
-  dim3 grid((n + kRows - 1) / kRows, s.H);
-  hipLaunchKernelGGL(drift_kernel, grid, dim3(kThreads), 0, st, P, vpool, M,
-                     vmv, n, eps, key, vout);
+  hipLaunchKernelGGL(vout_kernel, dim3((n + kVR - 1) / kVR, s.H), dim3(kThreads), 0, st, P,
+                     vpool, n, vout);
+  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
+  hipLaunchKernelGGL(key_kernel, tiles, dim3(kThreads), 0, st, P, vpool, M, vmv, vout, n, eps,
+                     key);
   return hipGetLastError();
 }
 
