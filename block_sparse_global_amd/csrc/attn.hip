@@ -102,18 +102,6 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// vmcnt(N): wait until at most N of this wave's vector memory operations
-// (here: tile copies into LDS) are outstanding; they complete in order.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008;
-constexpr int kSgValu = 0x002;
-
 // max of a lane's value and the one of lane l ^ 32 (v_permlane32_swap)
 __device__ inline float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -199,44 +187,50 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   };
   auto block_of = [&](int kb) { return list ? list[kb] : kb; };
 
-  // ---- staging of K or V rows of block j into an LDS buffer, in halves of
-  // BLK/2 rows. For half hh, each wave copies 2 windows of 8 rows (BLK/32
-  // waves, BLK/16 windows); in window it, lane l fills row
-  // r = (BLK/2)*hh + 16*w + 8*it + l/8 at physical chunk l%8, i.e. logical
-  // chunk (l%8) ^ swz(r). For V, swz(r) = 2*((l/8)&3); for K,
-  // swz(r) = (l/16) ^ (4*it). So two per-lane offsets (it = 0, 1) plus
-  // compile-time row steps cover every window. Rows past N (last block
-  // only) are read from row N-1: finite data whose scores are masked to
-  // -inf, so p = 0 multiplies a finite V row.
-  constexpr int kHalf = BLK / 2;
-  const int row0 = 16 * w + (lane >> 3);
+  // ---- staging of the K or V tile of block j into an LDS buffer. Each wave
+  // copies 4 windows of 8 rows; in window it, lane l fills row
+  // r = 32*w + 8*it + l/8 at physical chunk l%8, i.e. logical chunk
+  // (l%8) ^ swz(r). For V, swz(r) = 2*((l/8)&3) does not depend on it; for
+  // K, swz(r) = (l/16) ^ (4*(it&1)). So two per-lane offsets (windows 0 and
+  // 1) plus compile-time row steps cover all windows. Rows past N (last
+  // block only) are read from row N-1: finite data whose scores are masked
+  // to -inf, so p = 0 multiplies a finite V row.
+  const int row0 = 32 * w + (lane >> 3);
   const int kgo0 = row0 * kD + (((lane & 7) ^ (lane >> 4)) * 8);
   const int kgo1 = (row0 + 8) * kD + (((lane & 7) ^ (lane >> 4) ^ 4) * 8);
   const int vgo0 = row0 * kD + (((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 8);
-  auto issue_half = [&](const Tin* X, uint16_t* dst, int j, int hh, bool is_v) {
+  auto tile_off = [&](int it, bool is_v) {
+    return is_v ? vgo0 + 8 * it * kD : ((it & 1) ? kgo1 : kgo0) + 16 * (it >> 1) * kD;
+  };
+  auto issue_tile = [&](const Tin* X, uint16_t* dst, int j, bool is_v) {
     if constexpr (sizeof(Tin) == 2) {
       // block base (uniform) + 32-bit per-lane byte offset: the copies use
       // the scalar-base addressing form
       const char* base = reinterpret_cast<const char*>(
           X + head_off + (size_t)__builtin_amdgcn_readfirstlane(j) * BLK * kD);
       const bool full = (j + 1) * BLK <= N;
+      if (full) {
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        int off = (is_v ? vgo0 + 8 * it * kD : (it ? kgo1 : kgo0)) + kHalf * hh * kD;
-        if (!full) {
-          const int r = row0 + 8 * it + kHalf * hh;
-          off += (min(r, N - 1 - j * BLK) - r) * kD;
+        for (int it = 0; it < 4; ++it) {
+          const uint32_t off = 2u * (uint32_t)tile_off(it, is_v);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
         }
-        gload_lds16(reinterpret_cast<const uint16_t*>(base + 2u * (uint32_t)off),
-                    dst + ((BLK / 16) * hh + 2 * w + it) * 512);
+      } else {
+        const int last = N - 1 - j * BLK;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = row0 + 8 * it;
+          const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) + (min(r, last) - r) * kD);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
+        }
       }
     } else {
       // float32 inputs: rounded to bf16 (nearest even) through registers
       const Tin* base = X + head_off + (size_t)j * BLK * kD;
 #pragma unroll
-      for (int it = 0; it < kHalf * 8 / kThreads; ++it) {
+      for (int it = 0; it < BLK * 8 / kThreads; ++it) {
         const int idx = tid + it * kThreads;
-        const int r = kHalf * hh + (idx >> 3), c = idx & 7;
+        const int r = idx >> 3, c = idx & 7;
         const int rr = min(r, N - 1 - j * BLK);
         const int sw = is_v ? v_swz(r) : k_swz(r);
         *reinterpret_cast<uint4*>(&dst[r * kD + ((c ^ sw) * 8)]) =
@@ -260,137 +254,104 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
                  (q & 1) * 4;
   }
 
-  // S^T tile kt (keys 32*kt + 0..31) of the block in Ks
-  auto s_tile = [&](int kt) {
-    bf16x8 ka[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[kt * 32 * kD + koff[ks]]));
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
-    return acc;
-  };
-
   // ---- one kept block, V from buffer B (compile-time, so all LDS offsets
-  // are immediates); returns the next list position. The softmax runs per
-  // 32-key tile; while tile kt's exponentials and P.V products run, the
-  // S^T product of tile kt+1 is issued in between (instruction groups
-  // interleaved below), so the matrix cores and the vector ALUs overlap.
-  // K rows 0..BLK/2-1 are free once tile 1's product is issued and rows
-  // BLK/2.. once tile 3's is: each half of the next block's K is copied in
-  // as soon as its rows are free.
+  // are immediates); returns the next list position
   auto process = [&](auto bufc, int kb) {
     constexpr int B = decltype(bufc)::value;
     const int j = block_of(kb);
     const int kb_next = next_valid(kb + 1);
     const bool more = kb_next < cnt;
     const int j_next = more ? block_of(kb_next) : 0;
-    if (more) {
-      issue_half(Vx, Vs[B ^ 1], j_next, 0, true);
-      issue_half(Vx, Vs[B ^ 1], j_next, 1, true);
-    }
-    // K half hh has been read by every wave once the product of its last
-    // tile is issued: copy the next block's rows over it. Before half 0 is
-    // released, wait for this block's half 1 (copied during the previous
-    // block), which the products after the barrier read.
-    auto release_k = [&](int hh) {
-      if (hh == 0) {
-        if (more) wait_vmcnt<4>(); else wait_vmcnt<0>();
-      }
-      lds_barrier();
-      if (more) issue_half(Kx, Ks, j_next, hh, false);
-    };
-    const int live_keys = N - j * BLK;
+    if (more) issue_tile(Vx, Vs[B ^ 1], j_next, true);
+
+    // S^T = K Q^T
     f32x16 s[kKT];
-    s[0] = s_tile(0);
-    if (kKT == 2) release_k(0);
-    float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
-      // mask padded keys (only the last block has any). Branching on the
-      // block's valid-key count keeps the compiler from hoisting
-      // loop-invariant compare masks; the lane-half term is folded into the
-      // limit so that the compares use immediate key offsets only.
-      if (live_keys < BLK) {
-        const int lim = live_keys - 4 * half - 32 * kt;
+      bf16x8 ka[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[kt * 32 * kD + koff[ks]]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s[kt], 0, 0, 0);
+    }
+    // every wave has read its K operands: the K tile of the next block may
+    // replace this one
+    lds_barrier();
+    if (more) issue_tile(Kx, Ks, j_next, false);
+    // mask padded keys (only the last block has any). Branching on the
+    // block's valid-key count, which changes with j, keeps the compiler from
+    // hoisting loop-invariant compare masks; the lane-half term is folded
+    // into the limit so that the compares use immediate key offsets only.
+    const int live_keys = N - j * BLK;
+    if (live_keys < BLK) {
+      const int lim = live_keys - 4 * half;
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kc = 8 * (r >> 2) + (r & 3);
+          const int kc = 32 * kt + 8 * (r >> 2) + (r & 3);
           if (kc >= lim) s[kt][r] = -INFINITY;
         }
-      }
-      // online softmax (per lane = per query), lazy rescaling
-      float mloc = -INFINITY;
+    }
+    // online softmax (per lane = per query), lazy rescaling
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
-      mloc = max_halves(mloc);
-      const float m_blk = mloc * sl2;
-      if (__any(m_blk > m_use + kRescaleSlack)) {
-        const float m_new = fmaxf(m_use, m_blk);
-        const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
-        l_run *= alpha;
-        psum *= alpha;
+    mloc = max_halves(mloc);
+    const float m_blk = mloc * sl2;
+    if (__any(m_blk > m_use + kRescaleSlack)) {
+      const float m_new = fmaxf(m_use, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        m_use = m_new;
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      m_use = m_new;
+    }
+    // per 16-key step: P = exp2(S*scale*log2e - m) as bf16, then
+    // O^T += V^T P^T with the V^T operand read transposed from LDS
+    float psum = 0.f;
+#pragma unroll
+    for (int step = 0; step < 2 * kKT; ++step) {
+      const int kt = step >> 1, hf = step & 1;
+      bf16x8 pb;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        pb[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
+      // row sum of the very bf16 weights the PV product uses, two per
+      // instruction (bf16 dot product with (1, 1), float32 accumulation)
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        const bf16x2 pp = {pb[r], pb[r + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
       }
-      if (kt + 1 < kKT) s[kt + 1] = s_tile(kt + 1);
-      // two 16-key steps: P = exp2(S*scale*log2e - m) as bf16, then
-      // O^T += V^T P^T with the V^T operand read transposed from LDS
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int step = 2 * kt + hf;
-        bf16x8 pb;
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          pb[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
-        // row sum of the very bf16 weights the PV product uses, two per
-        // instruction (bf16 dot product with (1, 1), float32 accumulation)
-#pragma unroll
-        for (int r = 0; r < 8; r += 2) {
-          const bf16x2 pp = {pb[r], pb[r + 1]};
-          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const uint16_t* vp = &Vs[B][step * 16 * kD + voff[dt]];
-          const v4i16 lo = tr_read(vp);           // keys 16*step + 4*half + 0..3
-          const v4i16 hi = tr_read(vp + 8 * kD);  // keys 16*step + 8 + 4*half + 0..3
-          const v8i16 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, lohi);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vp = &Vs[B][step * 16 * kD + voff[dt]];
+        const v4i16 lo = tr_read(vp);           // keys 16*step + 4*half + 0..3
+        const v4i16 hi = tr_read(vp + 8 * kD);  // keys 16*step + 8 + 4*half + 0..3
+        const v8i16 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, lohi);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
       }
-      if (kt + 1 < kKT) {
-        // S MFMA / 8 VALU, four times (the next tile's product between
-        // this tile's exponentials), then the rest
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSgValu, 8, 0);
-        }
-      }
-      if (kt == kKT / 2 - 2) release_k(0);
-      if (kt == kKT - 2) release_k(1);
     }
     l_run += psum;
-    if (more) {
-      wait_vmcnt<2>();  // V and K rows 0..BLK/2-1 of the next block landed
-      lds_barrier();
-    }
+    wait_vmem();  // this wave's copies of the next block's tiles have landed
+    lds_barrier();
     return kb_next;
   };
 
   int kb = next_valid(0);
   if (kb < cnt) {
-    issue_half(Kx, Ks, block_of(kb), 0, false);
-    issue_half(Kx, Ks, block_of(kb), 1, false);
-    issue_half(Vx, Vs[0], block_of(kb), 0, true);
-    issue_half(Vx, Vs[0], block_of(kb), 1, true);
+    issue_tile(Kx, Ks, block_of(kb), false);
+    issue_tile(Vx, Vs[0], block_of(kb), true);
     wait_vmem();
   }
   lds_barrier();
