@@ -8,7 +8,8 @@ default workload is 100 views x 1374 tokens (137,400 tokens, 16 heads,
 head_dim 64, block 128, 90% sparsity, drift score + 3 refinement rounds),
 the only configuration that exercises every step. Printed: one JSON line with
 the kept-block attention throughput of the whole step (kept FLOPs / step
-time), the layer latency against the dense kernel at 8/32/100 views, the
+time), the layer latency against the dense kernel at 8/32/100 views (and 200
+views with either score), the
 roofline of the attention kernel (timed with HIP events on the launch
 stream) and the CPU oracle timed on a bounded sample.
 """
@@ -39,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "29619b6aef27ed59c110c48fa62af72501df52e2e11d07dd48f32df7e60febe7",
-    "read_bytes": 7943460635,
+    "source_sha256": "7311cc79cd2f57b47c70b605d450cbd18b58c35485cfe61117813fe045a38962",
+    "read_bytes": 8263645558,
     "write_bytes": 281542656,
 }
 
@@ -62,18 +63,20 @@ def dense_flops(w):
     return 4.0 * w.head_dim * w.heads * float(w.N) * float(w.N)
 
 
-def setup(name):
+def setup(name, mode=None, x=None):
     import torch
 
     import block_sparse_global_amd as bsg
     import synth
     w = synth.get_workload(name)
-    x = synth.make_inputs(w)
+    if x is None:
+        x = synth.make_inputs(w)
     to_t = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()) \
         if w.dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
     q, k, v = to_t(x["q"]), to_t(x["k"]), to_t(x["v"])
     shape = bsg.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
-    mode = "drift" if w.score in ("drift", "both") else "prob"
+    if mode is None:
+        mode = "drift" if w.score in ("drift", "both") else "prob"
     layer = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
                                            rounds=w.rounds if mode == "drift" else 0,
                                            rho=w.rho)
@@ -221,20 +224,39 @@ def main():
 
     sweep = {}
     if not args.no_sweep:
-        for name in ("views8", "views32", "views100"):
-            if name == args.workload and not args.no_dense:
-                sweep[name] = {"layer_ms": ms_step, "dense_ms": dense_ms}
+        # 8 / 32 / 100 views (the headline lines) and 200 views with both
+        # scores; each line: layer time, dense time, the attention kernel alone
+        lines = [("views8", None), ("views32", None), ("views100", None),
+                 ("views200", "prob"), ("views200", "drift")]
+        x200 = None
+        for name, mode in lines:
+            key = name if mode is None else f"{name}-{mode}"
+            if name == args.workload and mode is None and not args.no_dense:
+                sweep[key] = {"layer_ms": ms_step, "dense_ms": dense_ms, "attn_ms": attn_ms,
+                              "kept_flop": kf}
             else:
-                w2, x2, shape2, layer2, (q2, k2, v2), out2 = setup(name)
+                if name == "views200" and x200 is None:
+                    import synth
+                    x200 = synth.make_inputs(synth.get_workload(name))
+                w2, x2, shape2, layer2, (q2, k2, v2), out2 = setup(
+                    name, mode, x200 if name == "views200" else None)
                 for _ in range(2):
                     layer2(q2, k2, v2, out2)
-                l_ms = time_events(lambda: layer2(q2, k2, v2, out2), 10)
+                reps = 3 if name == "views200" else 10
+                l_ms = time_events(lambda: layer2(q2, k2, v2, out2), reps)
+                a_ms = time_events(lambda: layer2.attend(q2, k2, v2, out2), reps)
+                kf2 = kept_flops(w2, layer2.kept_idx.cpu().numpy(), layer2.kept_cnt.cpu().numpy())
                 d2 = torch.empty_like(q2)
-                d_ms = time_events(lambda: bsg.dense_attention(q2, k2, v2, shape2, d2), 5)
-                sweep[name] = {"layer_ms": l_ms, "dense_ms": d_ms}
+                d_ms = time_events(lambda: bsg.dense_attention(q2, k2, v2, shape2, d2),
+                                   2 if name == "views200" else 5)
+                sweep[key] = {"layer_ms": l_ms, "dense_ms": d_ms, "attn_ms": a_ms,
+                              "kept_flop": kf2}
                 del layer2, q2, k2, v2, out2, d2
-            sweep[name]["speedup_vs_dense"] = sweep[name]["dense_ms"] / sweep[name]["layer_ms"]
-        torch.cuda.empty_cache()
+                torch.cuda.empty_cache()
+            e = sweep[key]
+            e["speedup_vs_dense"] = e["dense_ms"] / e["layer_ms"]
+            e["attn_tflops"] = e["kept_flop"] / (e["attn_ms"] * 1e-3) / 1e12
+        x200 = None
 
     achieved = kf / (attn_ms * 1e-3) / 1e12
     res = {

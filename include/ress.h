@@ -183,8 +183,8 @@ size_t ress_refine_workspace_size(ress_shape shape);
 
 /*
  * ress_sparse_attn_fwd — exact attention over the kept key blocks (ReSS page
- * §3 step (3): softmax renormalised among the selected blocks, "as if the
- * unselected blocks never existed"; dense global attention when kept_idx is
+ * §3 step (3): softmax renormalised among the selected blocks alone, the
+ * unselected blocks contributing nothing; dense global attention when kept_idx is
  * NULL).
  *
  *   out[h][t] = sum_u softmax_u(scale q[h][t] . k[h][u]) v[h][u]

@@ -314,7 +314,7 @@ def masked_attention(q, k, v, kept, N: int, B: int, scale: float,
                      blocks=None):
     """O[h, t] = sum_u softmax_u(scale q_t . k_u) v_u over the valid keys u < N
     of the blocks kept for t's query block; softmax renormalised among them
-    (ReSS page §3: "as if the unselected blocks never existed").
+    (ReSS page §3: the unselected blocks take no part in the softmax).
 
     q, k, v: float64 [H][N_pad][D]; kept: bool [H][n][n]. Padded query rows
     are 0. ``blocks``: optional list of (h, i) query blocks to compute (the
