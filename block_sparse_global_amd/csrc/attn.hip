@@ -264,19 +264,28 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     const int j_next = more ? block_of(kb_next) : 0;
     if (more) issue_tile(Vx, Vs[B ^ 1], j_next, true);
 
-    // S^T = K Q^T
+    // S^T = K Q^T; the K operands of tile kt+1 are read while tile kt's
+    // MFMAs run
     f32x16 s[kKT];
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      ka[0][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[koff[ks]]));
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
-      bf16x8 ka[4];
+      if (kt + 1 < kKT) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[kt * 32 * kD + koff[ks]]));
+        for (int ks = 0; ks < 4; ++ks)
+          ka[(kt + 1) & 1][ks] = as_bf16x8(
+              *reinterpret_cast<const uint4*>(&Ks[(kt + 1) * 32 * kD + koff[ks]]));
+      }
+      // keeps those reads ahead of this tile's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt & 1][ks], qb[ks], s[kt], 0, 0, 0);
     }
     // every wave has read its K operands: the K tile of the next block may
     // replace this one
@@ -318,9 +327,24 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     // per 16-key step: P = exp2(S*scale*log2e - m) as bf16, then
     // O^T += V^T P^T with the V^T operand read transposed from LDS
     float psum = 0.f;
+    // V^T operands of 16-key step st (both 32-dim halves); those of step
+    // st+1 are read while step st computes
+    auto v_operands = [&](int st, bf16x8 (&va)[2]) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vp = &Vs[B][st * 16 * kD + voff[dt]];
+        const v4i16 lo = tr_read(vp);           // keys 16*st + 4*half + 0..3
+        const v4i16 hi = tr_read(vp + 8 * kD);  // keys 16*st + 8 + 4*half + 0..3
+        va[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    bf16x8 vops[2][2];
+    v_operands(0, vops[0]);
 #pragma unroll
     for (int step = 0; step < 2 * kKT; ++step) {
       const int kt = step >> 1, hf = step & 1;
+      if (step + 1 < 2 * kKT) v_operands(step + 1, vops[(step + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keeps those reads ahead of this step
       bf16x8 pb;
 #pragma unroll
       for (int r = 0; r < 8; ++r)
@@ -333,14 +357,8 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
         psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
       }
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const uint16_t* vp = &Vs[B][step * 16 * kD + voff[dt]];
-        const v4i16 lo = tr_read(vp);           // keys 16*step + 4*half + 0..3
-        const v4i16 hi = tr_read(vp + 8 * kD);  // keys 16*step + 8 + 4*half + 0..3
-        const v8i16 lohi = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, lohi);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < 2; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[step & 1][dt], pb, o[dt], 0, 0, 0);
     }
     l_run += psum;
     wait_vmem();  // this wave's copies of the next block's tiles have landed
