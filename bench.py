@@ -40,8 +40,8 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "7311cc79cd2f57b47c70b605d450cbd18b58c35485cfe61117813fe045a38962",
-    "read_bytes": 8263645558,
+    "source_sha256": "4547cc18bad6b7b80bb42632a6f04b3a45f6737345c3ba1824be5453b23b87ba",
+    "read_bytes": 8335926093,
     "write_bytes": 281542656,
 }
 
