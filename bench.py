@@ -40,9 +40,9 @@ PEAK_HBM_GBS = 8000.0
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "4547cc18bad6b7b80bb42632a6f04b3a45f6737345c3ba1824be5453b23b87ba",
-    "read_bytes": 8335926093,
-    "write_bytes": 281542656,
+    "source_sha256": "5b0e3a465ae00362a841b7f0972259f9ca9b31b152909c1f843f942c9a8d3aa9",
+    "read_bytes": 8459415931,
+    "write_bytes": 281544160,
 }
 
 

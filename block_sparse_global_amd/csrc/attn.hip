@@ -339,6 +339,11 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
       }
     };
     bf16x8 vops[2][2];
+    // Wave priority: raised for the whole PV section (exponentials and PV
+    // MFMAs) and raised further while its MFMAs issue, so that a wave whose
+    // P is ready gets the matrix core ahead of waves still in their S
+    // product or max (measured +2.5% at 100 views over equal priorities).
+    __builtin_amdgcn_s_setprio(1);
     v_operands(0, vops[0]);
 #pragma unroll
     for (int step = 0; step < 2 * kKT; ++step) {
@@ -356,10 +361,13 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
         const bf16x2 pp = {pb[r], pb[r + 1]};
         psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
       }
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[step & 1][dt], pb, o[dt], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(1);
     }
+    __builtin_amdgcn_s_setprio(0);
     l_run += psum;
     wait_vmem();  // this wave's copies of the next block's tiles have landed
     lds_barrier();
