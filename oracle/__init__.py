@@ -14,6 +14,7 @@ from .ress_oracle import (  # noqa: F401
     drift_key,
     score_key,
     select_topk,
+    select_cdf,
     kept_lists,
     swap_schedule,
     drop_objective,

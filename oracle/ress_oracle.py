@@ -27,6 +27,10 @@ reason in the design notes of the repository):
   products of mean-pooled Q and K (not token probabilities pooled after the
   fact); a partial (padded) block is pooled over its valid tokens only;
 * ties in any top-k / top-m go to the lower block index;
+* the cumulative-probability (CDF) selection takes the always-kept blocks'
+  mass first, then candidates by probability descending until the mass
+  reaches the threshold, capped by the per-head budget and raised to the
+  two-block floor;
 * refinement rounds are batched: restore and drop gains both come from the
   round-start state, m_r = floor(rho * c / 2^(r+1)), both sets applied, then
   g, K, G recomputed from their definitions; a drop whose K + u <= 0 gets a
@@ -173,6 +177,67 @@ def select_topk(key: np.ndarray, keep: np.ndarray, always: np.ndarray):
             if c < len(cand):
                 margin[h, i] = _rel_gap(kv[order[c - 1]], kv[order[c]])
     return kept, margin
+
+
+def select_cdf(P: np.ndarray, keep: np.ndarray, always: np.ndarray, tau: float,
+               floor: int = 2, rows=None):
+    """Kept key blocks under a cumulative-probability (top-p, "CDF") threshold
+    with the per-head budget as a cap.
+
+    This is the probability selection the ReSS page compares against: its
+    related-work section describes SparseVGGT as keeping the blocks with large
+    mass on the pooled map through top-k and top-p criteria; §4.4 and the
+    "+ CDF threshold" row of Table 2 contrast such a threshold, whose keep
+    count depends on the data, with a fixed budget; Appendix F applies the
+    sink rule (special blocks always kept) and a floor of two key blocks per
+    query row to every method. The pages do not print the rule itself; the
+    reading taken here, per (head, query-block row):
+
+    * s = sum of P over the always-kept blocks, accumulated in ascending
+      block order (those blocks are kept whatever the threshold);
+    * candidates (the other blocks) are visited by P descending, ties to the
+      lower block index; while s < tau and fewer than c_h = keep[h] - |always|
+      candidates are taken, take the next one and add its P to s (float64,
+      one addition at a time in that order);
+    * the row is then raised to at least ``floor`` kept blocks by taking the
+      next candidates in the same order.
+
+    Returns (kept bool [H][n][n], taken int [H][n] = number of candidates
+    kept, margin float64 [H][n]) where margin is the relative distance
+    between tau and the cumulative mass just before and just after the
+    decisive candidate (the smaller of the two; inf when the cap or the
+    floor decided the count), for near-tie checks.
+    """
+    H, n, _ = P.shape
+    cand = np.nonzero(always == 0)[0]
+    alw = np.nonzero(always != 0)[0]
+    kept = np.zeros(P.shape, dtype=bool)
+    taken = np.zeros((H, n), dtype=np.int64)
+    margin = np.full((H, n), np.inf)
+    todo = rows if rows is not None else [(h, i) for h in range(H) for i in range(n)]
+    for h, i in todo:
+        c = int(keep[h]) - len(alw)
+        s = 0.0
+        for j in alw:
+            s += float(P[h, i, j])
+        pv = P[h, i, cand]
+        order = _order_desc(pv, cand)
+        m = 0
+        before = s
+        while s < tau and m < c:
+            before = s
+            s += float(pv[order[m]])
+            m += 1
+        if s >= tau and m > 0:
+            margin[h, i] = min(_rel_gap(before, tau), _rel_gap(s, tau))
+        elif s >= tau:
+            margin[h, i] = _rel_gap(s, tau)
+        m = max(m, floor - len(alw))
+        m = min(m, c)
+        kept[h, i, cand[order[:m]]] = True
+        kept[h, i, alw] = True
+        taken[h, i] = m
+    return kept, taken, margin
 
 
 def kept_lists(kept: np.ndarray):

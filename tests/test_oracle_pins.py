@@ -191,6 +191,105 @@ def test_topk_ties_go_to_lower_index_and_lists_ascending():
 
 
 # ---------------------------------------------------------------------------
+# Cumulative-probability (CDF, top-p) selection with the budget as a cap
+# (ReSS page: related work on SparseVGGT's top-k / top-p selection, §4.4,
+# Table 2 "+ CDF threshold", Appendix F two-block floor and sink rule)
+# ---------------------------------------------------------------------------
+
+def _prob_rows(seed, rows, n):
+    r = rng(seed)
+    x = r.gamma(0.5, 1.0, (1, rows, n))
+    return x / x.sum(-1, keepdims=True)
+
+
+@pytest.mark.parametrize("alw", [(), (2, 7), (4,)])
+def test_cdf_is_brute_force_smallest_set_reaching_tau(alw):
+    n = 9
+    always = np.zeros(n, np.uint8)
+    always[list(alw)] = 1
+    cand = [j for j in range(n) if not always[j]]
+    r = rng(31 + len(alw))
+    checked = 0
+    for trial in range(12):
+        P = _prob_rows(100 + trial, n, n)
+        kk = int(r.integers(max(2, len(alw) + 1), n + 1))
+        c = kk - len(alw)
+        tau = float(r.uniform(0.05, 1.0))
+        kept, taken, _ = oracle.select_cdf(P, np.array([kk]), always, tau)
+        for i in range(n):
+            base = math.fsum(P[0, i, j] for j in alw)
+            best = {m: max(itertools.combinations(cand, m),
+                           key=lambda S: math.fsum(P[0, i, j] for j in S))
+                    for m in range(0, c + 1)}
+            mass = {m: base + math.fsum(P[0, i, j] for j in S) for m, S in best.items()}
+            if any(abs(v - tau) < 1e-12 for v in mass.values()):
+                continue              # a rounding tie: the count is not pinned
+            m = next((m for m in range(c + 1) if mass[m] >= tau), c)
+            m = min(max(m, 2 - len(alw)), c)
+            assert taken[0, i] == m
+            assert set(np.nonzero(kept[0, i])[0]) == set(best[m]) | set(alw)
+            checked += 1
+    assert checked > 80
+
+
+def test_cdf_unreachable_threshold_is_topk_on_probability():
+    n = 40
+    always = np.zeros(n, np.uint8); always[[38, 39]] = 1
+    P = _prob_rows(7, n, n)
+    keep = np.array([12])
+    kept, taken, margin = oracle.select_cdf(P, keep, always, 2.0)
+    ref, _ = oracle.select_topk(P, keep, always)
+    assert np.array_equal(kept, ref)
+    assert np.all(taken == 10) and np.all(np.isinf(margin))
+
+
+def test_cdf_uniform_row_closed_form():
+    n = 10
+    P = np.full((1, 1, n), 0.1)
+    none = np.zeros(n, np.uint8)
+    for tau, m in ((0.35, 4), (0.71, 8), (0.05, 2), (0.95, 10)):
+        kept, taken, _ = oracle.select_cdf(P, np.array([n]), none, tau)
+        # equal probabilities: the lowest indices come first
+        assert taken[0, 0] == m and list(np.nonzero(kept[0, 0])[0]) == list(range(m))
+    kept, taken, _ = oracle.select_cdf(P, np.array([6]), none, 0.95)   # the cap
+    assert taken[0, 0] == 6
+    # dyadic masses sum exactly: reaching tau exactly stops the scan
+    P = np.array([[[0.125, 0.5, 0.125, 0.25]]])
+    kept, taken, margin = oracle.select_cdf(P, np.array([4]), np.zeros(4, np.uint8), 0.75)
+    assert taken[0, 0] == 2 and list(np.nonzero(kept[0, 0])[0]) == [1, 3]
+    assert margin[0, 0] == 0.0
+
+
+def test_cdf_floor_and_always_kept_mass():
+    n = 8
+    P = _prob_rows(3, 1, n)
+    order = np.lexsort((np.arange(n), -P[0, 0]))
+    none = np.zeros(n, np.uint8)
+    kept, taken, _ = oracle.select_cdf(P, np.array([n]), none, 1e-12)
+    assert taken[0, 0] == 2 and set(np.nonzero(kept[0, 0])[0]) == set(order[:2])
+    one = none.copy(); one[5] = 1
+    kept, taken, _ = oracle.select_cdf(P, np.array([n]), one, 1e-12)
+    assert taken[0, 0] == 1 and kept[0, 0, 5]
+    two = none.copy(); two[[0, 5]] = 1
+    tau = P[0, 0, 0] + P[0, 0, 5]          # reached by the always-kept mass alone
+    kept, taken, _ = oracle.select_cdf(P, np.array([n]), two, tau * 0.999)
+    assert taken[0, 0] == 0 and set(np.nonzero(kept[0, 0])[0]) == {0, 5}
+
+
+def test_cdf_count_grows_with_tau():
+    n = 30
+    P = _prob_rows(9, n, n)
+    always = np.zeros(n, np.uint8); always[29] = 1
+    prev = None
+    for tau in np.linspace(0.05, 1.0, 12):
+        _, taken, _ = oracle.select_cdf(P, np.array([20]), always, float(tau))
+        if prev is not None:
+            assert np.all(taken >= prev)
+        prev = taken
+    assert prev.max() == 19
+
+
+# ---------------------------------------------------------------------------
 # Refinement (ReSS page §4.3 Eq. 10-17)
 # ---------------------------------------------------------------------------
 
