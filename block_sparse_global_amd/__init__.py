@@ -1,6 +1,6 @@
 """libress: block-sparse global attention for MI355X (gfx950).
 
-Python side of the C-ABI library built from ``csrc/``: the five entry points
+Python side of the C-ABI library built from ``csrc/``: the entry points
 under their C names, plus ``BlockSparseGlobalAttention`` which sequences them
 for one workload shape. Importing this package loads ``libress.so`` and
 raises if it has not been built (``python block_sparse_global_amd/build.py``
@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     ress_refine_dropset,
     ress_refine_workspace_size,
     ress_select_topk,
+    ress_select_cdf,
     ress_sparse_attn_fwd,
     ress_version,
 )

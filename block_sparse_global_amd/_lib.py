@@ -36,6 +36,7 @@ ENTRY_POINTS = (
     "ress_block_pool",
     "ress_block_score",
     "ress_select_topk",
+    "ress_select_cdf",
     "ress_refine_dropset",
     "ress_refine_workspace_size",
     "ress_sparse_attn_fwd",
@@ -84,6 +85,7 @@ def _load():
     lib.ress_block_score.argtypes = [dp, dp, dp, dp, ress_shape, ctypes.c_int,
                                      ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, vp]
     lib.ress_select_topk.argtypes = [dp, ress_shape, ip, vp, i32, ip, ip, vp]
+    lib.ress_select_cdf.argtypes = [dp, ress_shape, ip, vp, ctypes.c_double, i32, ip, ip, vp]
     lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
                                         ctypes.c_double, ctypes.c_double, i32, ip, ip,
                                         dp, dp, vp, ctypes.c_size_t, vp]
@@ -92,7 +94,7 @@ def _load():
     lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
                                          ctypes.c_float, vp, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
-              "ress_refine_dropset", "ress_sparse_attn_fwd"):
+              "ress_select_cdf", "ress_refine_dropset", "ress_sparse_attn_fwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ress_last_error.restype = ctypes.c_char_p
     lib.ress_last_error.argtypes = []
@@ -205,6 +207,21 @@ def ress_select_topk(key, shape: Shape, keep: Sequence[int], always_keep, k_max:
         raise ValueError(f"always_keep must have shape ({n},)")
     _check("ress_select_topk", LIB.ress_select_topk(
         _ptr(key, "key", torch.float64, (H, n, n)), shape.c(), keep_p, alw_p,
+        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
+
+
+def ress_select_cdf(P, shape: Shape, keep: Sequence[int], always_keep, tau: float,
+                    k_max: int, kept_idx, kept_cnt, stream=None):
+    H, n = shape.H, shape.n
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (n,):
+        raise ValueError(f"always_keep must have shape ({n},)")
+    _check("ress_select_cdf", LIB.ress_select_cdf(
+        _ptr(P, "P", torch.float64, (H, n, n)), shape.c(), keep_p, alw_p, float(tau),
         int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
 

@@ -219,6 +219,24 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
   return hip_status(e, "topk launch");
 }
 
+int ress_select_cdf(const double* P, ress_shape shape, const int32_t* keep,
+                    const uint8_t* always_keep, double tau, int32_t k_max,
+                    int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  if (!(tau > 0.0) || !isfinite(tau))
+    return fail(RESS_ERR_INVALID_ARG, "tau must be finite and > 0");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK)
+    return rc;
+  hipError_t e = ress::launch_cdf(P, shape, cfg, tau, k_max, kept_idx, kept_cnt,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, "cdf launch");
+}
+
 int ress_refine_dropset(const double* P, const double* key,
                         const double* vpool, const double* vout,
                         const double* M, ress_shape shape, const int32_t* keep,

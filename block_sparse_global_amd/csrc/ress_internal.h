@@ -71,6 +71,10 @@ hipError_t launch_topk(const double* key, const ress_shape& s,
                        const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,
                        int32_t* kept_cnt, hipStream_t st);
 
+hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg,
+                      double tau, int32_t k_max, int32_t* kept_idx,
+                      int32_t* kept_cnt, hipStream_t st);
+
 hipError_t launch_refine(const double* P, const double* key,
                          const double* vpool, const double* vout,
                          const double* M, const ress_shape& s,

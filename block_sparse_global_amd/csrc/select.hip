@@ -9,6 +9,16 @@
 // keys whose unsigned order equals the float64 order, with ties among equal
 // keys broken towards the lower block index by a block-wide prefix count.
 // No float atomics and fixed-order reductions: results are bit-reproducible.
+//
+// Cumulative-probability ("CDF", top-p) selection, the probability criterion
+// the ReSS page compares against (its related-work section on SparseVGGT's
+// top-k and top-p selection, §4.4 and Table 2 "+ CDF threshold"; Appendix F
+// two-block floor and sink rule): the always-kept blocks' mass first, then
+// candidates by probability descending until the mass reaches tau, at most
+// c_h of them, at least enough for two kept blocks. The same radix select
+// first finds the c_h best candidates; they are ranked exactly and one lane
+// accumulates their probabilities in rank order, one float64 addition at a
+// time, so the count matches a sequential scan bit for bit.
 #include "ress_internal.h"
 
 namespace ress {
@@ -200,6 +210,102 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
                 sh);
 }
 
+// float64 value of an order key (inverse of order_key)
+__device__ inline double order_key_value(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+// Dynamic LDS of cdf_kernel for up to `cap` selected candidates: their order
+// keys, their probabilities in rank order and their ranks.
+inline size_t cdf_smem_bytes(int cap) {
+  return (size_t)cap * (sizeof(uint64_t) + sizeof(double) + sizeof(int32_t));
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void cdf_kernel(
+    const double* __restrict__ P, int n, SelConfig cfg, double tau, int cap,
+    int k_max, int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cdf_smem[];
+  uint64_t* ck = reinterpret_cast<uint64_t*>(cdf_smem);  // [cap] keys, block order
+  double* sp = reinterpret_cast<double*>(ck + cap);       // [cap] P in rank order
+  int32_t* rk = reinterpret_cast<int32_t*>(sp + cap);     // [cap] rank of ck[a]
+  __shared__ SelShared sh;
+  __shared__ int s_taken;
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int t = threadIdx.x;
+  const double* row = P + ((size_t)h * n + i) * n;
+  uint64_t u[E];
+  uint32_t member = 0, always = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = t * E + e;
+    u[e] = 0;
+    if (j < n) {
+      u[e] = order_key(row[j]);
+      if (sel_always(cfg, j))
+        always |= 1u << e;
+      else
+        member |= 1u << e;
+    }
+  }
+  const int c = cfg.keep[h] - cfg.n_always;
+  const uint32_t sel = select_top<E>(u, member, c, sh);
+  // the c best candidates, compacted in ascending block order
+  int total;
+  const int pos = block_exclusive_scan(__popc(sel), sh, &total);
+  {
+    int p = pos;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((sel >> e) & 1u) ck[p++] = u[e];
+  }
+  __syncthreads();
+  // rank by probability descending; equal probabilities by block index,
+  // which is the compacted position
+  for (int a = t; a < c; a += kThreads) {
+    const uint64_t ka = ck[a];
+    int r = 0;
+    for (int b = 0; b < c; ++b) {
+      const uint64_t kb = ck[b];
+      r += (kb > ka) || (kb == ka && b < a);
+    }
+    rk[a] = r;
+    sp[r] = order_key_value(ka);
+  }
+  __syncthreads();
+  if (t == 0) {
+    double s = 0.0;
+    for (int wd = 0; wd * 64 < n; ++wd) {
+      uint64_t bits = cfg.always_bits[wd];
+      while (bits != 0) {
+        const int j = wd * 64 + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (j < n) s += row[j];
+      }
+    }
+    int m = 0;
+    while (s < tau && m < c) s += sp[m++];
+    m = max(m, 2 - cfg.n_always);
+    s_taken = min(m, c);
+  }
+  __syncthreads();
+  const int taken = s_taken;
+  uint32_t kept = always;
+  {
+    int p = pos;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((sel >> e) & 1u) {
+        if (rk[p] < taken) kept |= 1u << e;
+        ++p;
+      }
+  }
+  const size_t r = (size_t)h * n + i;
+  write_kept<E>(kept, n, k_max, kept_idx + r * k_max, kept_cnt + r, sh);
+}
+
 int pick_e(int n) {
   const int need = (n + kThreads - 1) / kThreads;
   int e = 1;
@@ -207,7 +313,39 @@ int pick_e(int n) {
   return e;
 }
 
+template <int E>
+hipError_t launch_cdf_e(const double* P, int n, int H, const SelConfig& cfg,
+                        double tau, int cap, int32_t k_max, int32_t* kept_idx,
+                        int32_t* kept_cnt, hipStream_t st) {
+  const size_t smem = cdf_smem_bytes(cap);
+  if (smem > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&cdf_kernel<E>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((cdf_kernel<E>), dim3(n, H), dim3(kThreads), smem, st, P, n,
+                     cfg, tau, cap, k_max, kept_idx, kept_cnt);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg,
+                      double tau, int32_t k_max, int32_t* kept_idx,
+                      int32_t* kept_cnt, hipStream_t st) {
+  const int n = s.N_pad / s.B;
+  int cap = 1;
+  for (int h = 0; h < s.H; ++h) cap = max(cap, cfg.keep[h] - cfg.n_always);
+  switch (pick_e(n)) {
+    case 1: return launch_cdf_e<1>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 2: return launch_cdf_e<2>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 4: return launch_cdf_e<4>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 8: return launch_cdf_e<8>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 16: return launch_cdf_e<16>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_topk(const double* key, const ress_shape& s,
                        const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,

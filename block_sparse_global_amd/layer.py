@@ -1,8 +1,8 @@
 """The whole block-sparse global-attention step over the C ABI.
 
 ``BlockSparseGlobalAttention`` owns the device buffers of one workload shape
-(allocated once with torch) and runs pool -> score -> top-k -> [refine] ->
-sparse attention as five library calls on one stream. It only allocates and
+(allocated once with torch) and runs pool -> score -> top-k (or the cumulative-probability
+threshold) -> [refine] -> sparse attention as library calls on one stream. It only allocates and
 sequences; every step is a libress kernel.
 """
 
@@ -22,6 +22,7 @@ from ._lib import (
     ress_block_score,
     ress_refine_dropset,
     ress_refine_workspace_size,
+    ress_select_cdf,
     ress_select_topk,
     ress_sparse_attn_fwd,
 )
@@ -31,11 +32,17 @@ class BlockSparseGlobalAttention:
     def __init__(self, shape: Shape, keep, always_keep, mode: str = "prob",
                  rounds: int = 0, rho: float = 0.5, eps: float = 1e-4,
                  scale: Optional[float] = None, M: Optional[torch.Tensor] = None,
-                 device="cuda", with_lse: bool = False):
+                 device="cuda", with_lse: bool = False, tau: Optional[float] = None):
+        """``tau`` switches the selection from top-k to the cumulative
+        probability threshold (ress_select_cdf, probability scoring only; the
+        budget ``keep`` is then the cap)."""
         if mode not in ("prob", "drift"):
             raise ValueError(mode)
         if rounds > 0 and mode != "drift":
             raise ValueError("refinement rounds need the drift-mode score outputs")
+        if tau is not None and mode != "prob":
+            raise ValueError("the cumulative threshold ranks by probability: mode='prob'")
+        self.tau = None if tau is None else float(tau)
         self.shape = shape
         self.keep = np.ascontiguousarray(np.asarray(keep, dtype=np.int32))
         self.always = (None if always_keep is None
@@ -79,6 +86,10 @@ class BlockSparseGlobalAttention:
                          stream)
 
     def select(self, stream=None):
+        if self.tau is not None:
+            ress_select_cdf(self.P, self.shape, self.keep, self.always, self.tau,
+                            self.k_max, self.kept_idx, self.kept_cnt, stream)
+            return
         key = self.key if self.key is not None else self.P
         ress_select_topk(key, self.shape, self.keep, self.always, self.k_max,
                          self.kept_idx, self.kept_cnt, stream)

@@ -134,6 +134,34 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
                      int32_t* kept_idx, int32_t* kept_cnt, void* stream);
 
 /*
+ * ress_select_cdf — per (head, query-block row) keep set under a cumulative
+ * probability (top-p, "CDF") threshold, with the per-head budget as a cap:
+ * the probability selection the ReSS page compares against (related work on
+ * SparseVGGT's top-k and top-p selection; §4.4 and Table 2 "+ CDF
+ * threshold"; Appendix F: special blocks always kept, at least two key
+ * blocks per query row).
+ *
+ * Per row of head h: s starts as the sum of P over the always-kept blocks
+ * (ascending block order); candidates (always_keep[j] == 0) are then taken
+ * by P descending (equal P: the lower block index first), each adding its P
+ * to s, one float64 addition at a time in that order, while s < tau and
+ * fewer than c_h = keep[h] - |always| are taken; the count is finally raised
+ * so that the row keeps at least two blocks. The kept blocks (the taken
+ * candidates and every always-kept block) go to kept_idx[h][i] in ascending
+ * order, the rest of the row (up to k_max) is set to -1, and kept_cnt[h][i]
+ * receives the row's count, which varies with the data (at most keep[h]).
+ * tau >= 1 (or above the row's total mass) keeps c_h candidates, the top-k
+ * rule on P.
+ *
+ * P: device float64 [H][n][n] (ress_block_score's map). tau: finite, > 0.
+ * keep, always_keep, k_max, kept_idx, kept_cnt: as for ress_select_topk.
+ * Uses cap * 20 bytes of LDS per workgroup, cap = max_h c_h.
+ */
+int ress_select_cdf(const double* P, ress_shape shape, const int32_t* keep,
+                    const uint8_t* always_keep, double tau, int32_t k_max,
+                    int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
  * ress_refine_dropset — ReSS iterative residual restoration (ReSS page
  * §4.3, Eq. 10-17, Appendix E), applied to the keep sets from
  * ress_select_topk.

@@ -18,9 +18,9 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(ress_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_call():
     names = declared_functions()
-    for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
+    for f in ("ress_block_pool", "ress_block_score", "ress_select_topk", "ress_select_cdf",
               "ress_refine_dropset", "ress_refine_workspace_size", "ress_sparse_attn_fwd",
               "ress_last_error", "ress_version"):
         assert f in names
@@ -130,6 +130,16 @@ def test_selection_budget_checks():
     big = _shape(H=65)
     _, k65 = _arr([2] * 65, np.int32)
     assert L.ress_select_topk(FAKE, big, k65, None, 2, FAKE, FAKE, None) == -2     # too many heads
+    d = ctypes.c_double
+    # the cumulative threshold: the same budget checks, and tau finite and > 0
+    assert L.ress_select_cdf(FAKE, s, low, None, d(0.9), 3, FAKE, FAKE, None) == -1
+    assert L.ress_select_cdf(FAKE, s, ok_keep, alw3, d(0.9), 3, FAKE, FAKE, None) == -1
+    assert L.ress_select_cdf(None, s, ok_keep, None, d(0.9), 3, FAKE, FAKE, None) == -1
+    assert L.ress_select_cdf(MISALIGNED, s, ok_keep, None, d(0.9), 3, FAKE, FAKE, None) == -1
+    for bad_tau in (0.0, -0.5, float("nan"), float("inf")):
+        assert L.ress_select_cdf(FAKE, s, ok_keep, None, d(bad_tau), 3, FAKE, FAKE, None) == -1
+        assert "tau" in b.ress_last_error()
+    assert L.ress_select_cdf(FAKE, big, k65, None, d(0.9), 2, FAKE, FAKE, None) == -2
     d = ctypes.c_double
     e = d(1e-4)
     assert L.ress_refine_dropset(FAKE, FAKE, FAKE, FAKE, None, s, ok_keep, alw, -1, d(0.5), e,

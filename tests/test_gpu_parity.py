@@ -8,7 +8,8 @@ and each stage is compared with the oracle on the same seeded inputs:
   relative 1e-12 (1e-10 for the drift key, whose GPU form is the Eq. 9
   expansion while the oracle uses the direct form);
 * keep sets: bit-exact except near-ties (oracle keys within 1e-6 relative of
-  the row's cut);
+  the row's cut); the cumulative-probability selection, run on the oracle's
+  own map, bit-exact;
 * refinement: started from the GPU's top-k sets; sets equal unless the
   oracle logged a near-tie (< 1e-6 relative) on the row's trajectory, in
   which case the GPU's J_final must equal the oracle's J of the GPU's set;
@@ -155,6 +156,46 @@ def test_topk(case):
     gm = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
     nd = compare_masks(gm, ref["kept"], ref["key"], x["always"], x["keep"])
     print(f"[topk] {name}/{mode}: {nd} near-tie rows of {w.heads * n}")
+
+
+@pytest.mark.parametrize("tau", [1e-9, 0.02, 0.1, 0.3, 2.0])
+def test_select_cdf(case, tau):
+    """Cumulative-probability selection on the oracle's own map P: the GPU
+    ranks and sums the same float64 values in the same order, so the keep
+    sets must be identical (no near-tie allowance)."""
+    name, mode, w, x, g, ref = case
+    if mode != "prob" and name != "views100":
+        pytest.skip("one drift workload covers the always-kept layout of 5 blocks")
+    b = _lib()
+    H, n = w.heads, w.n_blocks
+    shape = b.Shape(H, w.N, w.N_pad, w.head_dim, w.block)
+    keep = x["keep"]
+    k_max = int(np.max(keep))
+    P = torch.from_numpy(ref["P"]).cuda()
+    idx = torch.full((H, n, k_max), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((H, n), -5, dtype=torch.int32, device="cuda")
+    b.ress_select_cdf(P, shape, keep, x["always"], tau, k_max, idx, cnt)
+    torch.cuda.synchronize()
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    rows = ([(h, i) for h in range(H) for i in range(n)] if H * n <= 6000
+            else sample_blocks(H, n, 3000, seed=7))
+    kept, taken, _ = oracle.select_cdf(ref["P"], keep, x["always"], tau, rows=rows)
+    alw = np.nonzero(x["always"])[0] if x["always"] is not None else np.array([], int)
+    for h, i in rows:
+        c = int(gc[h, i])
+        assert c == taken[h, i] + len(alw), f"row ({h},{i}): count {c}"
+        lst = gi[h, i, :c]
+        assert np.all(np.diff(lst) > 0) and np.all(gi[h, i, c:] == -1)
+        assert set(lst.tolist()) == set(np.nonzero(kept[h, i])[0].tolist()), f"row ({h},{i})"
+    if tau > 1.5:
+        # unreachable threshold: the top-k rule on P, as the top-k call gives it
+        i2 = torch.empty_like(idx)
+        c2 = torch.empty_like(cnt)
+        b.ress_select_topk(P, shape, keep, x["always"], k_max, i2, c2)
+        torch.cuda.synchronize()
+        assert np.array_equal(i2.cpu().numpy(), gi) and np.array_equal(c2.cpu().numpy(), gc)
+    print(f"[cdf] {name} tau={tau}: mean kept {gc.mean():.2f} of {n} "
+          f"(cap {k_max}), {len(rows)} rows checked")
 
 
 def test_refine(case):
