@@ -52,17 +52,28 @@ ATTN_TRAFFIC = {
 }
 
 
+def _valid_tokens(N, blk, nb):
+    valid = np.full(nb, blk, dtype=np.int64)
+    valid[-1] = N - (nb - 1) * blk
+    return valid
+
+
 def kept_flops(w, idx, cnt):
     """4 * D * sum over kept (query block, key block) pairs of valid q * valid k."""
-    B, N, n = w.block, w.N, w.n_blocks
-    valid = np.full(n, B, dtype=np.int64)
-    valid[-1] = N - (n - 1) * B
+    n = w.n_blocks
+    vq = _valid_tokens(w.N, w.block, n)
+    vk = _valid_tokens(w.N, w.kblock, w.n_kblocks)
     tot = 0
     for h in range(idx.shape[0]):
         for i in range(n):
             js = idx[h, i, : cnt[h, i]]
-            tot += int(valid[i]) * int(valid[js].sum())
+            tot += int(vq[i]) * int(vk[js].sum())
     return 4.0 * w.head_dim * tot
+
+
+def sparsity_of(w, cnt):
+    """1 - kept (query block, key block) pairs / all pairs."""
+    return 1.0 - float(cnt.sum()) / (w.heads * w.n_blocks * w.n_kblocks)
 
 
 def dense_flops(w):
@@ -80,7 +91,7 @@ def setup(name, mode=None, x=None, tau=None):
     to_t = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()) \
         if w.dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
     q, k, v = to_t(x["q"]), to_t(x["k"]), to_t(x["v"])
-    shape = bsg.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+    shape = bsg.Shape(*w.shape_args())
     if mode is None:
         mode = "drift" if w.score in ("drift", "both") else "prob"
     layer = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
@@ -149,18 +160,18 @@ def cpu_baseline(w, x, idx, cnt, budget_s=15.0):
     qf = synth.as_f64(x["q"], w.dtype)
     kf = synth.as_f64(x["k"], w.dtype)
     vf = synth.as_f64(x["v"], w.dtype)
-    valid = np.full(n, B, dtype=np.int64)
-    valid[-1] = w.N - (n - 1) * B
+    vq = _valid_tokens(w.N, B, n)
+    vk = _valid_tokens(w.N, w.kblock, w.n_kblocks)
     flops, spent, blocks = 0.0, 0.0, 0
     while spent < budget_s and blocks < w.heads * n:
         h, i = int(rng.integers(w.heads)), int(rng.integers(n))
-        kept = np.zeros((w.heads, n, n), bool)
+        kept = np.zeros((w.heads, n, w.n_kblocks), bool)
         kept[h, i, idx[h, i, : cnt[h, i]]] = True
         t0 = time.perf_counter()
         oracle.masked_attention(qf, kf, vf, kept, w.N, B, 1.0 / math.sqrt(w.head_dim),
-                                blocks=[(h, i)])
+                                blocks=[(h, i)], Bk=w.kblock)
         spent += time.perf_counter() - t0
-        flops += 4.0 * w.head_dim * valid[i] * valid[idx[h, i, : cnt[h, i]]].sum()
+        flops += 4.0 * w.head_dim * vq[i] * vk[idx[h, i, : cnt[h, i]]].sum()
         blocks += 1
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
@@ -233,14 +244,15 @@ def main():
         # 8 / 32 / 100 views (the headline lines) and 200 views with both
         # scores; each line: layer time, dense time, the attention kernel alone
         lines = [("views8", None), ("views32", None), ("views100", None),
-                 ("views100", "cdf"), ("views200", "prob"), ("views200", "drift")]
+                 ("views100", "cdf"), ("views100-k64", None),
+                 ("views200", "prob"), ("views200", "drift")]
         x200 = None
         for name, mode in lines:
             key = name if mode is None else f"{name}-{mode}"
             if name == args.workload and mode is None and not args.no_dense:
                 sweep[key] = {"layer_ms": ms_step, "dense_ms": dense_ms, "attn_ms": attn_ms,
                               "select_ms": stages["select"], "kept_flop": kf,
-                              "realised_sparsity": 1.0 - float(cnt.sum()) / (w.heads * w.n_blocks ** 2)}
+                              "realised_sparsity": sparsity_of(w, cnt)}
             else:
                 if name == "views200" and x200 is None:
                     import synth
@@ -264,7 +276,7 @@ def main():
                                    2 if name == "views200" else 5)
                 sweep[key] = {"layer_ms": l_ms, "dense_ms": d_ms, "attn_ms": a_ms,
                               "select_ms": s_ms, "kept_flop": kf2,
-                              "realised_sparsity": 1.0 - float(cnt2.sum()) / (w2.heads * w2.n_blocks ** 2)}
+                              "realised_sparsity": sparsity_of(w2, cnt2)}
                 del layer2, q2, k2, v2, out2, d2
                 torch.cuda.empty_cache()
             e = sweep[key]
@@ -288,7 +300,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "views": w.views, "tokens": w.N, "padded_tokens": w.N_pad,
-            "heads": w.heads, "head_dim": w.head_dim, "block": w.block,
+            "heads": w.heads, "head_dim": w.head_dim, "block": w.block, "key_block": w.kblock,
             "sparsity": list(w.sparsity), "score": layer.mode, "refine_rounds": layer.rounds,
             "seed": w.seed,
         },
@@ -307,7 +319,7 @@ def main():
         "sparse_vs_dense_per_flop": None if args.no_dense else (kf / attn_ms) / (df / dense_ms),
         "attn_tflops": achieved,
         "kept_flop": kf,
-        "realised_sparsity": 1.0 - float(cnt.sum()) / (w.heads * w.n_blocks ** 2),
+        "realised_sparsity": sparsity_of(w, cnt),
         "stages_ms": stages,
         "views_sweep": sweep,
     }

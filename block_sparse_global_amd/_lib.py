@@ -54,23 +54,39 @@ class RessError(RuntimeError):
 class ress_shape(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("N_pad", ctypes.c_int32), ("D", ctypes.c_int32),
-                ("B", ctypes.c_int32)]
+                ("B", ctypes.c_int32), ("Bk", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
 class Shape:
+    """Query blocks of B tokens, key blocks of Bk tokens (0: Bk = B)."""
     H: int
     N: int
     N_pad: int
     D: int
     B: int
+    Bk: int = 0
+
+    @property
+    def kb(self) -> int:
+        return self.Bk if self.Bk > 0 else self.B
 
     @property
     def n(self) -> int:
+        """Query blocks (rows of the block maps)."""
         return self.N_pad // self.B
 
+    @property
+    def nq(self) -> int:
+        return self.n
+
+    @property
+    def nk(self) -> int:
+        """Key blocks (columns of the block maps)."""
+        return -(-self.N // self.kb)
+
     def c(self) -> ress_shape:
-        return ress_shape(self.H, self.N, self.N_pad, self.D, self.B)
+        return ress_shape(self.H, self.N, self.N_pad, self.D, self.B, self.Bk)
 
 
 def _load():
@@ -175,55 +191,56 @@ def ress_block_pool(q, k, v, shape: Shape, qpool, kpool, vpool, stream=None):
     ref = next(t for t in (q, k, v) if t is not None)
     dt = _dtype_code(ref)
     tok = (shape.H, shape.N_pad, shape.D)
-    blk = (shape.H, shape.n, shape.D)
+    qblk = (shape.H, shape.nq, shape.D)
+    kblk = (shape.H, shape.nk, shape.D)
     _check("ress_block_pool", LIB.ress_block_pool(
         _ptr(q, "q", ref.dtype, tok), _ptr(k, "k", ref.dtype, tok), _ptr(v, "v", ref.dtype, tok),
         dt, shape.c(),
-        _ptr(qpool, "qpool", torch.float64, blk), _ptr(kpool, "kpool", torch.float64, blk),
-        _ptr(vpool, "vpool", torch.float64, blk), _stream(stream)))
+        _ptr(qpool, "qpool", torch.float64, qblk), _ptr(kpool, "kpool", torch.float64, kblk),
+        _ptr(vpool, "vpool", torch.float64, kblk), _stream(stream)))
 
 
 def ress_block_score(qpool, kpool, vpool, M, shape: Shape, mode: int, scale: float,
                      eps: float, P, key, vout, vmv, stream=None):
-    H, n, D = shape.H, shape.n, shape.D
+    H, nq, nk, D = shape.H, shape.nq, shape.nk, shape.D
     f64 = torch.float64
     _check("ress_block_score", LIB.ress_block_score(
-        _ptr(qpool, "qpool", f64, (H, n, D)), _ptr(kpool, "kpool", f64, (H, n, D)),
-        _ptr(vpool, "vpool", f64, (H, n, D)), _ptr(M, "M", f64, (H, D, D)),
+        _ptr(qpool, "qpool", f64, (H, nq, D)), _ptr(kpool, "kpool", f64, (H, nk, D)),
+        _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(M, "M", f64, (H, D, D)),
         shape.c(), int(mode), float(scale), float(eps),
-        _ptr(P, "P", f64, (H, n, n)), _ptr(key, "key", f64, (H, n, n)),
-        _ptr(vout, "vout", f64, (H, n, D)), _ptr(vmv, "vmv", f64, (H, n)),
+        _ptr(P, "P", f64, (H, nq, nk)), _ptr(key, "key", f64, (H, nq, nk)),
+        _ptr(vout, "vout", f64, (H, nq, D)), _ptr(vmv, "vmv", f64, (H, nk)),
         _stream(stream)))
 
 
 def ress_select_topk(key, shape: Shape, keep: Sequence[int], always_keep, k_max: int,
                      kept_idx, kept_cnt, stream=None):
-    H, n = shape.H, shape.n
+    H, nq, nk = shape.H, shape.nq, shape.nk
     keep_arr, keep_p = _host_i32(keep, "keep")
     if keep_arr is not None and keep_arr.shape != (H,):
         raise ValueError(f"keep must have shape ({H},)")
     alw_arr, alw_p = _host_u8(always_keep, "always_keep")
-    if alw_arr is not None and alw_arr.shape != (n,):
-        raise ValueError(f"always_keep must have shape ({n},)")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
     _check("ress_select_topk", LIB.ress_select_topk(
-        _ptr(key, "key", torch.float64, (H, n, n)), shape.c(), keep_p, alw_p,
-        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
-        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
+        _ptr(key, "key", torch.float64, (H, nq, nk)), shape.c(), keep_p, alw_p,
+        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)), _stream(stream)))
 
 
 def ress_select_cdf(P, shape: Shape, keep: Sequence[int], always_keep, tau: float,
                     k_max: int, kept_idx, kept_cnt, stream=None):
-    H, n = shape.H, shape.n
+    H, nq, nk = shape.H, shape.nq, shape.nk
     keep_arr, keep_p = _host_i32(keep, "keep")
     if keep_arr is not None and keep_arr.shape != (H,):
         raise ValueError(f"keep must have shape ({H},)")
     alw_arr, alw_p = _host_u8(always_keep, "always_keep")
-    if alw_arr is not None and alw_arr.shape != (n,):
-        raise ValueError(f"always_keep must have shape ({n},)")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
     _check("ress_select_cdf", LIB.ress_select_cdf(
-        _ptr(P, "P", torch.float64, (H, n, n)), shape.c(), keep_p, alw_p, float(tau),
-        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
-        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)), _stream(stream)))
+        _ptr(P, "P", torch.float64, (H, nq, nk)), shape.c(), keep_p, alw_p, float(tau),
+        int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)), _stream(stream)))
 
 
 def ress_refine_workspace_size(shape: Shape) -> int:
@@ -239,7 +256,7 @@ def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
                         kept_cnt, J_init=None, J_final=None, workspace=None, stream=None):
     """workspace: a device uint8 tensor of at least ress_refine_workspace_size
     bytes (allocated here when None)."""
-    H, n, D = shape.H, shape.n, shape.D
+    H, nq, nk, D = shape.H, shape.nq, shape.nk, shape.D
     if workspace is None:
         workspace = torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
                                 device=kept_idx.device if isinstance(kept_idx, torch.Tensor)
@@ -250,15 +267,15 @@ def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
     if keep_arr is not None and keep_arr.shape != (H,):
         raise ValueError(f"keep must have shape ({H},)")
     alw_arr, alw_p = _host_u8(always_keep, "always_keep")
-    if alw_arr is not None and alw_arr.shape != (n,):
-        raise ValueError(f"always_keep must have shape ({n},)")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
     _check("ress_refine_dropset", LIB.ress_refine_dropset(
-        _ptr(P, "P", f64, (H, n, n)), _ptr(key, "key", f64, (H, n, n)),
-        _ptr(vpool, "vpool", f64, (H, n, D)), _ptr(vout, "vout", f64, (H, n, D)),
+        _ptr(P, "P", f64, (H, nq, nk)), _ptr(key, "key", f64, (H, nq, nk)),
+        _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(vout, "vout", f64, (H, nq, D)),
         _ptr(M, "M", f64, (H, D, D)), shape.c(), keep_p, alw_p, int(rounds), float(rho),
-        float(eps), int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)),
-        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)),
-        _ptr(J_init, "J_init", f64, (H, n)), _ptr(J_final, "J_final", f64, (H, n)),
+        float(eps), int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)),
+        _ptr(J_init, "J_init", f64, (H, nq)), _ptr(J_final, "J_final", f64, (H, nq)),
         ws_ptr, workspace.numel(), _stream(stream)))
 
 
@@ -266,11 +283,11 @@ def ress_sparse_attn_fwd(q, k, v, shape: Shape, kept_idx, kept_cnt, k_max: int,
                          scale: float, out, lse=None, stream=None):
     dt = _dtype_code(q)
     tok = (shape.H, shape.N_pad, shape.D)
-    H, n = shape.H, shape.n
+    H, nq = shape.H, shape.nq
     _check("ress_sparse_attn_fwd", LIB.ress_sparse_attn_fwd(
         _ptr(q, "q", q.dtype, tok), _ptr(k, "k", q.dtype, tok), _ptr(v, "v", q.dtype, tok),
         dt, shape.c(),
-        _ptr(kept_idx, "kept_idx", torch.int32, (H, n, k_max)) if kept_idx is not None else None,
-        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, n)) if kept_cnt is not None else None,
+        _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)) if kept_idx is not None else None,
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)) if kept_cnt is not None else None,
         int(k_max), float(scale), _ptr(out, "out", q.dtype, tok),
         _ptr(lse, "lse", torch.float32, (H, shape.N_pad)), _stream(stream)))

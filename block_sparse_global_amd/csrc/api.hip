@@ -59,14 +59,18 @@ int check_shape(const ress_shape& s) {
     return fail(RESS_ERR_INVALID_ARG,
                 "N=%d must satisfy N_pad-B < N <= N_pad (N_pad=%d, B=%d)", s.N,
                 s.N_pad, s.B);
-  const int n = s.N_pad / s.B;
-  if (n > RESS_MAX_BLOCKS)
-    return fail(RESS_ERR_UNSUPPORTED, "n=%d blocks exceeds the cap of %d", n,
+  if (s.Bk != 0 && ((s.Bk != 64 && s.Bk != 128) || s.Bk > s.B))
+    return fail(RESS_ERR_UNSUPPORTED,
+                "Bk=%d: key block size must be 0 (= B), or 64 or 128 and at most B=%d",
+                s.Bk, s.B);
+  const int nq = ress::n_qblocks(s), nk = ress::n_kblocks(s);
+  if (nq > RESS_MAX_BLOCKS || nk > RESS_MAX_BLOCKS)
+    return fail(RESS_ERR_UNSUPPORTED, "n_q=%d / n_k=%d blocks exceed the cap of %d", nq, nk,
                 RESS_MAX_BLOCKS);
   // element counts of the largest tensors must fit the 64-bit offsets used
-  // in the kernels; [H][n][n] maps with H*n*n < 2^40 are far inside that.
-  if ((double)s.H * n * n > 1e12)
-    return fail(RESS_ERR_UNSUPPORTED, "H*n*n too large");
+  // in the kernels; [H][n_q][n_k] maps below 2^40 elements are far inside.
+  if ((double)s.H * nq * nk > 1e12)
+    return fail(RESS_ERR_UNSUPPORTED, "H*n_q*n_k too large");
   return RESS_OK;
 }
 
@@ -84,7 +88,7 @@ int make_sel_config(const ress_shape& s, const int32_t* keep,
   if (s.H > RESS_MAX_SEL_HEADS)
     return fail(RESS_ERR_UNSUPPORTED, "H=%d exceeds %d heads for selection",
                 s.H, RESS_MAX_SEL_HEADS);
-  const int n = s.N_pad / s.B;
+  const int n = ress::n_kblocks(s);  // flags and budgets count key blocks
   memset(cfg, 0, sizeof *cfg);
   int n_always = 0;
   if (always_keep != nullptr) {
@@ -103,7 +107,7 @@ int make_sel_config(const ress_shape& s, const int32_t* keep,
   for (int h = 0; h < s.H; ++h) {
     const int k = keep[h];
     if (k < 2 || k > n)
-      return fail(RESS_ERR_INVALID_ARG, "keep[%d]=%d must lie in [2, n=%d]", h,
+      return fail(RESS_ERR_INVALID_ARG, "keep[%d]=%d must lie in [2, n_k=%d]", h,
                   k, n);
     if (k <= n_always)
       return fail(RESS_ERR_INVALID_ARG,
@@ -113,7 +117,7 @@ int make_sel_config(const ress_shape& s, const int32_t* keep,
     if (k > kmax_needed) kmax_needed = k;
   }
   if (k_max < kmax_needed || k_max > n)
-    return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [max keep=%d, n=%d]",
+    return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [max keep=%d, n_k=%d]",
                 k_max, kmax_needed, n);
   return RESS_OK;
 }
@@ -156,7 +160,10 @@ int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int a = 0; a < 3; ++a) {
     if (in[a] == nullptr) continue;
-    hipError_t e = ress::launch_block_pool(in[a], dtype, shape, out[a], st);
+    // queries in blocks of B, keys and values in blocks of Bk
+    const int blk = a == 0 ? shape.B : ress::key_block(shape);
+    const int nb = a == 0 ? ress::n_qblocks(shape) : ress::n_kblocks(shape);
+    hipError_t e = ress::launch_block_pool(in[a], dtype, shape, blk, nb, out[a], st);
     if (e != hipSuccess) return hip_status(e, "block_pool launch");
   }
   return ok();
@@ -188,10 +195,10 @@ int ress_block_score(const double* qpool, const double* kpool,
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = ress::launch_block_map(qpool, kpool, shape, scale, P, st);
   if (e != hipSuccess) return hip_status(e, "block_map launch");
-  const int n = shape.N_pad / shape.B;
   if (mode == RESS_SCORE_PROB) {
     if (key != nullptr && key != P) {
-      e = ress::launch_copy(P, key, (size_t)shape.H * n * n, st);
+      e = ress::launch_copy(P, key,
+                            (size_t)shape.H * ress::n_qblocks(shape) * ress::n_kblocks(shape), st);
       if (e != hipSuccess) return hip_status(e, "copy launch");
     }
     return ok();
@@ -298,9 +305,9 @@ int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
     return fail(RESS_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (kept_idx != nullptr) {
     REQUIRE_PTR(kept_cnt);
-    const int n = shape.N_pad / shape.B;
+    const int n = ress::n_kblocks(shape);
     if (k_max < 1 || k_max > n)
-      return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [1, n=%d]", k_max, n);
+      return fail(RESS_ERR_INVALID_ARG, "k_max=%d must lie in [1, n_k=%d]", k_max, n);
   }
   hipError_t e = ress::launch_attn(q, k, v, dtype, shape, kept_idx, kept_cnt,
                                    k_max, scale, out, lse,

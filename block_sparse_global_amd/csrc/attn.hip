@@ -5,7 +5,8 @@
 // float32 accumulation, for gfx950.
 //
 // Work decomposition: one workgroup per (query block, head); BLK/32 waves,
-// each owning 32 query rows. Per kept key block the K and V tiles are copied
+// each owning 32 query rows; key blocks hold KBLK <= BLK keys (KBLK = BLK, or
+// 64-key blocks under 128-query blocks). Per kept key block the K and V tiles are copied
 // straight from HBM into LDS (global_load_lds, double-buffered: the next kept
 // block streams in while the current one is computed) and every wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T held in
@@ -116,16 +117,21 @@ __device__ inline float max_halves(float x) {
 // for numerator and denominator.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int BLK, typename Tin, typename Tout>
+template <int BLK, int KBLK, typename Tin, typename Tout>
 __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     const Tin* __restrict__ Q, const Tin* __restrict__ Kx,
     const Tin* __restrict__ Vx, const int32_t* __restrict__ kept_idx,
     const int32_t* __restrict__ kept_cnt, int k_max, int n, int N, int N_pad,
     float scale, Tout* __restrict__ out, float* __restrict__ lse) {
+  // n: key blocks (of KBLK keys) per head; gridDim.x: query blocks per head
+  static_assert(KBLK <= BLK && BLK % KBLK == 0, "key blocks no larger than query blocks");
   constexpr int kThreads = BLK * 2;  // BLK/32 waves of 64
-  constexpr int kKT = BLK / 32;      // 32-key tiles per block
-  constexpr int kTile = BLK * kD;    // elements per K or V tile
-  // One K buffer and two V buffers (48 KB at BLK = 128, so three workgroups
+  constexpr int kKT = KBLK / 32;     // 32-key tiles per key block
+  constexpr int kTile = KBLK * kD;   // elements per K or V tile
+  constexpr int kRowsPerWave = KBLK / (BLK / 32);  // tile rows each wave copies
+  constexpr int kWin = kRowsPerWave / 8;           // 8-row copy windows per wave
+  static_assert(kRowsPerWave % 16 == 0, "the K swizzle repeats every 16 rows");
+  // One K buffer and two V buffers (48 KB at KBLK = 128, so three workgroups
   // share a CU): V of the next kept block streams in during the whole of the
   // current block, K of the next block once every wave has finished its
   // S = K Q^T product.
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   int cnt = n;
   const_i32p list = nullptr;
   if (kept_idx != nullptr) {
-    const size_t row = (size_t)h * n + i;
+    const size_t row = (size_t)h * gridDim.x + i;
     cnt = ((const_i32p)kept_cnt)[row];
     cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
     list = (const_i32p)(kept_idx + row * k_max);
@@ -188,14 +194,14 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   auto block_of = [&](int kb) { return list ? list[kb] : kb; };
 
   // ---- staging of the K or V tile of block j into an LDS buffer. Each wave
-  // copies 4 windows of 8 rows; in window it, lane l fills row
-  // r = 32*w + 8*it + l/8 at physical chunk l%8, i.e. logical chunk
+  // copies kWin windows of 8 rows; in window it, lane l fills row
+  // r = kRowsPerWave*w + 8*it + l/8 at physical chunk l%8, i.e. logical chunk
   // (l%8) ^ swz(r). For V, swz(r) = 2*((l/8)&3) does not depend on it; for
-  // K, swz(r) = (l/16) ^ (4*(it&1)). So two per-lane offsets (windows 0 and
-  // 1) plus compile-time row steps cover all windows. Rows past N (last
-  // block only) are read from row N-1: finite data whose scores are masked
-  // to -inf, so p = 0 multiplies a finite V row.
-  const int row0 = 32 * w + (lane >> 3);
+  // K, swz(r) = (l/16) ^ (4*(it&1)) (kRowsPerWave is a multiple of 16). So
+  // two per-lane offsets (windows 0 and 1) plus compile-time row steps cover
+  // all windows. Rows past N (last block only) are read from row N-1: finite
+  // data whose scores are masked to -inf, so p = 0 multiplies a finite V row.
+  const int row0 = kRowsPerWave * w + (lane >> 3);
   const int kgo0 = row0 * kD + (((lane & 7) ^ (lane >> 4)) * 8);
   const int kgo1 = (row0 + 8) * kD + (((lane & 7) ^ (lane >> 4) ^ 4) * 8);
   const int vgo0 = row0 * kD + (((lane & 7) ^ (((lane >> 3) & 3) << 1)) * 8);
@@ -207,31 +213,33 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
       // block base (uniform) + 32-bit per-lane byte offset: the copies use
       // the scalar-base addressing form
       const char* base = reinterpret_cast<const char*>(
-          X + head_off + (size_t)__builtin_amdgcn_readfirstlane(j) * BLK * kD);
-      const bool full = (j + 1) * BLK <= N;
+          X + head_off + (size_t)__builtin_amdgcn_readfirstlane(j) * KBLK * kD);
+      const bool full = (j + 1) * KBLK <= N;
       if (full) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
+        for (int it = 0; it < kWin; ++it) {
           const uint32_t off = 2u * (uint32_t)tile_off(it, is_v);
-          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off),
+                      dst + (kWin * w + it) * 512);
         }
       } else {
-        const int last = N - 1 - j * BLK;
+        const int last = N - 1 - j * KBLK;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
+        for (int it = 0; it < kWin; ++it) {
           const int r = row0 + 8 * it;
           const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) + (min(r, last) - r) * kD);
-          gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (4 * w + it) * 512);
+          gload_lds16(reinterpret_cast<const uint16_t*>(base + off),
+                      dst + (kWin * w + it) * 512);
         }
       }
     } else {
       // float32 inputs: rounded to bf16 (nearest even) through registers
-      const Tin* base = X + head_off + (size_t)j * BLK * kD;
+      const Tin* base = X + head_off + (size_t)j * KBLK * kD;
 #pragma unroll
-      for (int it = 0; it < BLK * 8 / kThreads; ++it) {
+      for (int it = 0; it < KBLK * 8 / kThreads; ++it) {
         const int idx = tid + it * kThreads;
         const int r = idx >> 3, c = idx & 7;
-        const int rr = min(r, N - 1 - j * BLK);
+        const int rr = min(r, N - 1 - j * KBLK);
         const int sw = is_v ? v_swz(r) : k_swz(r);
         *reinterpret_cast<uint4*>(&dst[r * kD + ((c ^ sw) * 8)]) =
             load_row8(base + (size_t)rr * kD + c * 8);
@@ -295,8 +303,8 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     // block's valid-key count, which changes with j, keeps the compiler from
     // hoisting loop-invariant compare masks; the lane-half term is folded
     // into the limit so that the compares use immediate key offsets only.
-    const int live_keys = N - j * BLK;
-    if (live_keys < BLK) {
+    const int live_keys = N - j * KBLK;
+    if (live_keys < KBLK) {
       const int lim = live_keys - 4 * half;
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
@@ -425,17 +433,21 @@ hipError_t launch_t(const Tin* q, const Tin* k, const Tin* v,
                     const ress_shape& s, const int32_t* kept_idx,
                     const int32_t* kept_cnt, int32_t k_max, float scale,
                     void* out, float* lse, hipStream_t st) {
-  const int n = s.N_pad / s.B;
-  dim3 grid(n, s.H);
+  const int nk = n_kblocks(s);
+  dim3 grid(n_qblocks(s), s.H);
   using Tout = Tin;
   Tout* o = static_cast<Tout*>(out);
-  if (s.B == 128)
-    hipLaunchKernelGGL((attn_kernel<128, Tin, Tout>), grid, dim3(256), 0, st,
-                       q, k, v, kept_idx, kept_cnt, k_max, n, s.N, s.N_pad,
+  if (s.B == 128 && key_block(s) == 128)
+    hipLaunchKernelGGL((attn_kernel<128, 128, Tin, Tout>), grid, dim3(256), 0, st,
+                       q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
+                       scale, o, lse);
+  else if (s.B == 128)
+    hipLaunchKernelGGL((attn_kernel<128, 64, Tin, Tout>), grid, dim3(256), 0, st,
+                       q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
                        scale, o, lse);
   else
-    hipLaunchKernelGGL((attn_kernel<64, Tin, Tout>), grid, dim3(128), 0, st,
-                       q, k, v, kept_idx, kept_cnt, k_max, n, s.N, s.N_pad,
+    hipLaunchKernelGGL((attn_kernel<64, 64, Tin, Tout>), grid, dim3(128), 0, st,
+                       q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
                        scale, o, lse);
   return hipGetLastError();
 }

@@ -79,26 +79,25 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 }
 
 template <typename T>
-hipError_t launch_t(const T* x, const ress_shape& s, double* out,
+hipError_t launch_t(const T* x, const ress_shape& s, int blk, int nb, double* out,
                     hipStream_t st) {
-  const int n = s.N_pad / s.B;
-  dim3 grid(n, s.H);
-  if (s.B == 128)
+  dim3 grid(nb, s.H);
+  if (blk == 128)
     hipLaunchKernelGGL((pool_kernel<T, 128>), grid, dim3(kThreads), 0, st, x,
-                       out, s.N, s.N_pad, n);
+                       out, s.N, s.N_pad, nb);
   else
     hipLaunchKernelGGL((pool_kernel<T, 64>), grid, dim3(kThreads), 0, st, x,
-                       out, s.N, s.N_pad, n);
+                       out, s.N, s.N_pad, nb);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
-                             double* out, hipStream_t st) {
+                             int blk, int nb, double* out, hipStream_t st) {
   if (dtype == RESS_DTYPE_BF16)
-    return launch_t(static_cast<const uint16_t*>(x), s, out, st);
-  return launch_t(static_cast<const float*>(x), s, out, st);
+    return launch_t(static_cast<const uint16_t*>(x), s, blk, nb, out, st);
+  return launch_t(static_cast<const float*>(x), s, blk, nb, out, st);
 }
 
 }  // namespace ress

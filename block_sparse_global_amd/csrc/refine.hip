@@ -17,7 +17,9 @@
 //     J = G / K^2 (Eq. 12) and keeps the drop set with the smallest J seen
 //     (track-best).
 // An init kernel builds the starting state from the top-k keep lists and a
-// final kernel writes the best sets back as keep lists.
+// final kernel writes the best sets back as keep lists. Rows are the n_q
+// query blocks of every head, each of n = n_k key blocks; the per-row
+// kernels run one workgroup per (row i, head h), gridDim.x = n_q.
 // s_j (Eq. 6) comes from the drift key of Eq. 7: s = key * max(1 - P, eps).
 // Every sum has a fixed order, so results are bit-reproducible.
 #include "ress_internal.h"
@@ -35,12 +37,12 @@ struct alignas(64) RowState {
 
 // Workspace regions (each 256-byte aligned).
 struct RefineWs {
-  uint64_t* gains;  // [H][n][n] order keys of the gains
-  uint8_t* fcur;    // [H][n][fs] 1 = block in the current drop set D
-  uint8_t* fbest;   // [H][n][fs] 1 = block in the best drop set
-  double* g;        // [H][n][64]
-  double* u;        // [H][n][64] M g
-  RowState* rs;     // [H][n]
+  uint64_t* gains;  // [H][n_q][n_k] order keys of the gains
+  uint8_t* fcur;    // [H][n_q][fs] 1 = block in the current drop set D
+  uint8_t* fbest;   // [H][n_q][fs] 1 = block in the best drop set
+  double* g;        // [H][n_q][64]
+  double* u;        // [H][n_q][64] M g
+  RowState* rs;     // [H][n_q]
 };
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -52,15 +54,15 @@ __host__ __device__ inline int flag_stride(int n) { return (n + 15) & ~15; }
 struct WsLayout {
   size_t gains, fcur, fbest, g, u, rs, total;
   explicit WsLayout(const ress_shape& s) {
-    const size_t n = (size_t)(s.N_pad / s.B), H = (size_t)s.H;
+    const size_t nq = (size_t)n_qblocks(s), nk = (size_t)n_kblocks(s), H = (size_t)s.H;
     size_t off = 0;
-    gains = off; off += align256(H * n * n * 8);
-    const size_t fs = (size_t)flag_stride((int)n);
-    fcur = off;  off += align256(H * n * fs);
-    fbest = off; off += align256(H * n * fs);
-    g = off;     off += align256(H * n * kD * 8);
-    u = off;     off += align256(H * n * kD * 8);
-    rs = off;    off += align256(H * n * sizeof(RowState));
+    gains = off; off += align256(H * nq * nk * 8);
+    const size_t fs = (size_t)flag_stride((int)nk);
+    fcur = off;  off += align256(H * nq * fs);
+    fbest = off; off += align256(H * nq * fs);
+    g = off;     off += align256(H * nq * kD * 8);
+    u = off;     off += align256(H * nq * kD * 8);
+    rs = off;    off += align256(H * nq * sizeof(RowState));
     total = off;
   }
   RefineWs at(void* base) const {
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
   int32_t* slist = reinterpret_cast<int32_t*>(smem + ((n + 15) & ~15));  // [n]
   double* gl = reinterpret_cast<double*>(slist + ((n + 3) & ~3));        // [64]
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const size_t row = (size_t)h * n + i;
+  const size_t row = (size_t)h * gridDim.x + i;
   const double* Prow = P + row * n;
   const double* Vh = vpool + (size_t)h * n * kD;
 
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
 }
 
 // ---------------------------------------------------------------- gains
-// C[i][j] = u_i . V_j over a 64 x 64 tile (rows i, key blocks j) of one head,
+// C[i][j] = u_i . V_j over a 64 x 64 tile (rows i < nq, key blocks j < nk) of one head,
 // the 64 dims staged through LDS in two halves, transposed. Thread (ti, tj)
 // owns rows i0 + ti + 16a and key blocks j0 + tj + 16b (a, b < 4), so that
 // the sixteen lanes of a row group read sixteen consecutive key blocks, in
@@ -193,7 +195,7 @@ constexpr int kGPad = 66;  // padded row of a transposed stage
 
 __global__ __launch_bounds__(256) void refine_gains_kernel(
     const double* __restrict__ P, const double* __restrict__ key,
-    const double* __restrict__ vpool, int n, SelConfig cfg, int round, double rho,
+    const double* __restrict__ vpool, int nq, int nk, SelConfig cfg, int round, double rho,
     double eps, RefineWs ws) {
   const int h = blockIdx.z;
   if (swaps_of(cfg, h, round, rho) <= 0) return;  // no swaps for this head
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
   const int tid = threadIdx.x;
   const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
   const int ti = tid >> 4, tj = tid & 15;
-  const double* Uh = ws.u + (size_t)h * n * kD;
-  const double* Vh = vpool + (size_t)h * n * kD;
+  const double* Uh = ws.u + (size_t)h * nq * kD;
+  const double* Vh = vpool + (size_t)h * nk * kD;
 
   double acc[4][4];
 #pragma unroll
@@ -211,9 +213,10 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
 
-  // staging: thread t copies row t/4 (clamped to n-1), dims (t%4)*8 .. +7
+  // staging: thread t copies row t/4 (clamped to the last row), dims
+  // (t%4)*8 .. +7
   const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const int ri = min(i0 + lr, n - 1), rj = min(j0 + lr, n - 1);
+  const int ri = min(i0 + lr, nq - 1), rj = min(j0 + lr, nk - 1);
 #pragma unroll
   for (int kc = 0; kc < kD; kc += kGK) {
     const double2* us = reinterpret_cast<const double2*>(Uh + (size_t)ri * kD + kc + lc);
@@ -250,13 +253,13 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
   // epilogue: the exact objective decrease of each swap (Eq. 13-16). Out
   // of range rows and blocks load from a clamped valid address and are not
   // stored.
-  const int fs = flag_stride(n);
+  const int fs = flag_stride(nk);
   double pv[4][4], kv[4][4];
   uint8_t fv[4][4];
   double sK[4], sG[4], sJ[4], svu[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const size_t row = (size_t)h * n + min(i0 + ti + 16 * a, n - 1);
+    const size_t row = (size_t)h * nq + min(i0 + ti + 16 * a, nq - 1);
     const RowState* st = ws.rs + row;
     sK[a] = st->K;
     sG[a] = st->G;
@@ -264,16 +267,16 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
     svu[a] = st->vu;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int j = min(j0 + tj + 16 * b, n - 1);
-      pv[a][b] = P[row * n + j];
-      kv[a][b] = key[row * n + j];
+      const int j = min(j0 + tj + 16 * b, nk - 1);
+      pv[a][b] = P[row * nk + j];
+      kv[a][b] = key[row * nk + j];
       fv[a][b] = ws.fcur[row * fs + j];
     }
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int i = i0 + ti + 16 * a;
-    const size_t row = (size_t)h * n + i;
+    const size_t row = (size_t)h * nq + i;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int j = j0 + tj + 16 * b;
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
         const double Ku = sK[a] - p;
         dJ = (Ku > 0.0) ? sJ[a] - (sG[a] + dG) / (Ku * Ku) : -INFINITY;
       }
-      if (i < n && j < n) ws.gains[row * n + j] = order_key(dJ);
+      if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
     }
   }
 }
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
   uint8_t* flags = smem + 1536 + 4 * ((n + 3) & ~3);                        // [fs]
   uint64_t* gkeys = reinterpret_cast<uint64_t*>(flags + flag_stride(n));    // [n] (KPL = 0)
 
-  const size_t row = (size_t)h * n + i;
+  const size_t row = (size_t)h * gridDim.x + i;
   const int fs = flag_stride(n);
   const uint4* fc = reinterpret_cast<const uint4*>(ws.fcur + row * fs);
   const uint64_t* grow = ws.gains + row * n;
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(64) void refine_final_kernel(
     double* __restrict__ J_final) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const size_t row = (size_t)h * n + i;
+  const size_t row = (size_t)h * gridDim.x + i;
   const int fs = flag_stride(n);
   const uint4* fsrc = reinterpret_cast<const uint4*>(ws.fbest + row * fs);
   for (int c = lane; c < fs / 16; c += 64) reinterpret_cast<uint4*>(smem)[c] = fsrc[c];
@@ -578,24 +581,29 @@ hipError_t launch_refine(const double* P, const double* key,
                          double eps, int32_t k_max, int32_t* kept_idx,
                          int32_t* kept_cnt, double* J_init, double* J_final,
                          void* workspace, hipStream_t st) {
-  const int n = s.N_pad / s.B;
+  const int nq = n_qblocks(s), n = n_kblocks(s);
   const RefineWs ws = WsLayout(s).at(workspace);
-  const dim3 rows(n, s.H);
+  const dim3 rows(nq, s.H);
   const size_t lds_init = (size_t)((n + 15) & ~15) + 4 * (size_t)((n + 3) & ~3) + 512;
   hipLaunchKernelGGL(refine_init_kernel, rows, dim3(64), lds_init, st, P, vpool, vout, M, n,
                      cfg, k_max, kept_idx, kept_cnt, ws);
-  const bool keys_in_regs = n <= 17 * 64;
+  // the row's keys in registers (17 or 34 per lane) up to 2176 key blocks,
+  // in LDS beyond
+  const int kpl = n <= 17 * 64 ? 17 : (n <= 34 * 64 ? 34 : 0);
   const size_t lds_sel = 1536 + 4 * (size_t)((n + 3) & ~3) + (size_t)((n + 15) & ~15) +
-                         (keys_in_regs ? 0 : 8 * (size_t)n);
-  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
+                         (kpl > 0 ? 0 : 8 * (size_t)n);
+  const dim3 tiles((n + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
   for (int r = 0; r < rounds; ++r) {
     int m_max = 0;
     for (int h = 0; h < s.H; ++h) m_max = max(m_max, swaps_of(cfg, h, r, rho));
     if (m_max <= 0) continue;  // no head swaps in this round
-    hipLaunchKernelGGL(refine_gains_kernel, tiles, dim3(256), 0, st, P, key, vpool, n, cfg,
-                       r, rho, eps, ws);
-    if (keys_in_regs)
+    hipLaunchKernelGGL(refine_gains_kernel, tiles, dim3(256), 0, st, P, key, vpool, nq, n,
+                       cfg, r, rho, eps, ws);
+    if (kpl == 17)
       hipLaunchKernelGGL((refine_select_kernel<17>), rows, dim3(64), lds_sel, st, P, vpool,
+                         vout, M, n, cfg, r, rho, ws);
+    else if (kpl == 34)
+      hipLaunchKernelGGL((refine_select_kernel<34>), rows, dim3(64), lds_sel, st, P, vpool,
                          vout, M, n, cfg, r, rho, ws);
     else
       hipLaunchKernelGGL((refine_select_kernel<0>), rows, dim3(64), lds_sel, st, P, vpool,

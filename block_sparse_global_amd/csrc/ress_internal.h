@@ -8,6 +8,15 @@
 
 namespace ress {
 
+// Block counts of a shape: n_q = N_pad / B query blocks of B tokens and
+// n_k = ceil(N / Bk) key blocks of Bk tokens (Bk = 0 means Bk = B).
+inline int key_block(const ress_shape& s) { return s.Bk > 0 ? s.Bk : s.B; }
+inline int n_qblocks(const ress_shape& s) { return s.N_pad / s.B; }
+inline int n_kblocks(const ress_shape& s) {
+  const int bk = key_block(s);
+  return (s.N + bk - 1) / bk;
+}
+
 // Always-kept key blocks as a bitmask (n <= 4096 -> 64 words) and per-head
 // keep budgets; small enough to travel in the kernel arguments, so the
 // selection kernels need no extra device memory.
@@ -50,8 +59,10 @@ __device__ inline void wave_lds_sync() {
 
 // Launchers (defined next to their kernels). Each returns hipGetLastError()
 // of its launches.
+// Pools x in blocks of `blk` tokens (nb blocks, the last one partial when
+// N is not a multiple of blk).
 hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
-                             double* out, hipStream_t st);
+                             int blk, int nb, double* out, hipStream_t st);
 
 hipError_t launch_block_map(const double* qpool, const double* kpool,
                             const ress_shape& s, double scale, double* P,

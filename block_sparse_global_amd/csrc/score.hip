@@ -7,7 +7,9 @@
 // q_ij = vout^T M vout - 2 vout^T M V_j + V_j^T M V_j (the Eq. 9 expansion,
 // so no per-pair D-vector is formed), key = P sqrt(max(q,0)) / max(1-P, eps).
 //
-// The three n x n x 64 products (logits, vout = P V, (M vout) . V_j) run as
+// Maps are [H][n_q][n_k] (query-block rows, key-block columns; the two
+// counts differ when key blocks are smaller than query blocks).
+// The three n_q x n_k x 64 products (logits, vout = P V, (M vout) . V_j) run as
 // tiled matrix products with their elementwise steps in the epilogues; the
 // row softmax is one wave per row. Every output element is one fma chain in
 // ascending index order and every reduction has a fixed order (no
@@ -37,7 +39,8 @@ __device__ inline double wave_max(double v) {
 // rows i0 + ti + 16a and columns j0 + tj + 16b (a, b < 4): the sixteen lanes
 // of a row group touch sixteen consecutive columns. acc[a][b] is one fma
 // chain over the dims in ascending order. `stage_a` fills the A half (rows
-// clamped to n-1), so that callers can form A on the fly.
+// clamped to the last row), so that callers can form A on the fly; B has nb
+// rows.
 constexpr int kGT = 64;    // tile edge
 constexpr int kGK = 32;    // dims per LDS stage
 constexpr int kGPad = 66;  // padded row of a transposed stage
@@ -48,12 +51,12 @@ struct TileSmem {
 };
 
 template <typename StageA>
-__device__ inline void tile_dot(const double* __restrict__ B, int n, int j0, StageA stage_a,
+__device__ inline void tile_dot(const double* __restrict__ B, int nb, int j0, StageA stage_a,
                                 TileSmem& sm, double (&acc)[4][4]) {
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tj = tid & 15;
   const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const int rj = min(j0 + lr, n - 1);
+  const int rj = min(j0 + lr, nb - 1);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -92,14 +95,14 @@ __device__ inline void tile_dot(const double* __restrict__ B, int n, int j0, Sta
 
 // Logits scale * qpool_i . kpool_j of one 64 x 64 tile, written into P.
 __global__ __launch_bounds__(kThreads) void logits_kernel(
-    const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int n,
-    double* __restrict__ P) {
+    const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int nq,
+    int nk, double* __restrict__ P) {
   __shared__ TileSmem sm;
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
-  const double* qh = qpool + (size_t)h * n * kD;
+  const double* qh = qpool + (size_t)h * nq * kD;
   auto stage_q = [&](int r, int d0, double (&x)[8]) {
-    const double2* src = reinterpret_cast<const double2*>(qh + (size_t)min(i0 + r, n - 1) * kD + d0);
+    const double2* src = reinterpret_cast<const double2*>(qh + (size_t)min(i0 + r, nq - 1) * kD + d0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const double2 v = src[e];
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(
     }
   };
   double acc[4][4];
-  tile_dot(kpool + (size_t)h * n * kD, n, j0, stage_q, sm, acc);
+  tile_dot(kpool + (size_t)h * nk * kD, nk, j0, stage_q, sm, acc);
   const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -116,19 +119,20 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int j = j0 + tj + 16 * b;
-      if (i < n && j < n) P[((size_t)h * n + i) * n + j] = scale * acc[a][b];
+      if (i < nq && j < nk) P[((size_t)h * nq + i) * nk + j] = scale * acc[a][b];
     }
   }
 }
 
-// Row softmax in place, one wave per row: max, exponentials and their sum,
-// normalisation. KPL > 0: the row (KPL >= ceil(n / 64) values per lane) is
-// held in registers; KPL = 0: in LDS (8 n bytes).
+// Row softmax in place, one wave per row (row i of head h is workgroup
+// (i, h)) of n values: max, exponentials and their sum, normalisation.
+// KPL > 0: the row (KPL >= ceil(n / 64) values per lane) is held in
+// registers; KPL = 0: in LDS (8 n bytes).
 template <int KPL>
 __global__ __launch_bounds__(64) void softmax_rows_kernel(int n, double* __restrict__ P) {
   extern __shared__ double rowbuf[];
   const int lane = threadIdx.x;
-  double* Prow = P + ((size_t)blockIdx.y * n + blockIdx.x) * n;
+  double* Prow = P + ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * n;
   constexpr int kK = KPL > 0 ? KPL : 1;
   double v[kK];
   double mx = -INFINITY;
@@ -212,7 +216,7 @@ constexpr int kVR = 32;  // rows per workgroup
 constexpr int kVJ = 64;  // key blocks per LDS stage
 
 __global__ __launch_bounds__(kThreads) void vout_kernel(
-    const double* __restrict__ P, const double* __restrict__ vpool, int n,
+    const double* __restrict__ P, const double* __restrict__ vpool, int nq, int nk,
     double* __restrict__ vout) {
   __shared__ double Ps[kVR][kVJ + 1];
   __shared__ double Vs[kVJ][kD + 2];
@@ -220,29 +224,29 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
   const int i0 = blockIdx.x * kVR;
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tj = tid & 15;
-  const double* Ph = P + (size_t)h * n * n;
-  const double* Vh = vpool + (size_t)h * n * kD;
+  const double* Ph = P + (size_t)h * nq * nk;
+  const double* Vh = vpool + (size_t)h * nk * kD;
   double acc[2][4] = {};
-  for (int jc = 0; jc < n; jc += kVJ) {
+  for (int jc = 0; jc < nk; jc += kVJ) {
     // P: 32 rows x 64 blocks (8 per thread); V: 64 blocks x 64 dims (16 per thread)
 #pragma unroll
     for (int e = 0; e < kVR * kVJ / kThreads; ++e) {
       const int idx = tid + e * kThreads;
       const int r = idx >> 6, c = idx & 63;
-      const int i = min(i0 + r, n - 1), j = jc + c;
-      Ps[r][c] = j < n ? Ph[(size_t)i * n + j] : 0.0;
+      const int i = min(i0 + r, nq - 1), j = jc + c;
+      Ps[r][c] = j < nk ? Ph[(size_t)i * nk + j] : 0.0;
     }
 #pragma unroll
     for (int e = 0; e < kVJ * kD / (2 * kThreads); ++e) {
       const int idx = tid + e * kThreads;
       const int r = idx >> 5, c2 = idx & 31;
-      const int j = min(jc + r, n - 1);
+      const int j = min(jc + r, nk - 1);
       const double2 x = reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[c2];
       Vs[r][2 * c2] = x.x;
       Vs[r][2 * c2 + 1] = x.y;
     }
     __syncthreads();
-    const int kmax = min(kVJ, n - jc);
+    const int kmax = min(kVJ, nk - jc);
     for (int k = 0; k < kmax; ++k) {
       const double p0 = Ps[ti][k], p1 = Ps[ti + 16][k];
 #pragma unroll
@@ -257,9 +261,9 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int i = i0 + ti + 16 * a;
-    if (i < n)
+    if (i < nq)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) vout[((size_t)h * n + i) * kD + tj + 16 * b] = acc[a][b];
+      for (int b = 0; b < 4; ++b) vout[((size_t)h * nq + i) * kD + tj + 16 * b] = acc[a][b];
   }
 }
 
@@ -269,18 +273,18 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
 __global__ __launch_bounds__(kThreads) void key_kernel(
     const double* __restrict__ P, const double* __restrict__ vpool,
     const double* __restrict__ M, const double* __restrict__ vmv,
-    const double* __restrict__ vout, int n, double eps, double* __restrict__ key) {
+    const double* __restrict__ vout, int nq, int nk, double eps, double* __restrict__ key) {
   __shared__ TileSmem sm;
   __shared__ double apart[2][kGT][4];
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
   const int tid = threadIdx.x;
-  const double* voh = vout + (size_t)h * n * kD;
+  const double* voh = vout + (size_t)h * nq * kD;
   const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;
   // stage w_i dims d0 .. d0+7 of row r; the partial vout . w over those
   // dims goes to apart[half][r][thread's quarter]
   auto stage_w = [&](int r, int d0, double (&x)[8]) {
-    const double* vr = voh + (size_t)min(i0 + r, n - 1) * kD;
+    const double* vr = voh + (size_t)min(i0 + r, nq - 1) * kD;
     double vo8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) vo8[e] = vr[d0 + e];
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
     apart[d0 >= kGK][r][(d0 % kGK) / 8] = pa;
   };
   double acc[4][4];
-  tile_dot(vpool + (size_t)h * n * kD, n, j0, stage_w, sm, acc);
+  tile_dot(vpool + (size_t)h * nk * kD, nk, j0, stage_w, sm, acc);
   const int ti = tid >> 4, tj = tid & 15;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -317,9 +321,9 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int j = j0 + tj + 16 * b;
-      if (i < n && j < n) {
-        const size_t off = ((size_t)h * n + i) * n + j;
-        const double q = fmax(ai - 2.0 * acc[a][b] + vmv[(size_t)h * n + j], 0.0);
+      if (i < nq && j < nk) {
+        const size_t off = ((size_t)h * nq + i) * nk + j;
+        const double q = fmax(ai - 2.0 * acc[a][b] + vmv[(size_t)h * nk + j], 0.0);
         const double p = P[off];
         key[off] = p * sqrt(q) / fmax(1.0 - p, eps);
       }
@@ -332,14 +336,17 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
 hipError_t launch_block_map(const double* qpool, const double* kpool,
                             const ress_shape& s, double scale, double* P,
                             hipStream_t st) {
-  const int n = s.N_pad / s.B;
-  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
-  hipLaunchKernelGGL(logits_kernel, tiles, dim3(kThreads), 0, st, qpool, kpool, scale, n, P);
-  const dim3 rows(n, s.H);
-  if (n <= 17 * 64)
-    hipLaunchKernelGGL((softmax_rows_kernel<17>), rows, dim3(64), 0, st, n, P);
+  const int nq = n_qblocks(s), nk = n_kblocks(s);
+  const dim3 tiles((nk + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
+  hipLaunchKernelGGL(logits_kernel, tiles, dim3(kThreads), 0, st, qpool, kpool, scale, nq, nk,
+                     P);
+  const dim3 rows(nq, s.H);
+  if (nk <= 17 * 64)
+    hipLaunchKernelGGL((softmax_rows_kernel<17>), rows, dim3(64), 0, st, nk, P);
+  else if (nk <= 34 * 64)
+    hipLaunchKernelGGL((softmax_rows_kernel<34>), rows, dim3(64), 0, st, nk, P);
   else
-    hipLaunchKernelGGL((softmax_rows_kernel<0>), rows, dim3(64), (size_t)n * 8, st, n, P);
+    hipLaunchKernelGGL((softmax_rows_kernel<0>), rows, dim3(64), (size_t)nk * 8, st, nk, P);
   return hipGetLastError();
 }
 
@@ -355,7 +362,7 @@ hipError_t launch_copy(const double* src, double* dst, size_t count,
 
 hipError_t launch_vmv(const double* vpool, const double* M,
                       const ress_shape& s, double* vmv, hipStream_t st) {
-  const int n = s.N_pad / s.B;
+  const int n = n_kblocks(s);
   const int per = kThreads / 64;
   dim3 grid((n + per - 1) / per, s.H);
   hipLaunchKernelGGL(vmv_kernel, grid, dim3(kThreads), 0, st, vpool, M, n,
@@ -366,12 +373,12 @@ hipError_t launch_vmv(const double* vpool, const double* M,
 hipError_t launch_drift(const double* P, const double* vpool, const double* M,
                         const double* vmv, const ress_shape& s, double eps,
                         double* key, double* vout, hipStream_t st) {
-  const int n = s.N_pad / s.B;
-  hipLaunchKernelGGL(vout_kernel, dim3((n + kVR - 1) / kVR, s.H), dim3(kThreads), 0, st, P,
-                     vpool, n, vout);
-  const dim3 tiles((n + kGT - 1) / kGT, (n + kGT - 1) / kGT, s.H);
-  hipLaunchKernelGGL(key_kernel, tiles, dim3(kThreads), 0, st, P, vpool, M, vmv, vout, n, eps,
-                     key);
+  const int nq = n_qblocks(s), nk = n_kblocks(s);
+  hipLaunchKernelGGL(vout_kernel, dim3((nq + kVR - 1) / kVR, s.H), dim3(kThreads), 0, st, P,
+                     vpool, nq, nk, vout);
+  const dim3 tiles((nk + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
+  hipLaunchKernelGGL(key_kernel, tiles, dim3(kThreads), 0, st, P, vpool, M, vmv, vout, nq, nk,
+                     eps, key);
   return hipGetLastError();
 }
 

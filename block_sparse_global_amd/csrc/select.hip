@@ -4,8 +4,9 @@
 // Transformers", §3 step (2), §4.1 Eq. 2, §4.4): per (head, query-block
 // row), keep the c_h candidates with the largest key plus every always-kept
 // block.
-// One workgroup owns one row; thread t owns the E consecutive key blocks
-// [t*E, t*E + E). Selection is exact: an MSB-first radix select over 64-bit
+// One workgroup owns one row (workgroup (i, h): query-block row i of head
+// h, gridDim.x = n_q rows per head, n key blocks per row); thread t owns the
+// E consecutive key blocks [t*E, t*E + E). Selection is exact: an MSB-first radix select over 64-bit
 // keys whose unsigned order equals the float64 order, with ties among equal
 // keys broken towards the lower block index by a block-wide prefix count.
 // No float atomics and fixed-order reductions: results are bit-reproducible.
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int h = blockIdx.y;
   const int t = threadIdx.x;
   __shared__ SelShared sh;
-  const double* row = key + ((size_t)h * n + i) * n;
+  const double* row = key + ((size_t)h * gridDim.x + i) * n;
   uint64_t u[E];
   uint32_t member = 0, always = 0;
 #pragma unroll
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   }
   const int c = cfg.keep[h] - cfg.n_always;
   const uint32_t sel = select_top<E>(u, member, c, sh);
-  const size_t r = (size_t)h * n + i;
+  const size_t r = (size_t)h * gridDim.x + i;
   write_kept<E>(sel | always, n, k_max, kept_idx + r * k_max, kept_cnt + r,
                 sh);
 }
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void cdf_kernel(
   const int i = blockIdx.x;
   const int h = blockIdx.y;
   const int t = threadIdx.x;
-  const double* row = P + ((size_t)h * n + i) * n;
+  const double* row = P + ((size_t)h * gridDim.x + i) * n;
   uint64_t u[E];
   uint32_t member = 0, always = 0;
 #pragma unroll
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void cdf_kernel(
         ++p;
       }
   }
-  const size_t r = (size_t)h * n + i;
+  const size_t r = (size_t)h * gridDim.x + i;
   write_kept<E>(kept, n, k_max, kept_idx + r * k_max, kept_cnt + r, sh);
 }
 
@@ -314,7 +315,7 @@ int pick_e(int n) {
 }
 
 template <int E>
-hipError_t launch_cdf_e(const double* P, int n, int H, const SelConfig& cfg,
+hipError_t launch_cdf_e(const double* P, int nq, int n, int H, const SelConfig& cfg,
                         double tau, int cap, int32_t k_max, int32_t* kept_idx,
                         int32_t* kept_cnt, hipStream_t st) {
   const size_t smem = cdf_smem_bytes(cap);
@@ -324,7 +325,7 @@ hipError_t launch_cdf_e(const double* P, int n, int H, const SelConfig& cfg,
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((cdf_kernel<E>), dim3(n, H), dim3(kThreads), smem, st, P, n,
+  hipLaunchKernelGGL((cdf_kernel<E>), dim3(nq, H), dim3(kThreads), smem, st, P, n,
                      cfg, tau, cap, k_max, kept_idx, kept_cnt);
   return hipGetLastError();
 }
@@ -334,15 +335,15 @@ hipError_t launch_cdf_e(const double* P, int n, int H, const SelConfig& cfg,
 hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg,
                       double tau, int32_t k_max, int32_t* kept_idx,
                       int32_t* kept_cnt, hipStream_t st) {
-  const int n = s.N_pad / s.B;
+  const int nq = n_qblocks(s), n = n_kblocks(s);
   int cap = 1;
   for (int h = 0; h < s.H; ++h) cap = max(cap, cfg.keep[h] - cfg.n_always);
   switch (pick_e(n)) {
-    case 1: return launch_cdf_e<1>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
-    case 2: return launch_cdf_e<2>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
-    case 4: return launch_cdf_e<4>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
-    case 8: return launch_cdf_e<8>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
-    case 16: return launch_cdf_e<16>(P, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 1: return launch_cdf_e<1>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 2: return launch_cdf_e<2>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 4: return launch_cdf_e<4>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 8: return launch_cdf_e<8>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    case 16: return launch_cdf_e<16>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -350,8 +351,8 @@ hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg
 hipError_t launch_topk(const double* key, const ress_shape& s,
                        const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,
                        int32_t* kept_cnt, hipStream_t st) {
-  const int n = s.N_pad / s.B;
-  dim3 grid(n, s.H);
+  const int n = n_kblocks(s);
+  dim3 grid(n_qblocks(s), s.H);
   switch (pick_e(n)) {
 #define RESS_CASE(E)                                                        \
   case E:                                                                   \

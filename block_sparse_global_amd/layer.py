@@ -54,20 +54,20 @@ class BlockSparseGlobalAttention:
         self.scale = float(scale if scale is not None else 1.0 / math.sqrt(shape.D))
         self.M = M
         self.k_max = int(self.keep.max())
-        H, n, D, Np = shape.H, shape.n, shape.D, shape.N_pad
+        H, nq, nk, D, Np = shape.H, shape.nq, shape.nk, shape.D, shape.N_pad
         f64 = dict(dtype=torch.float64, device=device)
-        self.qpool = torch.empty((H, n, D), **f64)
-        self.kpool = torch.empty((H, n, D), **f64)
+        self.qpool = torch.empty((H, nq, D), **f64)
+        self.kpool = torch.empty((H, nk, D), **f64)
         need_v = mode == "drift"
-        self.vpool = torch.empty((H, n, D), **f64) if need_v else None
-        self.P = torch.empty((H, n, n), **f64)
-        self.key = torch.empty((H, n, n), **f64) if mode == "drift" else None
-        self.vout = torch.empty((H, n, D), **f64) if need_v else None
-        self.vmv = torch.empty((H, n), **f64) if need_v else None
-        self.kept_idx = torch.empty((H, n, self.k_max), dtype=torch.int32, device=device)
-        self.kept_cnt = torch.empty((H, n), dtype=torch.int32, device=device)
-        self.J_init = torch.empty((H, n), **f64) if rounds > 0 else None
-        self.J_final = torch.empty((H, n), **f64) if rounds > 0 else None
+        self.vpool = torch.empty((H, nk, D), **f64) if need_v else None
+        self.P = torch.empty((H, nq, nk), **f64)
+        self.key = torch.empty((H, nq, nk), **f64) if mode == "drift" else None
+        self.vout = torch.empty((H, nq, D), **f64) if need_v else None
+        self.vmv = torch.empty((H, nk), **f64) if need_v else None
+        self.kept_idx = torch.empty((H, nq, self.k_max), dtype=torch.int32, device=device)
+        self.kept_cnt = torch.empty((H, nq), dtype=torch.int32, device=device)
+        self.J_init = torch.empty((H, nq), **f64) if rounds > 0 else None
+        self.J_final = torch.empty((H, nq), **f64) if rounds > 0 else None
         self.workspace = (torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
                                       device=device) if rounds > 0 else None)
         self.lse = (torch.empty((H, Np), dtype=torch.float32, device=device)

@@ -15,11 +15,18 @@
  *
  * Conventions shared by every call
  * --------------------------------
+ *  - Blocks: queries are grouped in blocks of B tokens, keys (and values)
+ *    in blocks of Bk tokens (Bk = 0 means Bk = B). There are n_q = N_pad / B
+ *    query blocks and n_k = ceil(N / Bk) key blocks; the last block of
+ *    either kind may be partial. Square blocks (Bk = B) are the common case;
+ *    ReSS Appendix F uses query blocks of 128 and key blocks of 64.
  *  - Tensor layout: head-major, row-major, contiguous. Token tensors are
- *    [H][N_pad][D]; block tensors [H][n][D]; block maps [H][n][n], where
- *    n = N_pad / B and tokens t >= N are padding (ignored as keys, written
- *    as zero rows of the attention output).
- *  - D must be 64; B must be 64 or 128; n must be <= 4096.
+ *    [H][N_pad][D]; pooled query blocks [H][n_q][D], pooled key and value
+ *    blocks [H][n_k][D]; block maps [H][n_q][n_k] (row i: query block i,
+ *    column j: key block j). Tokens t >= N are padding (ignored as keys,
+ *    written as zero rows of the attention output).
+ *  - D must be 64; B must be 64 or 128; Bk must be 0, 64 or 128 and at most
+ *    B; n_q and n_k must be <= 4096.
  *  - Pointers named "device" are caller-owned device memory on the current
  *    HIP device, 16-byte aligned, and must not alias one another. Arrays
  *    named "host" are read on the host during the call and not retained.
@@ -43,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RESS_VERSION 1
+#define RESS_VERSION 2
 
 /* Status codes. */
 #define RESS_OK 0
@@ -59,7 +66,7 @@ extern "C" {
 #define RESS_SCORE_PROB 0  /* pooled attention probability             */
 #define RESS_SCORE_DRIFT 1 /* ReSS drift key, Eq. 7 of the ReSS page   */
 
-/* Largest supported number of blocks per row (n). */
+/* Largest supported number of query blocks or key blocks (n_q, n_k). */
 #define RESS_MAX_BLOCKS 4096
 /* Largest number of heads accepted by the selection calls, whose per-head
  * budgets travel in the kernel arguments. */
@@ -70,7 +77,8 @@ typedef struct ress_shape {
   int32_t N;     /* valid tokens, 1 <= N <= N_pad             */
   int32_t N_pad; /* padded length, a multiple of B, N_pad-N<B */
   int32_t D;     /* head dimension, must be 64                */
-  int32_t B;     /* block size (query and key), 64 or 128     */
+  int32_t B;     /* query block size, 64 or 128               */
+  int32_t Bk;    /* key block size: 0 (= B), or 64 / 128 <= B */
 } ress_shape;
 
 /*
@@ -78,9 +86,10 @@ typedef struct ress_shape {
  *
  *   xpool[h][b][:] = mean of x[h][t][:] over the valid tokens t < N of block b
  *
- * q, k, v: device [H][N_pad][D] of `dtype`. Each of the three (input,
- * output) pairs is either both non-NULL or both NULL; at least one pair is
- * given. qpool, kpool, vpool: device float64 [H][n][D]. Accumulation is in
+ * with blocks of B tokens for q and of Bk tokens for k and v. q, k, v:
+ * device [H][N_pad][D] of `dtype`. Each of the three (input, output) pairs
+ * is either both non-NULL or both NULL; at least one pair is given. qpool:
+ * device float64 [H][n_q][D]; kpool, vpool: [H][n_k][D]. Accumulation is in
  * float64.
  */
 int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
@@ -104,8 +113,9 @@ int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
  *   with M_h = I when M is NULL, else M: device float64 [H][D][D], symmetric
  *   (a Gram matrix W_O^T W_O, Eq. 8). vpool, key, vout, vmv are required.
  *
- * qpool, kpool, vpool: device float64 [H][n][D]. P, key: device float64
- * [H][n][n]. vout: device float64 [H][n][D]. vmv: device float64 [H][n].
+ * qpool: device float64 [H][n_q][D]; kpool, vpool: [H][n_k][D]. P, key:
+ * device float64 [H][n_q][n_k]. vout: device float64 [H][n_q][D]. vmv:
+ * device float64 [H][n_k].
  * scale > 0 (1/sqrt(D) is the usual value); eps > 0 (1e-4 on the page).
  */
 int ress_block_score(const double* qpool, const double* kpool,
@@ -124,10 +134,11 @@ int ress_block_score(const double* qpool, const double* kpool,
  * ascending order and the rest of the row (up to k_max) is set to -1;
  * kept_cnt[h][i] = keep[h].
  *
- * key: device float64 [H][n][n]. keep: HOST int32 [H], each
- * 2 <= keep[h] <= n and keep[h] > |always|. always_keep: HOST uint8 [n] or
- * NULL (no always-kept blocks). k_max >= max_h keep[h]. kept_idx: device
- * int32 [H][n][k_max]. kept_cnt: device int32 [H][n]. H <= 64.
+ * key: device float64 [H][n_q][n_k]. keep: HOST int32 [H], each
+ * 2 <= keep[h] <= n_k and keep[h] > |always|. always_keep: HOST uint8 [n_k]
+ * (one flag per key block) or NULL (no always-kept blocks).
+ * max_h keep[h] <= k_max <= n_k. kept_idx: device int32 [H][n_q][k_max].
+ * kept_cnt: device int32 [H][n_q]. H <= 64.
  */
 int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
                      const uint8_t* always_keep, int32_t k_max,
@@ -153,7 +164,8 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
  * tau >= 1 (or above the row's total mass) keeps c_h candidates, the top-k
  * rule on P.
  *
- * P: device float64 [H][n][n] (ress_block_score's map). tau: finite, > 0.
+ * P: device float64 [H][n_q][n_k] (ress_block_score's map). tau: finite,
+ * > 0.
  * keep, always_keep, k_max, kept_idx, kept_cnt: as for ress_select_topk.
  * Uses cap * 20 bytes of LDS per workgroup, cap = max_h c_h.
  */
@@ -179,12 +191,13 @@ int ress_select_cdf(const double* P, ress_shape shape, const int32_t* keep,
  * (strictly smaller replaces) is written back to kept_idx / kept_cnt in the
  * same format as the top-k call.
  *
- * P, key: device float64 [H][n][n] (key = the drift key of ress_block_score
- * with the same eps and M). vpool, vout: device float64 [H][n][D] as written
- * by ress_block_score in drift mode. M: device float64 [H][D][D] or NULL
+ * P, key: device float64 [H][n_q][n_k] (key = the drift key of
+ * ress_block_score with the same eps and M). vpool: device float64
+ * [H][n_k][D] and vout: [H][n_q][D], as written by ress_block_score in drift
+ * mode. M: device float64 [H][D][D] or NULL
  * (= I). keep, always_keep: HOST, as for ress_select_topk. rounds >= 0,
  * 0 < rho <= 1, eps > 0. kept_idx, kept_cnt: device, in/out. J_init,
- * J_final: device float64 [H][n] or NULL. H <= 64. workspace: device,
+ * J_final: device float64 [H][n_q] or NULL. H <= 64. workspace: device,
  * workspace_bytes >= ress_refine_workspace_size(shape), 256-byte aligned;
  * calls that share one workspace must not overlap. The rounds run as
  * kernels on `stream` (an init kernel, then a gains and a selection kernel
@@ -201,7 +214,7 @@ int ress_refine_dropset(const double* P, const double* key,
 /*
  * ress_refine_workspace_size — bytes of device workspace that
  * ress_refine_dropset needs for `shape`: the refinement state of every
- * (head, query-block) row, about 10 n^2 H + 1100 n H bytes (the gains, the
+ * (head, query-block) row, about 10 n_q n_k H + 1100 n_q H bytes (the gains, the
  * current and best drop sets, g and M g per row). 0 for an invalid shape
  * (ress_last_error says why). The caller allocates it (256-byte aligned, as
  * hipMalloc returns) and may reuse it across calls on one stream; its
@@ -222,9 +235,11 @@ size_t ress_refine_workspace_size(ress_shape shape);
  * accumulation and a float32 online softmax; float32 inputs are rounded to
  * bf16 (nearest-even) when staged. Rows t >= N are written as zeros.
  *
- * q, k, v: device [H][N_pad][D] of `dtype`. kept_idx: device int32
- * [H][n][k_max] or NULL (dense); entries outside [0, n) are skipped.
- * kept_cnt: device int32 [H][n], required with kept_idx (values are clamped
+ * Query block i holds tokens i*B .. i*B+B-1 and key block j tokens
+ * j*Bk .. j*Bk+Bk-1. q, k, v: device [H][N_pad][D] of `dtype`. kept_idx:
+ * device int32 [H][n_q][k_max] or NULL (dense: all n_k key blocks); entries
+ * outside [0, n_k) are skipped. kept_cnt: device int32 [H][n_q], required
+ * with kept_idx (values are clamped
  * to [0, k_max]; a row with nothing kept is written as zeros). out: device
  * [H][N_pad][D] of `dtype`. lse: device float32 [H][N_pad] or NULL; it
  * receives log sum_u exp(scale q . k_u) (natural log; -inf for an empty

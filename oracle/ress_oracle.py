@@ -56,11 +56,12 @@ def block_pool(x: np.ndarray, N: int, B: int) -> np.ndarray:
     """Mean of the valid tokens of every block.
 
     x: float64 [H][N_pad][D]; tokens t >= N are padding and are ignored.
-    Returns float64 [H][n][D], n = N_pad / B.  (ReSS page, §3: "mean pooling
-    within each block".)
+    Returns float64 [H][n][D] with n = ceil(N / B) blocks of B tokens, the
+    last one possibly partial.  (ReSS page, §3: "mean pooling within each
+    block".)
     """
     H, N_pad, D = x.shape
-    n = N_pad // B
+    n = -(-N // B)
     out = np.empty((H, n, D), dtype=np.float64)
     for b in range(n):
         lo, hi = b * B, min((b + 1) * B, N)
@@ -103,13 +104,14 @@ def drift_key(P: np.ndarray, vpool: np.ndarray, M: Optional[np.ndarray],
     key is s_ij / max(1 - P_ij, eps) (Eq. 7). q is clamped at 0 against
     rounding. Returns (key, vout, q), all float64.
     """
-    H, n, D = vpool.shape
+    H, nq, nk = P.shape
+    D = vpool.shape[-1]
     vout = pooled_output(P, vpool)
-    q = np.empty((H, n, n), dtype=np.float64)
+    q = np.empty((H, nq, nk), dtype=np.float64)
     for h in range(H):
         Mh = _gram(M, h, D)
-        for i0 in range(0, n, row_chunk):
-            i1 = min(n, i0 + row_chunk)
+        for i0 in range(0, nq, row_chunk):
+            i1 = min(nq, i0 + row_chunk)
             e = vout[h, i0:i1, None, :] - vpool[h, None, :, :]  # [ci][n][D]
             Me = e if M is None else np.matmul(e, Mh)          # M_h = I: e itself
             q[h, i0:i1] = np.sum(Me * e, axis=-1)
@@ -353,14 +355,15 @@ def refine_dropset(P, vpool, vout, M, keep, always, kept, rounds, rho,
     """Refine every (or the listed) rows. Returns (kept', J_init, J_final,
     margin); kept' is a copy of ``kept`` with the refined rows replaced, and
     the per-row arrays are NaN for rows not refined."""
-    H, n, D = vpool.shape
+    H, nq, nk = P.shape
+    D = vpool.shape[-1]
     cand = always == 0
     n_alw = int((always != 0).sum())
     out = kept.copy()
-    J0 = np.full((H, n), np.nan)
-    J1 = np.full((H, n), np.nan)
-    mg = np.full((H, n), np.nan)
-    todo = rows if rows is not None else [(h, i) for h in range(H) for i in range(n)]
+    J0 = np.full((H, nq), np.nan)
+    J1 = np.full((H, nq), np.nan)
+    mg = np.full((H, nq), np.nan)
+    todo = rows if rows is not None else [(h, i) for h in range(H) for i in range(nq)]
     for h, i in todo:
         Mh = _gram(M, h, D)
         c = int(keep[h]) - n_alw
@@ -376,16 +379,19 @@ def refine_dropset(P, vpool, vout, M, keep, always, kept, rounds, rho,
 # ---------------------------------------------------------------------------
 
 def masked_attention(q, k, v, kept, N: int, B: int, scale: float,
-                     blocks=None):
+                     blocks=None, Bk: Optional[int] = None):
     """O[h, t] = sum_u softmax_u(scale q_t . k_u) v_u over the valid keys u < N
     of the blocks kept for t's query block; softmax renormalised among them
     (ReSS page §3: the unselected blocks take no part in the softmax).
 
-    q, k, v: float64 [H][N_pad][D]; kept: bool [H][n][n]. Padded query rows
-    are 0. ``blocks``: optional list of (h, i) query blocks to compute (the
-    rest stay 0). Returns (O float64 [H][N_pad][D], lse float64 [H][N_pad]).
+    q, k, v: float64 [H][N_pad][D]; query block i holds tokens i*B ..
+    i*B + B - 1 and key block j tokens j*Bk .. j*Bk + Bk - 1 (Bk = B when not
+    given); kept: bool [H][n_q][n_k]. Padded query rows are 0. ``blocks``:
+    optional list of (h, i) query blocks to compute (the rest stay 0).
+    Returns (O float64 [H][N_pad][D], lse float64 [H][N_pad]).
     """
     H, N_pad, D = q.shape
+    Bk = B if Bk is None else Bk
     n = N_pad // B
     O = np.zeros((H, N_pad, D), dtype=np.float64)
     lse = np.full((H, N_pad), np.nan)
@@ -394,7 +400,7 @@ def masked_attention(q, k, v, kept, N: int, B: int, scale: float,
         r0, r1 = i * B, min((i + 1) * B, N)
         if r1 <= r0:
             continue
-        keys = np.concatenate([np.arange(j * B, min((j + 1) * B, N))
+        keys = np.concatenate([np.arange(j * Bk, min((j + 1) * Bk, N))
                                for j in np.nonzero(kept[h, i])[0]])
         s = scale * (q[h, r0:r1] @ k[h, keys].T)
         m = s.max(axis=1, keepdims=True)
@@ -405,12 +411,13 @@ def masked_attention(q, k, v, kept, N: int, B: int, scale: float,
     return O, lse
 
 
-def dense_attention(q, k, v, N: int, B: int, scale: float, blocks=None):
+def dense_attention(q, k, v, N: int, B: int, scale: float, blocks=None,
+                    Bk: Optional[int] = None):
     """Dense softmax attention over all valid keys: every block kept."""
     H, N_pad, _ = q.shape
-    n = N_pad // B
-    kept = np.ones((H, n, n), dtype=bool)
-    return masked_attention(q, k, v, kept, N, B, scale, blocks)
+    Bk = B if Bk is None else Bk
+    kept = np.ones((H, N_pad // B, -(-N // Bk)), dtype=bool)
+    return masked_attention(q, k, v, kept, N, B, scale, blocks, Bk)
 
 
 # ---------------------------------------------------------------------------
@@ -418,8 +425,9 @@ def dense_attention(q, k, v, N: int, B: int, scale: float, blocks=None):
 # ---------------------------------------------------------------------------
 
 def run_selection(q, k, v, N, B, keep, always, mode, rounds=0, rho=0.5,
-                  M=None, eps=1e-4, scale=None):
-    """pool -> map -> key -> top-k (-> refine) on float64 inputs.
+                  M=None, eps=1e-4, scale=None, Bk=None):
+    """pool -> map -> key -> top-k (-> refine) on float64 inputs; queries in
+    blocks of B tokens, keys and values in blocks of Bk (default B).
 
     Returns a dict with qpool, kpool, vpool, P, key, vout (drift only),
     kept (after top-k), topk_margin, and when rounds > 0: kept_refined,
@@ -429,11 +437,12 @@ def run_selection(q, k, v, N, B, keep, always, mode, rounds=0, rho=0.5,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = {}
+    Bk = B if Bk is None else Bk
     out["qpool"] = block_pool(q, N, B)
-    out["kpool"] = block_pool(k, N, B)
+    out["kpool"] = block_pool(k, N, Bk)
     out["P"] = block_map(out["qpool"], out["kpool"], scale)
     if mode == "drift" or rounds > 0:
-        out["vpool"] = block_pool(v, N, B)
+        out["vpool"] = block_pool(v, N, Bk)
     if mode == "drift":
         key, vout, qd = drift_key(out["P"], out["vpool"], M, eps)
         out["key"], out["vout"], out["q"] = key, vout, qd

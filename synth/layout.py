@@ -42,18 +42,18 @@ def token_views(w: Workload):
 
 
 def always_keep_blocks(w: Workload) -> np.ndarray:
-    """uint8 flags [n]: 1 where the key block holds a special token."""
-    flags = np.zeros(w.n_blocks, dtype=np.uint8)
+    """uint8 flags [n_k]: 1 where the key block holds a special token."""
+    flags = np.zeros(w.n_kblocks, dtype=np.uint8)
     if w.specials_per_view:
         first = w.views * w.patches_per_view
         last = w.N - 1
-        flags[first // w.block: last // w.block + 1] = 1
+        flags[first // w.kblock: last // w.kblock + 1] = 1
     return flags
 
 
 def keep_budgets(w: Workload) -> np.ndarray:
     """int32 [H]: total kept key blocks per query-block row, per head."""
-    n = w.n_blocks
+    n = w.n_kblocks
     k = []
     for h in range(w.heads):
         s = w.head_sparsity(h)

@@ -1,4 +1,4 @@
-"""The five synthetic workloads of block-sparse global attention.
+"""The synthetic workloads of block-sparse global attention.
 
 Each workload is one global-attention call of a VGGT-style multi-view
 transformer: the tokens of all views are concatenated into one bidirectional
@@ -33,6 +33,9 @@ class Workload:
     rounds: int  # drop-set refinement rounds (0 = none)
     rho: float  # total swap fraction of the keep budget
     generator: str  # "shared_vector" or "low_rank"
+    # Key block size (0: the same as `block`, square blocks). ReSS Appendix F
+    # uses query blocks of 128 and key blocks of 64.
+    key_block: int = 0
     seed: int = 0
     notes: str = field(default="", compare=False)
 
@@ -52,7 +55,17 @@ class Workload:
 
     @property
     def n_blocks(self) -> int:
+        """Query blocks (rows of the block maps)."""
         return self.N_pad // self.block
+
+    @property
+    def kblock(self) -> int:
+        return self.key_block if self.key_block else self.block
+
+    @property
+    def n_kblocks(self) -> int:
+        """Key blocks (columns of the block maps); the last one may be partial."""
+        return -(-self.N // self.kblock)
 
     def head_sparsity(self, h: int) -> float:
         s0, s1 = self.sparsity
@@ -63,6 +76,10 @@ class Workload:
     def dense_flop(self) -> float:
         """4*D*N_pad^2*H: QK^T and PV over every block pair."""
         return 4.0 * self.head_dim * self.N_pad * self.N_pad * self.heads
+
+    def shape_args(self):
+        """(H, N, N_pad, D, B, Bk) of the library's shape."""
+        return (self.heads, self.N, self.N_pad, self.head_dim, self.block, self.key_block)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -101,6 +118,22 @@ WORKLOADS: Dict[str, Workload] = {
             notes="100 views, drift score + 3 refinement rounds",
         ),
         Workload(
+            name="views8-k64",
+            views=8, patches_per_view=1369, specials_per_view=5,
+            heads=16, head_dim=64, block=128, dtype="bf16",
+            sparsity=(0.5, 0.5), score="drift", rounds=2, rho=0.5,
+            generator="low_rank", key_block=64,
+            notes="8 views on ReSS Appendix F's grid: query blocks 128, key blocks 64",
+        ),
+        Workload(
+            name="views100-k64",
+            views=100, patches_per_view=1369, specials_per_view=5,
+            heads=16, head_dim=64, block=128, dtype="bf16",
+            sparsity=(0.9, 0.9), score="drift", rounds=3, rho=0.5,
+            generator="low_rank", key_block=64,
+            notes="100 views, drift + 3 rounds, query blocks 128, key blocks 64",
+        ),
+        Workload(
             name="views200",
             views=200, patches_per_view=1369, specials_per_view=5,
             heads=16, head_dim=64, block=128, dtype="bf16",
@@ -112,7 +145,7 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 # The workloads in the order small -> large.
-ORDER = ["tiny", "views8", "views32", "views100", "views200"]
+ORDER = ["tiny", "views8", "views32", "views100", "views200", "views8-k64", "views100-k64"]
 
 
 def get_workload(name: str) -> Workload:
@@ -137,6 +170,7 @@ def _check():
     for w in WORKLOADS.values():
         assert w.N_pad % w.block == 0
         assert 0 <= w.N_pad - w.N < w.block
+        assert w.kblock <= w.block and w.block % w.kblock == 0
         assert math.isfinite(w.dense_flop())
 
 

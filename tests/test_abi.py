@@ -31,13 +31,13 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(b.LIB_PATH)
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in ress.h but not exported"
-    assert b.ress_version() == 1
+    assert b.ress_version() == 2
     assert set(b.ENTRY_POINTS) == set(declared_functions())
 
 
-def _shape(H=2, N=256, N_pad=256, D=64, B=64):
+def _shape(H=2, N=256, N_pad=256, D=64, B=64, Bk=0):
     import block_sparse_global_amd as b
-    return b.Shape(H, N, N_pad, D, B).c()
+    return b.Shape(H, N, N_pad, D, B, Bk).c()
 
 
 FAKE = ctypes.c_void_p(0x1000)        # 16-byte aligned, never dereferenced
@@ -52,6 +52,9 @@ MISALIGNED = ctypes.c_void_p(0x1008)
     (dict(N=100), -1, "N="),
     (dict(N=300), -1, "N="),
     (dict(N=4097 * 64, N_pad=4097 * 64), -2, "cap"),
+    (dict(Bk=32), -2, "key block"),
+    (dict(Bk=128), -2, "key block"),             # larger than B = 64
+    (dict(B=128, Bk=64, N=4096 * 64 + 1, N_pad=4096 * 64 + 128), -2, "cap"),  # n_k = 4097
 ])
 def test_attention_rejects_bad_shapes(shape, code, msg):
     import block_sparse_global_amd as b

@@ -59,7 +59,7 @@ def _lib():
 def run_gpu(w, x, mode, M=None, stream=None, blocks_out=True):
     """The whole step on the GPU; every intermediate copied to the host."""
     b = _lib()
-    shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+    shape = b.Shape(*w.shape_args())
     rounds = w.rounds if mode == "drift" else 0
     Mt = torch.from_numpy(M).cuda() if M is not None else None
     layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
@@ -93,7 +93,8 @@ def run_gpu(w, x, mode, M=None, stream=None, blocks_out=True):
 
 
 CASES = [("tiny", "prob"), ("views8", "prob"), ("views32", "drift"),
-         ("views100", "drift"), ("views200", "prob"), ("views200", "drift")]
+         ("views100", "drift"), ("views200", "prob"), ("views200", "drift"),
+         ("views8-k64", "drift"), ("views100-k64", "drift")]
 
 
 @pytest.fixture(scope="module", params=CASES, ids=[f"{a}-{b}" for a, b in CASES])
@@ -103,13 +104,13 @@ def case(request):
     w, x = case_inputs(name)
     g = run_gpu(w, x, mode)
     qf, kf = f64(x["q"], w), f64(x["k"], w)
-    N, B = w.N, w.block
-    ref = {"qpool": oracle.block_pool(qf, N, B), "kpool": oracle.block_pool(kf, N, B)}
+    N, B, Bk = w.N, w.block, w.kblock
+    ref = {"qpool": oracle.block_pool(qf, N, B), "kpool": oracle.block_pool(kf, N, Bk)}
     del qf, kf
     scale = 1.0 / math.sqrt(w.head_dim)
     ref["P"] = oracle.block_map(ref["qpool"], ref["kpool"], scale)
     if mode == "drift":
-        ref["vpool"] = oracle.block_pool(f64(x["v"], w), N, B)
+        ref["vpool"] = oracle.block_pool(f64(x["v"], w), N, Bk)
         ref["key"], ref["vout"], _ = oracle.drift_key(ref["P"], ref["vpool"], None, 1e-4)
     else:
         ref["key"] = ref["P"]
@@ -151,7 +152,7 @@ def test_drift_key(case):
 
 def test_topk(case):
     name, mode, w, x, g, ref = case
-    n = w.n_blocks
+    n = w.n_kblocks
     check_lists_wellformed(g["topk_idx"], g["topk_cnt"], x["keep"], x["always"], n)
     gm = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
     nd = compare_masks(gm, ref["kept"], ref["key"], x["always"], x["keep"])
@@ -164,21 +165,22 @@ def test_select_cdf(case, tau):
     ranks and sums the same float64 values in the same order, so the keep
     sets must be identical (no near-tie allowance)."""
     name, mode, w, x, g, ref = case
-    if mode != "prob" and name != "views100":
-        pytest.skip("one drift workload covers the always-kept layout of 5 blocks")
+    if mode != "prob" and name not in ("views100", "views8-k64"):
+        pytest.skip("views100 covers the always-kept layout of 5 blocks, views8-k64 "
+                    "the 128 x 64 grid")
     b = _lib()
-    H, n = w.heads, w.n_blocks
-    shape = b.Shape(H, w.N, w.N_pad, w.head_dim, w.block)
+    H, nq, n = w.heads, w.n_blocks, w.n_kblocks
+    shape = b.Shape(*w.shape_args())
     keep = x["keep"]
     k_max = int(np.max(keep))
     P = torch.from_numpy(ref["P"]).cuda()
-    idx = torch.full((H, n, k_max), 7, dtype=torch.int32, device="cuda")
-    cnt = torch.full((H, n), -5, dtype=torch.int32, device="cuda")
+    idx = torch.full((H, nq, k_max), 7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((H, nq), -5, dtype=torch.int32, device="cuda")
     b.ress_select_cdf(P, shape, keep, x["always"], tau, k_max, idx, cnt)
     torch.cuda.synchronize()
     gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
-    rows = ([(h, i) for h in range(H) for i in range(n)] if H * n <= 6000
-            else sample_blocks(H, n, 3000, seed=7))
+    rows = ([(h, i) for h in range(H) for i in range(nq)] if H * nq <= 6000
+            else sample_blocks(H, nq, 3000, seed=7))
     kept, taken, _ = oracle.select_cdf(ref["P"], keep, x["always"], tau, rows=rows)
     alw = np.nonzero(x["always"])[0] if x["always"] is not None else np.array([], int)
     for h, i in rows:
@@ -202,10 +204,10 @@ def test_refine(case):
     name, mode, w, x, g, ref = case
     if mode != "drift" or w.rounds == 0:
         pytest.skip("no refinement rounds in this workload")
-    n = w.n_blocks
+    n = w.n_kblocks
     check_lists_wellformed(g["idx"], g["cnt"], x["keep"], x["always"], n)
     start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
-    rows = [(h, i) for h, i in sample_blocks(w.heads, n, 512, seed=3)]
+    rows = [(h, i) for h, i in sample_blocks(w.heads, w.n_blocks, 512, seed=3)]
     kr, J0, J1, mg = oracle.refine_dropset(ref["P"], ref["vpool"], ref["vout"], None,
                                            x["keep"], x["always"], start, w.rounds, w.rho,
                                            rows=rows)
@@ -233,12 +235,12 @@ def test_refine(case):
 def test_attention(case):
     name, mode, w, x, g, ref = case
     n, B, N = w.n_blocks, w.block, w.N
-    kept = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    kept = kept_mask_from_lists(g["idx"], g["cnt"], w.n_kblocks)
     count = w.heads * n if w.heads * n <= 64 else 48
     blocks = sample_blocks(w.heads, n, count, seed=5)
     qf, kf, vf = (f64(x[t], w) for t in ("q", "k", "v"))
     O, lse = oracle.masked_attention(qf, kf, vf, kept, N, B, 1.0 / math.sqrt(w.head_dim),
-                                     blocks=blocks)
+                                     blocks=blocks, Bk=w.kblock)
     got, want, gl, wl = [], [], [], []
     for h, i in blocks:
         r0, r1 = i * B, min((i + 1) * B, N)
@@ -268,15 +270,18 @@ def _small(**kw):
 def test_dense_mode_matches_dense_oracle():
     b = _lib()
     for w, x in (case_inputs("tiny"), _small(name="d", views=3, patches_per_view=300,
-                                              specials_per_view=5, heads=3, block=128)):
-        shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
+                                              specials_per_view=5, heads=3, block=128),
+                 # 128-row query blocks over 64-key blocks, the last one partial
+                 _small(name="d64", views=3, patches_per_view=300, specials_per_view=5,
+                        heads=3, block=128, key_block=64)):
+        shape = b.Shape(*w.shape_args())
         q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
         out = torch.empty_like(q)
         lse = torch.empty((w.heads, w.N_pad), dtype=torch.float32, device="cuda")
         b.dense_attention(q, k, v, shape, out, lse=lse)
         torch.cuda.synchronize()
         O, L = oracle.dense_attention(*(f64(x[t], w) for t in ("q", "k", "v")), w.N, w.block,
-                                      1.0 / math.sqrt(w.head_dim))
+                                      1.0 / math.sqrt(w.head_dim), Bk=w.kblock)
         got = out.float().cpu().numpy()
         mx, mean, _ = attn_errors(got[:, : w.N], O[:, : w.N])
         assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
@@ -285,23 +290,25 @@ def test_dense_mode_matches_dense_oracle():
         assert np.allclose(lse.cpu().numpy()[:, : w.N], L[:, : w.N], atol=lse_tol, rtol=0)
 
 
-def test_single_kept_block_is_restricted_softmax():
+@pytest.mark.parametrize("block,key_block", [(64, 0), (128, 64)])
+def test_single_kept_block_is_restricted_softmax(block, key_block):
     b = _lib()
     w, x = _small(name="s", views=2, patches_per_view=250, specials_per_view=0, heads=2,
-                  block=64)
-    shape = b.Shape(w.heads, w.N, w.N_pad, w.head_dim, w.block)
-    n = w.n_blocks
+                  block=block, key_block=key_block)
+    shape = b.Shape(*w.shape_args())
+    n, nk = w.n_blocks, w.n_kblocks
     rng = np.random.default_rng(7)
-    idx = rng.integers(0, n, size=(w.heads, n, 1)).astype(np.int32)
+    idx = rng.integers(0, nk, size=(w.heads, n, 1)).astype(np.int32)
+    idx[0, 0, 0] = nk - 1                   # the partial last key block
     cnt = np.ones((w.heads, n), np.int32)
     q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
     out = torch.empty_like(q)
     b.ress_sparse_attn_fwd(q, k, v, shape, torch.from_numpy(idx).cuda(),
                            torch.from_numpy(cnt).cuda(), 1, 0.125, out)
     torch.cuda.synchronize()
-    kept = kept_mask_from_lists(idx, cnt, n)
+    kept = kept_mask_from_lists(idx, cnt, nk)
     O, _ = oracle.masked_attention(*(f64(x[t], w) for t in ("q", "k", "v")), kept, w.N,
-                                   w.block, 0.125)
+                                   w.block, 0.125, Bk=w.kblock)
     mx, mean, _ = attn_errors(out.float().cpu().numpy()[:, : w.N], O[:, : w.N])
     assert mx <= MAX_ABS and mean <= MEAN_ABS
 

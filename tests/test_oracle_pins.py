@@ -111,24 +111,28 @@ def test_map_single_block_and_orthogonal_cases():
 # Drift key (ReSS page Eq. 3-9)
 # ---------------------------------------------------------------------------
 
-def _random_map(seed, H, n, D):
+def _random_map(seed, H, n, D, nk=None):
     r = rng(seed)
-    P = oracle.block_map(r.standard_normal((H, n, D)), r.standard_normal((H, n, D)), 0.7)
-    V = r.standard_normal((H, n, D))
+    nk = n if nk is None else nk
+    P = oracle.block_map(r.standard_normal((H, n, D)), r.standard_normal((H, nk, D)), 0.7)
+    V = r.standard_normal((H, nk, D))
     return P, V
 
 
-def test_drift_key_equals_explicit_single_block_masking():
+@pytest.mark.parametrize("nk", [9, 14])   # square, and more key blocks than rows
+def test_drift_key_equals_explicit_single_block_masking(nk):
     # Eq. 3-4: deleting block j and renormalising moves the pooled output by
     # vtilde_ij - vout_i; Eq. 7's key is that move's M-norm.
     H, n, D = 2, 9, 6
-    P, V = _random_map(7, H, n, D)
+    P, V = _random_map(7, H, n, D, nk)
+    assert P.shape == (H, n, nk)
     for M in (None, np.stack([np.diag(rng(8).uniform(0.2, 3, D)) for _ in range(H)])):
         key, vout, _ = oracle.drift_key(P, V, M, eps=1e-4)
+        assert key.shape == (H, n, nk) and vout.shape == (H, n, D)
         for h in range(H):
             Mh = np.eye(D) if M is None else M[h]
             for i in range(n):
-                for j in range(n):
+                for j in range(nk):
                     w = P[h, i].copy(); w[j] = 0.0
                     vt = (w[:, None] * V[h]).sum(0) / w.sum()
                     dv = vt - (P[h, i][:, None] * V[h]).sum(0)
@@ -429,6 +433,21 @@ def test_refine_invariants_and_brute_force_bound():
           f"mean gap closed {np.mean(closed):.3f}")
 
 
+def test_refine_on_a_rectangular_map():
+    # more key blocks than query-block rows (the 128 x 64 grid): every row
+    # still keeps c candidates and never ends above its starting objective
+    H, nq, nk, D = 1, 5, 12, 4
+    P, V = _random_map(43, H, nq, D, nk)
+    vout = oracle.pooled_output(P, V)
+    always = np.zeros(nk, np.uint8); always[11] = 1
+    keep = np.array([6])
+    kept, _ = oracle.select_topk(P, keep, always)
+    kr, J0, J1, _ = oracle.refine_dropset(P, V, vout, None, keep, always, kept, 3, 0.5)
+    assert kr.shape == (H, nq, nk) and J0.shape == (H, nq)
+    assert np.all(kr.sum(-1) == 6) and np.all(kr[..., 11])
+    assert np.all(J1 <= J0)
+
+
 def test_refine_zero_rounds_is_identity():
     P, V = _random_map(300, 2, 8, 4)
     always = np.zeros(8, np.uint8); always[7] = 1
@@ -456,6 +475,37 @@ def _sdpa(q, k, v, scale):
     return torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
         scale=scale)[0].numpy()
+
+
+def test_key_blocks_of_half_size_pool_and_attend_like_the_square_grid():
+    # ReSS Appendix F's grid: query blocks of 128, key blocks of 64. A 128-key
+    # block is the union of two 64-key blocks: its mean is their mean, and
+    # keeping both halves attends exactly like keeping the whole block.
+    r = rng(41)
+    H, D, N, N_pad = 2, 8, 4 * 128 - 70, 4 * 128      # partial last blocks
+    q, k, v = (r.standard_normal((H, N_pad, D)) for _ in range(3))
+    k64, k128 = oracle.block_pool(k, N, 64), oracle.block_pool(k, N, 128)
+    assert k64.shape == (H, 7, D) and k128.shape == (H, 4, D)     # ceil(442 / 64) = 7
+    assert np.allclose((k64[:, 0:6:2] + k64[:, 1:6:2]) / 2, k128[:, :3], rtol=0, atol=1e-15)
+    assert np.allclose(k64[:, 6], k[:, 384:N].mean(axis=1), rtol=0, atol=1e-15)
+    kept128 = r.uniform(size=(H, 4, 4)) < 0.5
+    kept128[:, :, 0] = True
+    kept64 = np.repeat(kept128, 2, axis=2)[:, :, :7]
+    O1, L1 = oracle.masked_attention(q, k, v, kept128, N, 128, 0.3)
+    O2, L2 = oracle.masked_attention(q, k, v, kept64, N, 128, 0.3, Bk=64)
+    assert np.allclose(O1, O2, rtol=0, atol=1e-13)
+    # all 64-key blocks kept: dense attention by torch on the valid keys
+    Od, _ = oracle.dense_attention(q, k, v, N, 128, 0.3, Bk=64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[:, :N]), torch.from_numpy(k[:, :N]), torch.from_numpy(v[:, :N]),
+        scale=0.3).numpy()
+    assert np.allclose(Od[:, :N], ref, rtol=0, atol=1e-12)
+    # one 64-key block kept: the softmax restricted to its 64 keys
+    one = np.zeros((H, 4, 7), dtype=bool); one[:, :, 3] = True
+    O3, _ = oracle.masked_attention(q, k, v, one, N, 128, 0.3, Bk=64)
+    s = 0.3 * q[0, :128] @ k[0, 192:256].T
+    w = np.exp(s - s.max(1, keepdims=True)); w /= w.sum(1, keepdims=True)
+    assert np.allclose(O3[0, :128], w @ v[0, 192:256], rtol=0, atol=1e-13)
 
 
 def test_attention_zero_sparsity_equals_dense_sdpa():

@@ -44,6 +44,16 @@ def test_layout_and_budgets(name, n, always, keep):
     assert list(synth.keep_budgets(w)) == keep
 
 
+def test_key_blocks_of_64_under_query_blocks_of_128():
+    w = synth.get_workload("views100-k64")
+    assert (w.block, w.kblock) == (128, 64)
+    assert w.n_blocks == 1074 and w.n_kblocks == 2147      # ceil(137400 / 64)
+    assert w.n_kblocks * 64 <= w.N_pad
+    assert list(np.nonzero(synth.always_keep_blocks(w))[0]) == list(range(2139, 2147))
+    assert list(synth.keep_budgets(w)) == [215] * 16       # floor(0.1 * 2147 + 0.5)
+    assert w.shape_args() == (16, 137400, 137472, 64, 128, 64)
+
+
 def test_views200_per_head_budgets():
     w = synth.get_workload("views200")
     k = synth.keep_budgets(w)
@@ -60,7 +70,7 @@ def test_special_tokens_sit_in_the_always_kept_blocks():
         w = synth.get_workload(name)
         view, special = synth.token_views(w)
         flags = synth.always_keep_blocks(w)
-        blocks_with_special = np.unique(np.nonzero(special)[0] // w.block)
+        blocks_with_special = np.unique(np.nonzero(special)[0] // w.kblock)
         assert list(blocks_with_special) == list(np.nonzero(flags)[0])
         assert special.sum() == 5 * w.views
 
