@@ -6,9 +6,9 @@
 // in a caller-provided workspace in HBM, and each round is two kernels over
 // all rows of all heads:
 //   * gains: for every head, the products V_j . (M g_i) of all key blocks j
-//     and query-block rows i form one n x n x 64 float64 product, computed
-//     as a tiled matrix product (64 x 64 tiles, the dims staged through
-//     LDS); its epilogue turns each product into the exact objective
+//     and query-block rows i form one n_q x n_k x 64 float64 product, computed
+//     on the matrix cores in 64 x 64 tiles (the dims staged through LDS);
+//     its epilogue turns each product into the exact objective
 //     decrease of Eq. 16 for restoring (j in D_i, Eq. 14) or dropping (j
 //     kept, Eq. 15) j, stored as a 64-bit order key;
 //   * select: one wave per row selects the m_r best restores and the m_r
@@ -23,6 +23,7 @@
 // s_j (Eq. 6) comes from the drift key of Eq. 7: s = key * max(1 - P, eps).
 // Every sum has a fixed order, so results are bit-reproducible.
 #include "ress_internal.h"
+#include "tile_f64.h"
 
 namespace ress {
 namespace {
@@ -182,16 +183,18 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
 }
 
 // ---------------------------------------------------------------- gains
-// C[i][j] = u_i . V_j over a 64 x 64 tile (rows i < nq, key blocks j < nk) of one head,
-// the 64 dims staged through LDS in two halves, transposed. Thread (ti, tj)
-// owns rows i0 + ti + 16a and key blocks j0 + tj + 16b (a, b < 4), so that
-// the sixteen lanes of a row group read sixteen consecutive key blocks, in
-// LDS and in the epilogue's loads and stores. Every product is one fma chain
-// over the dims in ascending order. The epilogue issues all its loads first,
-// then forms the gain of each (i, j).
-constexpr int kGT = 64;    // tile edge
-constexpr int kGK = 32;    // dims per LDS stage
-constexpr int kGPad = 66;  // padded row of a transposed stage
+// C[i][j] = u_i . V_j over a 64 x 64 tile (rows i < nq, key blocks j < nk)
+// of one head on the float64 matrix cores (mfma_tile_f64); the epilogue
+// issues all its loads first, then forms the gain of each (i, j).
+__device__ inline void load8d(const double* p, double (&x)[8]) {
+  const double2* src = reinterpret_cast<const double2*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double2 v = src[e];
+    x[2 * e] = v.x;
+    x[2 * e + 1] = v.y;
+  }
+}
 
 __global__ __launch_bounds__(256) void refine_gains_kernel(
     const double* __restrict__ P, const double* __restrict__ key,
@@ -199,102 +202,66 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
     double eps, RefineWs ws) {
   const int h = blockIdx.z;
   if (swaps_of(cfg, h, round, rho) <= 0) return;  // no swaps for this head
-  __shared__ double Ut[kGK][kGPad];
-  __shared__ double Vt[kGK][kGPad];
-  const int tid = threadIdx.x;
-  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
-  const int ti = tid >> 4, tj = tid & 15;
+  __shared__ TileF64Smem sm;
+  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
   const double* Uh = ws.u + (size_t)h * nq * kD;
   const double* Vh = vpool + (size_t)h * nk * kD;
-
-  double acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-
-  // staging: thread t copies row t/4 (clamped to the last row), dims
-  // (t%4)*8 .. +7
-  const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const int ri = min(i0 + lr, nq - 1), rj = min(j0 + lr, nk - 1);
-#pragma unroll
-  for (int kc = 0; kc < kD; kc += kGK) {
-    const double2* us = reinterpret_cast<const double2*>(Uh + (size_t)ri * kD + kc + lc);
-    const double2* vs = reinterpret_cast<const double2*>(Vh + (size_t)rj * kD + kc + lc);
-    double2 xu[4], xv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      xu[e] = us[e];
-      xv[e] = vs[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Ut[lc + 2 * e][lr] = xu[e].x;
-      Ut[lc + 2 * e + 1][lr] = xu[e].y;
-      Vt[lc + 2 * e][lr] = xv[e].x;
-      Vt[lc + 2 * e + 1][lr] = xv[e].y;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < kGK; ++k) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = Ut[k][ti + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Vt[k][tj + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(bv[b], av[a], acc[a][b]);
-    }
-    __syncthreads();
-  }
+  f64x4 acc[2][2];
+  mfma_tile_f64(
+      [&](int r, int d0, double (&x)[8]) { load8d(Uh + (size_t)min(i0 + r, nq - 1) * kD + d0, x); },
+      [&](int r, int d0, double (&x)[8]) { load8d(Vh + (size_t)min(j0 + r, nk - 1) * kD + d0, x); },
+      sm, acc);
 
   // epilogue: the exact objective decrease of each swap (Eq. 13-16). Out
   // of range rows and blocks load from a clamped valid address and are not
-  // stored.
+  // stored. The lane's results cover 8 rows (tr, r) x 2 key blocks (tc),
+  // taken in two passes of 4 rows: all loads of a pass, then its gains.
+  const TileF64Map mp;
   const int fs = flag_stride(nk);
-  double pv[4][4], kv[4][4];
-  uint8_t fv[4][4];
-  double sK[4], sG[4], sJ[4], svu[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const size_t row = (size_t)h * nq + min(i0 + ti + 16 * a, nq - 1);
-    const RowState* st = ws.rs + row;
-    sK[a] = st->K;
-    sG[a] = st->G;
-    sJ[a] = st->J;
-    svu[a] = st->vu;
+  for (int tr = 0; tr < 2; ++tr) {
+    double pv[4][2], kv[4][2];
+    uint8_t fv[4][2];
+    double sK[4], sG[4], sJ[4], svu[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = min(j0 + tj + 16 * b, nk - 1);
-      pv[a][b] = P[row * nk + j];
-      kv[a][b] = key[row * nk + j];
-      fv[a][b] = ws.fcur[row * fs + j];
-    }
-  }
+    for (int r = 0; r < 4; ++r) {
+      const size_t row = (size_t)h * nq + min(i0 + mp.row_of(tr, r), nq - 1);
+      const RowState* st = ws.rs + row;
+      sK[r] = st->K;
+      sG[r] = st->G;
+      sJ[r] = st->J;
+      svu[r] = st->vu;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ti + 16 * a;
-    const size_t row = (size_t)h * nq + i;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tj + 16 * b;
-      const double p = pv[a][b];
-      const double sv = kv[a][b] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
-      const double s2 = sv * sv;
-      const double dMg = p * (svu[a] - acc[a][b]);      // d_j^T M g_i
-      double dJ;
-      if (fv[a][b]) {  // restore (Eq. 13-14), u = +P_j
-        const double dG = -2.0 * dMg + s2;
-        const double Ku = sK[a] + p;
-        dJ = sJ[a] - (sG[a] + dG) / (Ku * Ku);
-      } else {  // drop (Eq. 15), u = -P_j
-        const double dG = 2.0 * dMg + s2;
-        const double Ku = sK[a] - p;
-        dJ = (Ku > 0.0) ? sJ[a] - (sG[a] + dG) / (Ku * Ku) : -INFINITY;
+      for (int tc = 0; tc < 2; ++tc) {
+        const int j = min(j0 + mp.col_of(tc), nk - 1);
+        pv[r][tc] = P[row * nk + j];
+        kv[r][tc] = key[row * nk + j];
+        fv[r][tc] = ws.fcur[row * fs + j];
       }
-      if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + mp.row_of(tr, r);
+      const size_t row = (size_t)h * nq + i;
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int j = j0 + mp.col_of(tc);
+        const double p = pv[r][tc];
+        const double sv = kv[r][tc] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
+        const double s2 = sv * sv;
+        const double dMg = p * (svu[r] - acc[tr][tc][r]);  // d_j^T M g_i
+        double dJ;
+        if (fv[r][tc]) {  // restore (Eq. 13-14), u = +P_j
+          const double dG = -2.0 * dMg + s2;
+          const double Ku = sK[r] + p;
+          dJ = sJ[r] - (sG[r] + dG) / (Ku * Ku);
+        } else {  // drop (Eq. 15), u = -P_j
+          const double dG = 2.0 * dMg + s2;
+          const double Ku = sK[r] - p;
+          dJ = (Ku > 0.0) ? sJ[r] - (sG[r] + dG) / (Ku * Ku) : -INFINITY;
+        }
+        if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
+      }
     }
   }
 }
@@ -592,7 +559,7 @@ hipError_t launch_refine(const double* P, const double* key,
   const int kpl = n <= 17 * 64 ? 17 : (n <= 34 * 64 ? 34 : 0);
   const size_t lds_sel = 1536 + 4 * (size_t)((n + 3) & ~3) + (size_t)((n + 15) & ~15) +
                          (kpl > 0 ? 0 : 8 * (size_t)n);
-  const dim3 tiles((n + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
+  const dim3 tiles((n + kTF - 1) / kTF, (nq + kTF - 1) / kTF, s.H);
   for (int r = 0; r < rounds; ++r) {
     int m_max = 0;
     for (int h = 0; h < s.H; ++h) m_max = max(m_max, swaps_of(cfg, h, r, rho));

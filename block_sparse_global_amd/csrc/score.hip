@@ -9,12 +9,14 @@
 //
 // Maps are [H][n_q][n_k] (query-block rows, key-block columns; the two
 // counts differ when key blocks are smaller than query blocks).
-// The three n_q x n_k x 64 products (logits, vout = P V, (M vout) . V_j) run as
-// tiled matrix products with their elementwise steps in the epilogues; the
-// row softmax is one wave per row. Every output element is one fma chain in
-// ascending index order and every reduction has a fixed order (no
-// atomics), so repeated calls give identical bits.
+// The three n_q x n_k x 64 products (logits, vout = P V, (M vout) . V_j) run
+// as float64 matrix-core products (v_mfma_f64_16x16x4_f64) with their
+// elementwise steps in the epilogues; the row softmax is one wave per row.
+// Every output element is a fixed sequence of fused multiply-adds and every
+// reduction has a fixed order (no atomics), so repeated calls give
+// identical bits.
 #include "ress_internal.h"
+#include "tile_f64.h"
 
 namespace ress {
 namespace {
@@ -34,62 +36,14 @@ __device__ inline double wave_max(double v) {
   return v;
 }
 
-// ---- 64 x 64 tile of A_i . B_j over the 64 dims (A, B row-major [.][64]),
-// the dims staged through LDS in two transposed halves. Thread (ti, tj) owns
-// rows i0 + ti + 16a and columns j0 + tj + 16b (a, b < 4): the sixteen lanes
-// of a row group touch sixteen consecutive columns. acc[a][b] is one fma
-// chain over the dims in ascending order. `stage_a` fills the A half (rows
-// clamped to the last row), so that callers can form A on the fly; B has nb
-// rows.
-constexpr int kGT = 64;    // tile edge
-constexpr int kGK = 32;    // dims per LDS stage
-constexpr int kGPad = 66;  // padded row of a transposed stage
-
-struct TileSmem {
-  double At[kGK][kGPad];
-  double Bt[kGK][kGPad];
-};
-
-template <typename StageA>
-__device__ inline void tile_dot(const double* __restrict__ B, int nb, int j0, StageA stage_a,
-                                TileSmem& sm, double (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tj = tid & 15;
-  const int lr = tid >> 2, lc = (tid & 3) * 8;
-  const int rj = min(j0 + lr, nb - 1);
+// 8 consecutive float64 of a row (two 16-byte loads per pair).
+__device__ inline void load8d(const double* p, double (&x)[8]) {
+  const double2* src = reinterpret_cast<const double2*>(p);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-#pragma unroll
-  for (int kc = 0; kc < kD; kc += kGK) {
-    double xa[8];
-    stage_a(lr, kc + lc, xa);
-    const double2* bs = reinterpret_cast<const double2*>(B + (size_t)rj * kD + kc + lc);
-    double2 xb[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) xb[e] = bs[e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.At[lc + 2 * e][lr] = xa[2 * e];
-      sm.At[lc + 2 * e + 1][lr] = xa[2 * e + 1];
-      sm.Bt[lc + 2 * e][lr] = xb[e].x;
-      sm.Bt[lc + 2 * e + 1][lr] = xb[e].y;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < kGK; ++k) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = sm.At[k][ti + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = sm.Bt[k][tj + 16 * b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
-    }
-    __syncthreads();
+  for (int e = 0; e < 4; ++e) {
+    const double2 v = src[e];
+    x[2 * e] = v.x;
+    x[2 * e + 1] = v.y;
   }
 }
 
@@ -97,31 +51,28 @@ __device__ inline void tile_dot(const double* __restrict__ B, int nb, int j0, St
 __global__ __launch_bounds__(kThreads) void logits_kernel(
     const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int nq,
     int nk, double* __restrict__ P) {
-  __shared__ TileSmem sm;
+  __shared__ TileF64Smem sm;
   const int h = blockIdx.z;
-  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
+  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
   const double* qh = qpool + (size_t)h * nq * kD;
-  auto stage_q = [&](int r, int d0, double (&x)[8]) {
-    const double2* src = reinterpret_cast<const double2*>(qh + (size_t)min(i0 + r, nq - 1) * kD + d0);
+  const double* kh = kpool + (size_t)h * nk * kD;
+  f64x4 acc[2][2];
+  mfma_tile_f64(
+      [&](int r, int d0, double (&x)[8]) { load8d(qh + (size_t)min(i0 + r, nq - 1) * kD + d0, x); },
+      [&](int r, int d0, double (&x)[8]) { load8d(kh + (size_t)min(j0 + r, nk - 1) * kD + d0, x); },
+      sm, acc);
+  const TileF64Map mp;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double2 v = src[e];
-      x[2 * e] = v.x;
-      x[2 * e + 1] = v.y;
+  for (int tr = 0; tr < 2; ++tr)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + mp.row_of(tr, r);
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int j = j0 + mp.col_of(tc);
+        if (i < nq && j < nk) P[((size_t)h * nq + i) * nk + j] = scale * acc[tr][tc][r];
+      }
     }
-  };
-  double acc[4][4];
-  tile_dot(kpool + (size_t)h * nk * kD, nk, j0, stage_q, sm, acc);
-  const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ti + 16 * a;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tj + 16 * b;
-      if (i < nq && j < nk) P[((size_t)h * nq + i) * nk + j] = scale * acc[a][b];
-    }
-  }
 }
 
 // Row softmax in place, one wave per row (row i of head h is workgroup
@@ -208,25 +159,27 @@ __global__ __launch_bounds__(kThreads) void vmv_kernel(
   if (j < n && lane == 0) vmv[(size_t)h * n + j] = s;
 }
 
-// vout = P V for 32 rows (all 64 dims) per workgroup: thread (ti, tj) owns
-// rows ti and ti + 16 and dims tj + 16b (b < 4); the key blocks stream
-// through LDS 64 at a time. Each vout element is one fma chain over j in
-// ascending order.
+// vout = P V for 32 rows (all 64 dims) per workgroup on the matrix cores:
+// wave w owns rows 16*(w>>1) .. +15 and dims 32*(w&1) .. +31 (two 16 x 16
+// tiles); the key blocks stream through LDS 64 at a time, 4 per MFMA step.
+// Row padding: 66 doubles for P (a half-wave reads 16 rows x 2 columns) and
+// 80 for V (2 rows x 16 columns), so both reads are free of bank conflicts.
 constexpr int kVR = 32;  // rows per workgroup
 constexpr int kVJ = 64;  // key blocks per LDS stage
 
 __global__ __launch_bounds__(kThreads) void vout_kernel(
     const double* __restrict__ P, const double* __restrict__ vpool, int nq, int nk,
     double* __restrict__ vout) {
-  __shared__ double Ps[kVR][kVJ + 1];
-  __shared__ double Vs[kVJ][kD + 2];
+  __shared__ double Ps[kVR][kVJ + 2];
+  __shared__ double Vs[kVJ][kD + 16];
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * kVR;
   const int tid = threadIdx.x;
-  const int ti = tid >> 4, tj = tid & 15;
+  const int w = tid >> 6, l = tid & 63;
+  const int rt = 16 * (w >> 1), dt = 32 * (w & 1);
   const double* Ph = P + (size_t)h * nq * nk;
   const double* Vh = vpool + (size_t)h * nk * kD;
-  double acc[2][4] = {};
+  f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
   for (int jc = 0; jc < nk; jc += kVJ) {
     // P: 32 rows x 64 blocks (8 per thread); V: 64 blocks x 64 dims (16 per thread)
 #pragma unroll
@@ -241,29 +194,28 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
       const int idx = tid + e * kThreads;
       const int r = idx >> 5, c2 = idx & 31;
       const int j = min(jc + r, nk - 1);
-      const double2 x = reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[c2];
-      Vs[r][2 * c2] = x.x;
-      Vs[r][2 * c2 + 1] = x.y;
+      *reinterpret_cast<double2*>(&Vs[r][2 * c2]) =
+          reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[c2];
     }
     __syncthreads();
-    const int kmax = min(kVJ, nk - jc);
-    for (int k = 0; k < kmax; ++k) {
-      const double p0 = Ps[ti][k], p1 = Ps[ti + 16][k];
+#pragma unroll 4
+    for (int s4 = 0; s4 < kVJ / 4; ++s4) {
+      const int k = 4 * s4 + (l >> 4);
+      const double a = Ps[rt + (l & 15)][k];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const double vv = Vs[k][tj + 16 * b];
-        acc[0][b] = fma(p0, vv, acc[0][b]);
-        acc[1][b] = fma(p1, vv, acc[1][b]);
-      }
+      for (int t = 0; t < 2; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Vs[k][dt + 16 * t + (l & 15)], acc[t],
+                                                      0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int i = i0 + ti + 16 * a;
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + rt + (l >> 4) + 4 * r;
     if (i < nq)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) vout[((size_t)h * nq + i) * kD + tj + 16 * b] = acc[a][b];
+      for (int t = 0; t < 2; ++t)
+        vout[((size_t)h * nq + i) * kD + dt + 16 * t + (l & 15)] = acc[t][r];
   }
 }
 
@@ -274,20 +226,19 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
     const double* __restrict__ P, const double* __restrict__ vpool,
     const double* __restrict__ M, const double* __restrict__ vmv,
     const double* __restrict__ vout, int nq, int nk, double eps, double* __restrict__ key) {
-  __shared__ TileSmem sm;
-  __shared__ double apart[2][kGT][4];
+  __shared__ TileF64Smem sm;
+  __shared__ double apart[2][kTF][4];
   const int h = blockIdx.z;
-  const int j0 = blockIdx.x * kGT, i0 = blockIdx.y * kGT;
-  const int tid = threadIdx.x;
+  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
   const double* voh = vout + (size_t)h * nq * kD;
+  const double* vph = vpool + (size_t)h * nk * kD;
   const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;
   // stage w_i dims d0 .. d0+7 of row r; the partial vout . w over those
   // dims goes to apart[half][r][thread's quarter]
   auto stage_w = [&](int r, int d0, double (&x)[8]) {
     const double* vr = voh + (size_t)min(i0 + r, nq - 1) * kD;
     double vo8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vo8[e] = vr[d0 + e];
+    load8d(vr + d0, vo8);
     if (Mh == nullptr) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = vo8[e];
@@ -295,40 +246,45 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const double* Mrow = Mh + (size_t)(d0 + e) * kD;
-        double w = 0.0;
+        double wv = 0.0;
 #pragma unroll 8
-        for (int f = 0; f < kD; ++f) w = fma(Mrow[f], vr[f], w);
-        x[e] = w;
+        for (int f = 0; f < kD; ++f) wv = fma(Mrow[f], vr[f], wv);
+        x[e] = wv;
       }
     }
     double pa = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pa = fma(vo8[e], x[e], pa);
-    apart[d0 >= kGK][r][(d0 % kGK) / 8] = pa;
+    apart[d0 >= kTFHalf][r][(d0 % kTFHalf) / 8] = pa;
   };
-  double acc[4][4];
-  tile_dot(vpool + (size_t)h * nk * kD, nk, j0, stage_w, sm, acc);
-  const int ti = tid >> 4, tj = tid & 15;
+  f64x4 acc[2][2];
+  mfma_tile_f64(
+      stage_w,
+      [&](int r, int d0, double (&x)[8]) { load8d(vph + (size_t)min(j0 + r, nk - 1) * kD + d0, x); },
+      sm, acc);
+  const TileF64Map mp;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int r = ti + 16 * a;
-    const int i = i0 + r;
-    double ai = 0.0;
+  for (int tr = 0; tr < 2; ++tr)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int r = 0; r < 4; ++r) {
+      const int rl = mp.row_of(tr, r);
+      const int i = i0 + rl;
+      double ai = 0.0;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) ai += apart[hh][r][q4];
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tj + 16 * b;
-      if (i < nq && j < nk) {
-        const size_t off = ((size_t)h * nq + i) * nk + j;
-        const double q = fmax(ai - 2.0 * acc[a][b] + vmv[(size_t)h * nk + j], 0.0);
-        const double p = P[off];
-        key[off] = p * sqrt(q) / fmax(1.0 - p, eps);
+        for (int q4 = 0; q4 < 4; ++q4) ai += apart[hh][rl][q4];
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int j = j0 + mp.col_of(tc);
+        if (i < nq && j < nk) {
+          const size_t off = ((size_t)h * nq + i) * nk + j;
+          const double q = fmax(ai - 2.0 * acc[tr][tc][r] + vmv[(size_t)h * nk + j], 0.0);
+          const double p = P[off];
+          key[off] = p * sqrt(q) / fmax(1.0 - p, eps);
+        }
       }
     }
-  }
 }
 
 }  // namespace
@@ -337,7 +293,7 @@ hipError_t launch_block_map(const double* qpool, const double* kpool,
                             const ress_shape& s, double scale, double* P,
                             hipStream_t st) {
   const int nq = n_qblocks(s), nk = n_kblocks(s);
-  const dim3 tiles((nk + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
+  const dim3 tiles((nk + kTF - 1) / kTF, (nq + kTF - 1) / kTF, s.H);
   hipLaunchKernelGGL(logits_kernel, tiles, dim3(kThreads), 0, st, qpool, kpool, scale, nq, nk,
                      P);
   const dim3 rows(nq, s.H);
@@ -376,7 +332,7 @@ hipError_t launch_drift(const double* P, const double* vpool, const double* M,
   const int nq = n_qblocks(s), nk = n_kblocks(s);
   hipLaunchKernelGGL(vout_kernel, dim3((nq + kVR - 1) / kVR, s.H), dim3(kThreads), 0, st, P,
                      vpool, nq, nk, vout);
-  const dim3 tiles((nk + kGT - 1) / kGT, (nq + kGT - 1) / kGT, s.H);
+  const dim3 tiles((nk + kTF - 1) / kTF, (nq + kTF - 1) / kTF, s.H);
   hipLaunchKernelGGL(key_kernel, tiles, dim3(kThreads), 0, st, P, vpool, M, vmv, vout, nq, nk,
                      eps, key);
   return hipGetLastError();
