@@ -180,6 +180,35 @@ def cpu_baseline(w, x, idx, cnt, budget_s=15.0):
                       f"{spent:.1f} s"}
 
 
+def residual_drift_report(w, x, shape, qkv, out, dense_out):
+    """Realised residual drift (mean over heads and query blocks of the
+    per-token ||o_sparse - o_dense||^2, M = I) of this workload's selection
+    and of the probability and drift top-k selections at the same budgets;
+    outside any timed region."""
+    import torch
+
+    import block_sparse_global_amd as bsg
+    q, k, v = qkv
+    dr = torch.empty((shape.H, shape.nq), dtype=torch.float64, device="cuda")
+    res = {"measure": "mean over heads and query blocks of per-token ||o_sparse - o_dense||^2"}
+
+    def one(o):
+        bsg.ress_residual_drift(o, dense_out, shape, dr)
+        torch.cuda.synchronize()
+        return float(dr.mean().item())
+
+    res["this_selection"] = one(out)
+    for name, mode, rounds in (("prob_topk", "prob", 0), ("drift_topk", "drift", 0)):
+        lay = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
+                                             rounds=rounds, rho=w.rho)
+        o2 = torch.empty_like(q)
+        lay(q, k, v, o2)
+        res[name] = one(o2)
+        del lay, o2
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,11 +253,14 @@ def main():
     import block_sparse_global_amd as bsg
     df = dense_flops(w)
     dense_ms = float("nan")
+    drift_report = None
     if not args.no_dense:
         dense_out = torch.empty_like(q)
         dense_reps = max(2, min(args.steps, 5))
         dense_ms = time_events(lambda: bsg.dense_attention(q, k, v, shape, dense_out),
                                dense_reps)
+        if not args.no_sweep:
+            drift_report = residual_drift_report(w, x, shape, qkv, out, dense_out)
         del dense_out
     if args.copy_calibration > 0:
         nb = int(args.copy_calibration)
@@ -322,6 +354,7 @@ def main():
         "realised_sparsity": sparsity_of(w, cnt),
         "stages_ms": stages,
         "views_sweep": sweep,
+        "residual_drift": drift_report,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, idx, cnt)

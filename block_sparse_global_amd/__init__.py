@@ -24,9 +24,12 @@ from ._lib import (  # noqa: F401
     Shape,
     ress_block_pool,
     ress_block_score,
+    ress_gram_from_wo,
+    ress_head_budgets,
     ress_last_error,
     ress_refine_dropset,
     ress_refine_workspace_size,
+    ress_residual_drift,
     ress_select_topk,
     ress_select_cdf,
     ress_sparse_attn_fwd,

@@ -39,6 +39,9 @@ ENTRY_POINTS = (
     "ress_select_cdf",
     "ress_refine_dropset",
     "ress_refine_workspace_size",
+    "ress_gram_from_wo",
+    "ress_head_budgets",
+    "ress_residual_drift",
     "ress_sparse_attn_fwd",
     "ress_last_error",
     "ress_version",
@@ -109,8 +112,12 @@ def _load():
     lib.ress_refine_workspace_size.restype = ctypes.c_size_t
     lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
                                          ctypes.c_float, vp, vp, vp]
+    lib.ress_gram_from_wo.argtypes = [vp, ctypes.c_int, i32, ress_shape, dp, vp]
+    lib.ress_head_budgets.argtypes = [vp, i32, i32, vp, ctypes.c_int64, vp]
+    lib.ress_residual_drift.argtypes = [vp, vp, ctypes.c_int, dp, ress_shape, dp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
-              "ress_select_cdf", "ress_refine_dropset", "ress_sparse_attn_fwd"):
+              "ress_select_cdf", "ress_refine_dropset", "ress_sparse_attn_fwd",
+              "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ress_last_error.restype = ctypes.c_char_p
     lib.ress_last_error.argtypes = []
@@ -277,6 +284,39 @@ def ress_refine_dropset(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)),
         _ptr(J_init, "J_init", f64, (H, nq)), _ptr(J_final, "J_final", f64, (H, nq)),
         ws_ptr, workspace.numel(), _stream(stream)))
+
+
+def ress_head_budgets(score, n_k: int, always_keep, total_keep: int) -> np.ndarray:
+    """Per-head keep budgets from head scores (host only); returns int32 [H]."""
+    sc = np.ascontiguousarray(np.asarray(score, dtype=np.float64))
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (int(n_k),):
+        raise ValueError(f"always_keep must have shape ({n_k},)")
+    out = np.empty(sc.shape[0], dtype=np.int32)
+    _check("ress_head_budgets", LIB.ress_head_budgets(
+        sc.ctypes.data_as(ctypes.c_void_p), int(sc.shape[0]), int(n_k), alw_p,
+        int(total_keep), out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def ress_residual_drift(out_sparse, out_dense, shape: Shape, drift, M=None, stream=None):
+    """drift[h][i] = mean over block i's valid tokens of e^T M_h e,
+    e = out_sparse - out_dense (||e||^2 when M is None)."""
+    tok = (shape.H, shape.N_pad, shape.D)
+    _check("ress_residual_drift", LIB.ress_residual_drift(
+        _ptr(out_sparse, "out_sparse", out_sparse.dtype, tok),
+        _ptr(out_dense, "out_dense", out_sparse.dtype, tok), _dtype_code(out_sparse),
+        _ptr(M, "M", torch.float64, (shape.H, shape.D, shape.D)), shape.c(),
+        _ptr(drift, "drift", torch.float64, (shape.H, shape.nq)), _stream(stream)))
+
+
+def ress_gram_from_wo(w_o, shape: Shape, M, stream=None):
+    """M[h] = W_O^h^T W_O^h for w_o of shape [d_model][H*D] (bf16 or float32)."""
+    if w_o.dim() != 2 or w_o.shape[1] != shape.H * shape.D:
+        raise ValueError(f"w_o must have shape [d_model][{shape.H * shape.D}]")
+    _check("ress_gram_from_wo", LIB.ress_gram_from_wo(
+        _ptr(w_o, "w_o", w_o.dtype, tuple(w_o.shape)), _dtype_code(w_o), int(w_o.shape[0]),
+        shape.c(), _ptr(M, "M", torch.float64, (shape.H, shape.D, shape.D)), _stream(stream)))
 
 
 def ress_sparse_attn_fwd(q, k, v, shape: Shape, kept_idx, kept_cnt, k_max: int,

@@ -289,6 +289,122 @@ size_t ress_refine_workspace_size(ress_shape shape) {
   return ress::refine_workspace_bytes(shape);
 }
 
+int ress_head_budgets(const double* score, int32_t H, int32_t n_k, const uint8_t* always_keep,
+                      int64_t total_keep, int32_t* keep) {
+  if (H < 1 || H > RESS_MAX_SEL_HEADS)
+    return fail(RESS_ERR_INVALID_ARG, "H=%d must lie in [1, %d]", H, RESS_MAX_SEL_HEADS);
+  if (n_k < 2 || n_k > RESS_MAX_BLOCKS)
+    return fail(RESS_ERR_INVALID_ARG, "n_k=%d must lie in [2, %d]", n_k, RESS_MAX_BLOCKS);
+  if (score == nullptr || keep == nullptr)
+    return fail(RESS_ERR_INVALID_ARG, "score and keep are required");
+  int n_always = 0;
+  if (always_keep != nullptr)
+    for (int j = 0; j < n_k; ++j) {
+      if (always_keep[j] > 1)
+        return fail(RESS_ERR_INVALID_ARG, "always_keep[%d]=%d is not 0 or 1", j, always_keep[j]);
+      n_always += always_keep[j];
+    }
+  const int cap = n_k - n_always;                         // candidates per row
+  const int floor_c = n_always >= 2 ? 1 : 2 - n_always;   // two kept blocks, one candidate
+  if (cap < floor_c)
+    return fail(RESS_ERR_INVALID_ARG, "no room for candidates (n_k=%d, %d always kept)", n_k,
+                n_always);
+  for (int h = 0; h < H; ++h)
+    if (!(score[h] >= 0.0) || !isfinite(score[h]))
+      return fail(RESS_ERR_INVALID_ARG, "score[%d] must be finite and >= 0", h);
+  const int64_t lo = (int64_t)H * (n_always + floor_c), hi = (int64_t)H * n_k;
+  if (total_keep < lo || total_keep > hi)
+    return fail(RESS_ERR_INVALID_ARG, "total_keep=%lld must lie in [%lld, %lld]",
+                (long long)total_keep, (long long)lo, (long long)hi);
+  // every head gets the floor; the surplus U goes in proportion to the
+  // scores, clipped at cap - floor, the excess of clipped heads spread over
+  // the others until no head exceeds the cap
+  const double U = (double)(total_keep - lo);
+  const double capU = (double)(cap - floor_c);
+  double a[RESS_MAX_SEL_HEADS];
+  bool clipped[RESS_MAX_SEL_HEADS];
+  for (int h = 0; h < H; ++h) clipped[h] = false;
+  for (;;) {
+    double S = 0.0, R = U;
+    int active = 0;
+    for (int h = 0; h < H; ++h) {
+      if (clipped[h]) {
+        R -= capU;
+      } else {
+        S += score[h];
+        ++active;
+      }
+    }
+    bool over = false;
+    for (int h = 0; h < H; ++h) {
+      if (clipped[h]) continue;
+      a[h] = S > 0.0 ? R * score[h] / S : R / (double)active;
+      if (a[h] > capU) over = true;
+    }
+    if (!over) break;
+    for (int h = 0; h < H; ++h)
+      if (!clipped[h] && a[h] > capU) {
+        clipped[h] = true;
+        a[h] = capU;
+      }
+  }
+  // integers: floors, then one more unit to the largest fractional parts
+  // (equal parts: the lower head index), never beyond the cap
+  int64_t b[RESS_MAX_SEL_HEADS], given = 0;
+  for (int h = 0; h < H; ++h) {
+    b[h] = (int64_t)floor(a[h]);
+    if (b[h] > (int64_t)capU) b[h] = (int64_t)capU;
+    given += b[h];
+  }
+  int64_t rem = (int64_t)U - given;
+  while (rem > 0) {
+    int best = -1;
+    double bf = -1.0;
+    for (int h = 0; h < H; ++h) {
+      if (b[h] >= (int64_t)capU) continue;
+      const double f = a[h] - floor(a[h]);
+      if (f > bf) {
+        bf = f;
+        best = h;
+      }
+    }
+    if (best < 0) break;  // cannot happen when total_keep <= H * n_k
+    ++b[best];
+    a[best] = floor(a[best]);  // its fractional part is used up
+    --rem;
+  }
+  for (int h = 0; h < H; ++h) keep[h] = (int32_t)(n_always + floor_c + b[h]);
+  return ok();
+}
+
+int ress_gram_from_wo(const void* w_o, int dtype, int32_t d_model, ress_shape shape,
+                      double* M, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_dtype(dtype)) != RESS_OK) return rc;
+  REQUIRE_PTR(w_o);
+  REQUIRE_PTR(M);
+  if (d_model < 1 || d_model > (1 << 20))
+    return fail(RESS_ERR_INVALID_ARG, "d_model=%d must lie in [1, 2^20]", d_model);
+  hipError_t e = ress::launch_gram(w_o, dtype, d_model, shape, M,
+                                   static_cast<hipStream_t>(stream));
+  return hip_status(e, "gram launch");
+}
+
+int ress_residual_drift(const void* out_sparse, const void* out_dense, int dtype,
+                        const double* M, ress_shape shape, double* drift, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_dtype(dtype)) != RESS_OK) return rc;
+  REQUIRE_PTR(out_sparse);
+  REQUIRE_PTR(out_dense);
+  OPTIONAL_PTR(M);
+  REQUIRE_PTR(drift);
+  hipError_t e = ress::launch_residual_drift(out_sparse, out_dense, dtype, M, shape, drift,
+                                             static_cast<hipStream_t>(stream));
+  return hip_status(e, "residual drift launch");
+}
+
 int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
                          int dtype, ress_shape shape, const int32_t* kept_idx,
                          const int32_t* kept_cnt, int32_t k_max, float scale,

@@ -98,6 +98,12 @@ hipError_t launch_refine(const double* P, const double* key,
 // rows of all heads, in HBM).
 size_t refine_workspace_bytes(const ress_shape& s);
 
+hipError_t launch_gram(const void* w_o, int dtype, int d_model, const ress_shape& s, double* M,
+                       hipStream_t st);
+
+hipError_t launch_residual_drift(const void* os, const void* od, int dtype, const double* M,
+                                 const ress_shape& s, double* drift, hipStream_t st);
+
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
                        const ress_shape& s, const int32_t* kept_idx,
                        const int32_t* kept_cnt, int32_t k_max, float scale,

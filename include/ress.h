@@ -223,6 +223,47 @@ int ress_refine_dropset(const double* P, const double* key,
 size_t ress_refine_workspace_size(ress_shape shape);
 
 /*
+ * ress_head_budgets — per-head keep budgets from head importance scores, the
+ * allocation ReSS adopts from HeSS (ReSS page §4.4 and Appendix D:
+ * proportional allocation with iterative clipping at the cap). Host only;
+ * no device memory is touched.
+ *
+ * Every head first gets the floor f (at least two kept blocks per row and at
+ * least one candidate: f = max(1, 2 - |always|) candidates). The surplus
+ * U = total_keep - H (|always| + f) is split in proportion to score[h]
+ * (equally when every score is 0); a head whose share exceeds the cap
+ * (all n_k - |always| candidates, less f) is fixed at the cap and the rest
+ * of U is split again among the others, until no share exceeds the cap.
+ * Integer budgets: each share rounded down, then the units still missing go
+ * one each to the largest fractional parts (equal parts: the lower head),
+ * never beyond the cap. keep[h] = |always| + f + that integer, so
+ * sum_h keep[h] = total_keep, ready for ress_select_topk.
+ *
+ * score: HOST float64 [H], finite, >= 0. H: 1 .. 64. n_k: key blocks per
+ * row, 2 .. 4096. always_keep: HOST uint8 [n_k] or NULL. total_keep: in
+ * [H (|always| + f), H n_k]. keep: HOST int32 [H], written.
+ */
+int ress_head_budgets(const double* score, int32_t H, int32_t n_k, const uint8_t* always_keep,
+                      int64_t total_keep, int32_t* keep);
+
+/*
+ * ress_gram_from_wo — per-head Gram matrices of the output projection
+ * (ReSS page §4.2, Eq. 8): M[h] = (W_O^h)^T W_O^h, where W_O^h is the slice
+ * of the output projection that maps head h's D outputs into the residual
+ * stream, so that e^T M[h] e = ||W_O^h e||^2 (Eq. 6, 9). The result feeds
+ * the M argument of ress_block_score and ress_refine_dropset, making the
+ * drift score and the refinement objective residual-space exact.
+ *
+ * w_o: device [d_model][H*D] row-major of `dtype` (the layout of a linear
+ * layer's weight from H*D inputs to d_model outputs; W_O^h is columns
+ * h*D .. h*D+D-1). d_model: 1 .. 2^20. M: device float64 [H][D][D]; each
+ * entry is a fixed-order float64 sum over the d_model rows (products of
+ * bf16 or float32 values are exact in float64).
+ */
+int ress_gram_from_wo(const void* w_o, int dtype, int32_t d_model, ress_shape shape,
+                      double* M, void* stream);
+
+/*
  * ress_sparse_attn_fwd — exact attention over the kept key blocks (ReSS page
  * §3 step (3): softmax renormalised among the selected blocks alone, the
  * unselected blocks contributing nothing; dense global attention when kept_idx is
@@ -249,6 +290,25 @@ int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
                          int dtype, ress_shape shape, const int32_t* kept_idx,
                          const int32_t* kept_cnt, int32_t k_max, float scale,
                          void* out, float* lse, void* stream);
+
+/*
+ * ress_residual_drift — the drift a sparse attention output leaves in the
+ * residual stream, measured against the dense output (ReSS page §4.2,
+ * Eq. 6 and 9 at token level; the quantity the page argues governs the cost
+ * of sparsification, §6):
+ *
+ *   drift[h][i] = mean over the valid tokens t of query block i of
+ *                 e^T M[h] e,   e = out_sparse[h][t] - out_dense[h][t],
+ *
+ * = ||W_O^h e||^2 averaged over the block when M[h] = (W_O^h)^T W_O^h
+ * (ress_gram_from_wo); ||e||^2 when M is NULL.
+ *
+ * out_sparse, out_dense: device [H][N_pad][D] of `dtype` (outputs of
+ * ress_sparse_attn_fwd with and without kept_idx). M: device float64
+ * [H][D][D], symmetric, or NULL. drift: device float64 [H][n_q].
+ */
+int ress_residual_drift(const void* out_sparse, const void* out_dense, int dtype,
+                        const double* M, ress_shape shape, double* drift, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* ress_last_error(void);

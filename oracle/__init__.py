@@ -12,15 +12,18 @@ from .ress_oracle import (  # noqa: F401
     block_map,
     pooled_output,
     drift_key,
+    gram_from_wo,
     score_key,
     select_topk,
     select_cdf,
     kept_lists,
+    head_budgets,
     swap_schedule,
     drop_objective,
     swap_gains,
     refine_dropset,
     masked_attention,
     dense_attention,
+    residual_drift,
     run_selection,
 )

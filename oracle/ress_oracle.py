@@ -94,6 +94,18 @@ def _gram(M: Optional[np.ndarray], h: int, D: int) -> np.ndarray:
     return np.eye(D) if M is None else M[h]
 
 
+def gram_from_wo(W: np.ndarray, H: int, D: int) -> np.ndarray:
+    """Per-head Gram matrices of the output projection, ReSS page Eq. 8:
+    M_h = (W_O^h)^T W_O^h with W_O^h the columns h*D .. h*D+D-1 of
+    W [d_model][H*D] (the head's slice of the projection into the residual
+    stream). Returns float64 [H][D][D]."""
+    M = np.empty((H, D, D), dtype=np.float64)
+    for h in range(H):
+        Wh = np.asarray(W[:, h * D:(h + 1) * D], dtype=np.float64)
+        M[h] = Wh.T @ Wh
+    return M
+
+
 def drift_key(P: np.ndarray, vpool: np.ndarray, M: Optional[np.ndarray],
               eps: float = 1e-4, row_chunk: int = 64):
     """ReSS drift ranking key, Eq. 5-7, in the direct (unexpanded) form.
@@ -253,6 +265,59 @@ def kept_lists(kept: np.ndarray):
             js = np.nonzero(kept[h, i])[0]
             idx[h, i, : len(js)] = js
     return idx, cnt
+
+
+def head_budgets(score, n_k: int, always, total_keep: int):
+    """Per-head keep budgets from head importance scores: the HeSS allocation
+    the ReSS page adopts (§4.4; Appendix D: proportional allocation with
+    iterative clipping at the cap).
+
+    Reading: every head first gets the floor f = max(1, 2 - |always|)
+    candidates (two kept blocks per row, Appendix F, and at least one
+    candidate); the surplus U = total_keep - H (|always| + f) is split in
+    proportion to the scores (equally if all are 0); heads whose share
+    exceeds the cap (n_k - |always| - f) are fixed at the cap and the rest
+    of U is split again among the others, until no share exceeds the cap.
+    Integers: shares rounded down, then one unit each to the largest
+    fractional parts (ties: lower head), never beyond the cap.
+
+    Returns (keep int [H], share float64 [H]) with share the real-valued
+    surplus allocation before rounding.
+    """
+    score = [float(x) for x in score]
+    H = len(score)
+    n_alw = int(np.sum(np.asarray(always) != 0)) if always is not None else 0
+    f = max(1, 2 - n_alw)
+    capU = float(n_k - n_alw - f)
+    U = float(total_keep - H * (n_alw + f))
+    clipped = [False] * H
+    a = [0.0] * H
+    while True:
+        active = [h for h in range(H) if not clipped[h]]
+        S = 0.0
+        for h in active:
+            S += score[h]
+        R = U - capU * (H - len(active))
+        for h in active:
+            a[h] = R * score[h] / S if S > 0.0 else R / len(active)
+        over = [h for h in active if a[h] > capU]
+        if not over:
+            break
+        for h in over:
+            clipped[h] = True
+            a[h] = capU
+    share = list(a)
+    b = [min(math.floor(x), int(capU)) for x in a]
+    rem = int(U) - sum(b)
+    frac = [x - math.floor(x) for x in a]
+    while rem > 0:
+        cands = [h for h in range(H) if b[h] < int(capU)]
+        best = max(cands, key=lambda h: (frac[h], -h))
+        b[best] += 1
+        frac[best] = 0.0
+        rem -= 1
+    keep = np.array([n_alw + f + x for x in b], dtype=np.int32)
+    return keep, np.array(share)
 
 
 # ---------------------------------------------------------------------------
@@ -418,6 +483,27 @@ def dense_attention(q, k, v, N: int, B: int, scale: float, blocks=None,
     Bk = B if Bk is None else Bk
     kept = np.ones((H, N_pad // B, -(-N // Bk)), dtype=bool)
     return masked_attention(q, k, v, kept, N, B, scale, blocks, Bk)
+
+
+def residual_drift(O_sparse, O_dense, M, N: int, B: int):
+    """Mean over the valid tokens t of every query block of e_t^T M_h e_t,
+    e_t = O_sparse[h, t] - O_dense[h, t] (ReSS page Eq. 6 and 9 at token
+    level: ||W_O^h e_t||^2 when M_h = (W_O^h)^T W_O^h; ||e_t||^2 for M None).
+
+    O_sparse, O_dense: float64 [H][N_pad][D]. Returns float64 [H][n_q].
+    """
+    H, N_pad, D = O_sparse.shape
+    n = N_pad // B
+    out = np.zeros((H, n), dtype=np.float64)
+    for h in range(H):
+        Mh = _gram(M, h, D)
+        for i in range(n):
+            t0, t1 = i * B, min((i + 1) * B, N)
+            if t1 <= t0:
+                continue
+            e = O_sparse[h, t0:t1] - O_dense[h, t0:t1]
+            out[h, i] = np.mean(np.sum((e @ Mh) * e, axis=1))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -20,4 +20,5 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_inputs,
     make_gram,
+    make_wo,
 )

@@ -136,6 +136,17 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
+def make_wo(heads: int, head_dim: int = 64, d_model: int = 1024, seed: int = 2,
+            scale: float = 0.03):
+    """A random output projection W_O [d_model][heads*head_dim] (the layout of
+    a linear layer's weight), entries N(0, scale^2) rounded once to bf16 and
+    returned as bf16 bit patterns (uint16). Stands in for a trained
+    projection, which does not exist here."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((d_model, heads * head_dim)) * scale).astype(np.float32)
+    return f32_to_bf16_bits(w)
+
+
 def make_gram(heads: int, head_dim: int = 64, width: int = 1024, seed: int = 1):
     """Random symmetric positive semi-definite matrices [H][D][D], float64.
 

@@ -22,6 +22,7 @@ def test_header_declares_every_call():
     names = declared_functions()
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk", "ress_select_cdf",
               "ress_refine_dropset", "ress_refine_workspace_size", "ress_sparse_attn_fwd",
+              "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
               "ress_last_error", "ress_version"):
         assert f in names
 
@@ -114,6 +115,18 @@ def _arr(a, t):
     return a, a.ctypes.data_as(ctypes.c_void_p)
 
 
+def test_gram_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    s = _shape(H=2)
+    assert L.ress_gram_from_wo(None, 0, 64, s, FAKE, None) == -1
+    assert L.ress_gram_from_wo(FAKE, 0, 64, s, MISALIGNED, None) == -1
+    assert L.ress_gram_from_wo(FAKE, 5, 64, s, FAKE, None) == -1
+    assert L.ress_gram_from_wo(FAKE, 0, 0, s, FAKE, None) == -1
+    assert "d_model" in b.ress_last_error()
+    assert L.ress_gram_from_wo(FAKE, 0, 64, _shape(D=32), FAKE, None) == -2
+
+
 def test_selection_budget_checks():
     import block_sparse_global_amd as b
     L = b.LIB
@@ -200,3 +213,35 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros((1, 128, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device tensor"):
         b.ress_sparse_attn_fwd(x, x, x, shape, None, None, 1, 0.125, x)
+
+
+def test_head_budgets_match_the_oracle_and_check_arguments():
+    """The host allocation against the oracle on random scores (bit-exact
+    integers), and its argument checks."""
+    import block_sparse_global_amd as b
+    import oracle
+    r = np.random.default_rng(61)
+    for trial in range(200):
+        H = int(r.integers(1, 65))
+        n_k = int(r.integers(4, 2200))
+        n_alw = int(r.integers(0, 9))
+        always = np.zeros(n_k, np.uint8); always[n_k - n_alw:] = 1
+        f = max(1, 2 - n_alw)
+        score = r.gamma(0.5, 1.0, H) * (r.uniform(size=H) < 0.9)
+        if trial % 17 == 0:
+            score[:] = 0.0
+        total = int(r.integers(H * (n_alw + f), H * n_k + 1))
+        got = b.ress_head_budgets(score, n_k, always if n_alw else None, total)
+        want, _ = oracle.head_budgets(score, n_k, always if n_alw else None, total)
+        assert np.array_equal(got, want), (trial, got, want)
+    with pytest.raises(b.RessError):
+        b.ress_head_budgets([1.0, -1.0], 10, None, 10)
+    with pytest.raises(b.RessError):
+        b.ress_head_budgets([1.0, float("nan")], 10, None, 10)
+    with pytest.raises(b.RessError):
+        b.ress_head_budgets([1.0, 1.0], 10, None, 3)      # below two blocks per head
+    with pytest.raises(b.RessError):
+        b.ress_head_budgets([1.0, 1.0], 10, None, 21)     # above n_k per head
+    with pytest.raises(b.RessError):
+        b.ress_head_budgets([1.0] * 65, 10, None, 200)    # too many heads
+

@@ -385,6 +385,77 @@ def test_block64_bf16_drift_with_gram_and_refine():
     assert np.mean(g["J_final"] / g["J_init"]) < 1.0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gram_from_wo_feeds_the_drift_score(dtype):
+    """Eq. 8 on the GPU from a 1024 x (16*64) projection, then the drift key
+    and refinement with that M against the oracle with the oracle's M."""
+    b = _lib()
+    H, D = 16, 64
+    wbits = synth.make_wo(H, D, 1024)
+    W64 = synth.as_f64(wbits, "bf16")
+    if dtype == "bf16":
+        Wt = torch.from_numpy(wbits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        Wt = torch.from_numpy(W64.astype(np.float32)).cuda()
+    shape = b.Shape(H, 256, 256, D, 64)
+    Mg = torch.empty((H, D, D), dtype=torch.float64, device="cuda")
+    b.ress_gram_from_wo(Wt, shape, Mg)
+    torch.cuda.synchronize()
+    Mref = oracle.gram_from_wo(W64, H, D)
+    err = np.abs(Mg.cpu().numpy() - Mref).max() / np.abs(Mref).max()
+    assert err <= 1e-13, f"Gram relative error {err:.3e}"
+    if dtype == "f32":
+        return
+    w, x = _small(name="wo", views=4, patches_per_view=300, specials_per_view=5, heads=H,
+                  block=64, sparsity=(0.75, 0.75), score="drift", rounds=3, rho=0.5)
+    g = run_gpu(w, x, "drift", M=Mg.cpu().numpy())
+    N, B, n = w.N, w.block, w.n_blocks
+    qp = oracle.block_pool(f64(x["q"], w), N, B)
+    kp = oracle.block_pool(f64(x["k"], w), N, B)
+    vp = oracle.block_pool(f64(x["v"], w), N, B)
+    P = oracle.block_map(qp, kp, 0.125)
+    key, vout, _ = oracle.drift_key(P, vp, Mref, 1e-4)
+    _close(g["key"], key, 1e-10, "drift key with M from W_O")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    compare_masks(kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n), kept, key,
+                  x["always"], x["keep"])
+    start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
+    kr, J0, J1, mg = oracle.refine_dropset(P, vp, vout, Mref, x["keep"], x["always"], start,
+                                           w.rounds, w.rho)
+    assert np.allclose(g["J_init"], J0, rtol=1e-9, atol=0)
+    same = np.all(kept_mask_from_lists(g["idx"], g["cnt"], n) == kr, axis=-1)
+    assert np.all(same | (mg < 1e-6))
+    assert np.allclose(g["J_final"][same], J1[same], rtol=1e-9, atol=0)
+
+
+@pytest.mark.parametrize("with_m", [False, True])
+def test_residual_drift_of_sparse_vs_dense(with_m):
+    """Eq. 6/9 at token level on the GPU's own sparse and dense outputs."""
+    b = _lib()
+    w, x = _small(name="rd", views=4, patches_per_view=300, specials_per_view=5, heads=16,
+                  block=128, sparsity=(0.75, 0.75), score="drift", rounds=2)
+    M = None
+    if with_m:
+        M = oracle.gram_from_wo(synth.as_f64(synth.make_wo(16, 64, 1024), "bf16"), 16, 64)
+    g = run_gpu(w, x, "drift", M=M)
+    shape = b.Shape(*w.shape_args())
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    dense = torch.empty_like(q)
+    b.dense_attention(q, k, v, shape, dense)
+    sparse = torch.from_numpy(g["out"]).to(torch.bfloat16).cuda()   # exact: bf16 values
+    drift = torch.empty((w.heads, w.n_blocks), dtype=torch.float64, device="cuda")
+    Mt = torch.from_numpy(M).cuda() if M is not None else None
+    b.ress_residual_drift(sparse, dense, shape, drift, Mt)
+    torch.cuda.synchronize()
+    ref = oracle.residual_drift(g["out"].astype(np.float64),
+                                dense.float().cpu().numpy().astype(np.float64), M, w.N, w.block)
+    got = drift.cpu().numpy()
+    assert np.all(ref > 0)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err <= 1e-12, f"drift relative error {err:.3e}"
+    print(f"[drift] M={'W_O' if with_m else 'I'}: mean {got.mean():.4e}")
+
+
 def test_reruns_are_bit_identical_on_a_side_stream():
     w, x = _small(name="r", views=6, patches_per_view=400, specials_per_view=5, heads=4,
                   block=128, sparsity=(0.8, 0.8), score="drift", rounds=3)

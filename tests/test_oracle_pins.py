@@ -153,6 +153,33 @@ def test_drift_key_with_gram_is_norm_after_projection():
             assert key[0, i, j] == pytest.approx(np.linalg.norm(W @ (vt - vo)), rel=1e-11)
 
 
+def test_gram_from_wo_orthonormal_slices_and_residual_norm():
+    # Eq. 8: a head whose projection slice has orthonormal columns gets
+    # M = I; in general e^T M e = ||W_O^h e||^2 (Eq. 9), so the drift key
+    # with M from the slices is the residual-space norm of the explicit
+    # single-block masking change (Eq. 3-4, 6-7).
+    H, D, d = 3, 5, 17
+    r = rng(21)
+    Wq = np.concatenate([np.linalg.qr(r.standard_normal((d, D)))[0] for _ in range(H)], axis=1)
+    assert np.allclose(oracle.gram_from_wo(Wq, H, D), np.eye(D)[None].repeat(H, 0), atol=1e-14)
+    W = r.standard_normal((d, H * D))
+    M = oracle.gram_from_wo(W, H, D)
+    for h in range(H):
+        assert np.allclose(M[h], M[h].T, rtol=0, atol=1e-13)
+        assert np.trace(M[h]) == pytest.approx(np.sum(W[:, h * D:(h + 1) * D] ** 2), rel=1e-13)
+    n = 7
+    P, V = _random_map(22, H, n, D)
+    key, _, _ = oracle.drift_key(P, V, M, eps=1e-4)
+    for h in range(H):
+        Wh = W[:, h * D:(h + 1) * D]
+        for i in range(n):
+            for j in range(n):
+                w = P[h, i].copy(); w[j] = 0.0
+                vt = (w[:, None] * V[h]).sum(0) / w.sum()
+                vo = (P[h, i][:, None] * V[h]).sum(0)
+                assert key[h, i, j] == pytest.approx(np.linalg.norm(Wh @ (vt - vo)), rel=1e-11)
+
+
 def test_drift_key_eps_clamp():
     # a block holding almost all mass: 1 - P < eps, so the key is s / eps
     D = 2
@@ -291,6 +318,68 @@ def test_cdf_count_grows_with_tau():
             assert np.all(taken >= prev)
         prev = taken
     assert prev.max() == 19
+
+
+# ---------------------------------------------------------------------------
+# Head budgets (ReSS page §4.4, Appendix D: HeSS proportional allocation with
+# iterative clipping at the cap)
+# ---------------------------------------------------------------------------
+
+def _water_fill(score, U, capU):
+    # independent form of proportional allocation with clipping: the share of
+    # head h is min(capU, alpha s_h) with alpha found by bisection
+    lo, hi = 0.0, 1.0
+    while sum(min(capU, hi * x) for x in score) < U:
+        hi *= 2.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if sum(min(capU, mid * x) for x in score) < U:
+            lo = mid
+        else:
+            hi = mid
+    return np.array([min(capU, hi * x) for x in score])
+
+
+def test_head_budgets_are_water_filling_and_sum_to_the_total():
+    r = rng(51)
+    for trial in range(40):
+        H = int(r.integers(2, 17))
+        n_k = int(r.integers(8, 300))
+        n_alw = int(r.integers(0, 4))
+        always = np.zeros(n_k, np.uint8); always[n_k - n_alw:] = 1
+        f = max(1, 2 - n_alw)
+        score = r.gamma(0.7, 1.0, H) + 1e-3        # positive: alpha is defined
+        lo, hi = H * (n_alw + f), H * n_k
+        total = int(r.integers(lo, hi + 1))
+        keep, share = oracle.head_budgets(score, n_k, always, total)
+        assert keep.sum() == total
+        assert np.all(keep >= n_alw + f) and np.all(keep <= n_k)
+        U, capU = total - lo, n_k - n_alw - f
+        assert np.allclose(share, _water_fill(score, U, capU), rtol=0, atol=1e-9 * max(U, 1))
+        # integers: each within one unit of the real share
+        assert np.all(np.abs((keep - n_alw - f) - share) < 1.0 + 1e-9)
+
+
+def test_head_budgets_closed_forms():
+    # equal scores: uniform, the remainder one unit each to the lowest heads
+    keep, share = oracle.head_budgets([2.0] * 5, 100, None, 5 * 20 + 3)
+    assert list(keep) == [21, 21, 21, 20, 20] and np.allclose(share, (103 - 5 * 2) / 5)
+    # no clipping: shares proportional to the scores
+    keep, share = oracle.head_budgets([1.0, 2.0, 5.0], 1000, None, 3 * 2 + 80)
+    assert np.allclose(share, [10.0, 20.0, 50.0]) and list(keep) == [12, 22, 52]
+    # one dominant head clipped at all candidates, the rest split evenly
+    keep, _ = oracle.head_budgets([100.0, 1.0, 1.0], 10, None, 20)
+    assert list(keep) == [10, 5, 5]
+    # a zero-score head keeps the floor: two blocks, or one candidate plus
+    # the always-kept ones
+    keep, _ = oracle.head_budgets([0.0, 1.0], 50, None, 30)
+    assert list(keep) == [2, 28]
+    alw = np.zeros(50, np.uint8); alw[[48, 49]] = 1
+    keep, _ = oracle.head_budgets([0.0, 1.0], 50, alw, 30)
+    assert list(keep) == [3, 27]
+    # the scored head clipped, the zero-score heads then share the rest evenly
+    keep, _ = oracle.head_budgets([1.0, 0.0, 0.0], 10, None, 24)
+    assert list(keep) == [10, 7, 7]
 
 
 # ---------------------------------------------------------------------------
@@ -506,6 +595,28 @@ def test_key_blocks_of_half_size_pool_and_attend_like_the_square_grid():
     s = 0.3 * q[0, :128] @ k[0, 192:256].T
     w = np.exp(s - s.max(1, keepdims=True)); w /= w.sum(1, keepdims=True)
     assert np.allclose(O3[0, :128], w @ v[0, 192:256], rtol=0, atol=1e-13)
+
+
+def test_residual_drift_is_the_projected_output_change():
+    # Eq. 6 / 9 at token level: with M = W^T W the drift of a token is
+    # ||W (o_sparse - o_dense)||^2; equal outputs give 0; padded rows and the
+    # partial last block count only valid tokens
+    r = rng(71)
+    H, D, N, N_pad, B, d = 2, 6, 300, 384, 128, 9
+    Os, Od = r.standard_normal((H, N_pad, D)), r.standard_normal((H, N_pad, D))
+    Os[:, N:] = 1e6                                    # padding must not count
+    W = r.standard_normal((d, H * D))
+    M = oracle.gram_from_wo(W, H, D)
+    got = oracle.residual_drift(Os, Od, M, N, B)
+    for h in range(H):
+        Wh = W[:, h * D:(h + 1) * D]
+        for i, (t0, t1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+            ref = np.mean([np.linalg.norm(Wh @ (Os[h, t] - Od[h, t])) ** 2 for t in range(t0, t1)])
+            assert got[h, i] == pytest.approx(ref, rel=1e-12)
+    assert np.all(oracle.residual_drift(Od, Od, M, N, B) == 0.0)
+    e = Os[:, :N] - Od[:, :N]
+    assert oracle.residual_drift(Os, Od, None, N, B)[1, 0] == pytest.approx(
+        np.mean(np.sum(e[1, :128] ** 2, axis=1)), rel=1e-13)
 
 
 def test_attention_zero_sparsity_equals_dense_sdpa():
