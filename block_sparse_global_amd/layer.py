@@ -74,7 +74,7 @@ class BlockSparseGlobalAttention:
                     if with_lse else None)
         self.out = None
 
-    # -- the five steps -------------------------------------------------------
+    # -- the steps ------------------------------------------------------------
     def pool(self, q, k, v, stream=None):
         ress_block_pool(q, k, v if self.vpool is not None else None, self.shape,
                         self.qpool, self.kpool, self.vpool, stream)
