@@ -358,6 +358,63 @@ def test_padding_garbage_is_ignored():
     assert np.all(got["out"][:, w.N:] == 0)
 
 
+def test_single_token_sequence():
+    """N = 1: the only key is the token itself, so the output is v[0] and the
+    log-sum-exp is scale q.k; the 63 padded rows are zero."""
+    b = _lib()
+    r = np.random.default_rng(5)
+    x = {t: synth.f32_to_bf16_bits(r.standard_normal((1, 64, 64)).astype(np.float32))
+         for t in ("q", "k", "v")}
+    shape = b.Shape(1, 1, 64, 64, 64)
+    q, k, v = (to_torch_tokens(x[t], "bf16") for t in ("q", "k", "v"))
+    out = torch.full_like(q, 3.0)
+    lse = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    b.dense_attention(q, k, v, shape, out, lse=lse)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    vf, qf, kf = (synth.as_f64(x[t], "bf16") for t in ("v", "q", "k"))
+    assert np.array_equal(got[0, 0], vf[0, 0].astype(np.float32))
+    assert np.all(got[0, 1:] == 0)
+    assert lse.cpu().numpy()[0, 0] == pytest.approx(0.125 * float(qf[0, 0] @ kf[0, 0]), abs=1e-3)
+
+
+def test_maximum_block_count_drift_refine_and_attention():
+    """n = 4096 key blocks (the cap), two heads, drift + 2 refinement rounds at
+    99% sparsity: the long-row paths (keys in LDS) against the oracle on
+    sampled rows, and attention on sampled query blocks."""
+    w, x = _small(name="max", views=1, patches_per_view=524288 - 100, specials_per_view=0,
+                  heads=2, block=128, sparsity=(0.99, 0.99), score="drift", rounds=2)
+    assert w.n_blocks == 4096
+    g = run_gpu(w, x, "drift")
+    N, B, n, H = w.N, w.block, w.n_blocks, w.heads
+    qp = oracle.block_pool(f64(x["q"], w), N, B)
+    kp = oracle.block_pool(f64(x["k"], w), N, B)
+    vp = oracle.block_pool(f64(x["v"], w), N, B)
+    _close(g["qpool"], qp, 1e-12, "qpool")
+    P = oracle.block_map(qp, kp, 0.125)
+    rows = [0, 1, 777, 2048, 3001, 4095]
+    _close(g["P"][:, rows], P[:, rows], 1e-12, "P rows")
+    key, vout, _ = oracle.drift_key(P[:, rows], vp, None, 1e-4)
+    _close(g["key"][:, rows], key, 1e-10, "drift key rows")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    topk = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)[:, rows]
+    compare_masks(topk, kept, key, x["always"], x["keep"])
+    kr, J0, J1, mg = oracle.refine_dropset(P[:, rows], vp, vout, None, x["keep"], x["always"],
+                                           topk, w.rounds, w.rho)
+    assert np.allclose(g["J_init"][:, rows], J0, rtol=1e-9, atol=0)
+    same = np.all(kept_mask_from_lists(g["idx"], g["cnt"], n)[:, rows] == kr, axis=-1)
+    assert np.all(same | (mg < 1e-6))
+    assert np.allclose(g["J_final"][:, rows][same], J1[same], rtol=1e-9, atol=0)
+    full = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    blocks = [(0, 0), (1, 2048), (0, 4095), (1, 4095)]
+    O, _ = oracle.masked_attention(f64(x["q"], w), f64(x["k"], w), f64(x["v"], w), full, N, B,
+                                   0.125, blocks=blocks)
+    got = np.concatenate([g["out"][h, i * B:min((i + 1) * B, N)] for h, i in blocks])
+    want = np.concatenate([O[h, i * B:min((i + 1) * B, N)] for h, i in blocks])
+    mx, mean, _ = attn_errors(got, want)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+
+
 def test_block64_bf16_drift_with_gram_and_refine():
     w, x = _small(name="g", views=4, patches_per_view=300, specials_per_view=5, heads=2,
                   block=64, sparsity=(0.5, 0.5), score="drift", rounds=4, rho=1.0)
