@@ -46,9 +46,9 @@ CDF_TAU = 0.05
 
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "5b0e3a465ae00362a841b7f0972259f9ca9b31b152909c1f843f942c9a8d3aa9",
-    "read_bytes": 8459415931,
-    "write_bytes": 281544160,
+    "source_sha256": "f2550d696f457638dec8475fab88a1be5918e0440e6531ef6cb2d1160362011a",
+    "read_bytes": 4708016605,
+    "write_bytes": 281542976,
 }
 
 

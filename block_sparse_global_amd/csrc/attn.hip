@@ -346,34 +346,39 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
         va[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
+    // Two phases with the wave's priority raised: first every bf16 weight of
+    // the block (exponentials and their row sum, VALU only), then all PV
+    // MFMAs back to back at a higher priority. A wave and its matrix core
+    // then alternate in long runs instead of one exponential batch per MFMA
+    // pair, and a wave whose P is complete gets the matrix core ahead of
+    // waves still in their S product or max. Same bits as an interleaved
+    // order; measured 4-5% faster at 100 views.
     bf16x8 vops[2][2];
-    // Wave priority: raised for the whole PV section (exponentials and PV
-    // MFMAs) and raised further while its MFMAs issue, so that a wave whose
-    // P is ready gets the matrix core ahead of waves still in their S
-    // product or max (measured +2.5% at 100 views over equal priorities).
+    bf16x8 pall[2 * kKT];
     __builtin_amdgcn_s_setprio(1);
-    v_operands(0, vops[0]);
 #pragma unroll
     for (int step = 0; step < 2 * kKT; ++step) {
       const int kt = step >> 1, hf = step & 1;
-      if (step + 1 < 2 * kKT) v_operands(step + 1, vops[(step + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);  // keeps those reads ahead of this step
-      bf16x8 pb;
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        pb[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
+        pall[step][r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
       // row sum of the very bf16 weights the PV product uses, two per
       // instruction (bf16 dot product with (1, 1), float32 accumulation)
 #pragma unroll
       for (int r = 0; r < 8; r += 2) {
-        const bf16x2 pp = {pb[r], pb[r + 1]};
+        const bf16x2 pp = {pall[step][r], pall[step][r + 1]};
         psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
       }
-      __builtin_amdgcn_s_setprio(2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(3);
+    v_operands(0, vops[0]);
+#pragma unroll
+    for (int step = 0; step < 2 * kKT; ++step) {
+      if (step + 1 < 2 * kKT) v_operands(step + 1, vops[(step + 1) & 1]);
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[step & 1][dt], pb, o[dt], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(1);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[step & 1][dt], pall[step], o[dt], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     l_run += psum;
