@@ -101,6 +101,19 @@ def setup(name, mode=None, x=None, tau=None):
     return w, x, shape, layer, (q, k, v), out
 
 
+def hess_inputs(name):
+    """Inputs of workload `name` with per-head budgets from stand-in head
+    scores, allocated by ress_head_budgets (proportional with clipping) at
+    the same total budget as the workload's own."""
+    import block_sparse_global_amd as bsg
+    import synth
+    w = synth.get_workload(name)
+    x = dict(synth.make_inputs(w))
+    x["keep"] = bsg.ress_head_budgets(synth.make_head_scores(w.heads), w.n_kblocks,
+                                      x["always"], int(np.sum(x["keep"])))
+    return x
+
+
 def attn_traffic(workload):
     """Counter-measured bytes of one attention launch, or None when the kernel
     source or the workload differs from the ones the counters were taken on."""
@@ -143,6 +156,40 @@ def stage_breakdown(layer, qkv, out, reps):
         for i, n in enumerate(names):
             acc[n] += ev[i].elapsed_time(ev[i + 1])
     return {n: acc[n] / reps for n in names}
+
+
+def refine_paths_ms(w, x, shape, layer, reps):
+    """The refinement step by both library paths on the same top-k lists:
+    kernels per round (the layer's) and the fused kernel; None without
+    refinement or for rows longer than the fused kernel takes."""
+    import torch
+
+    import block_sparse_global_amd as bsg
+    if layer.rounds <= 0 or shape.nk > bsg.REFINE_FUSED_MAX_BLOCKS:
+        return None
+    fused = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=layer.mode,
+                                           rounds=layer.rounds, rho=layer.rho, M=layer.M,
+                                           refine_impl="fused")
+    for buf in ("P", "key", "vpool", "vout"):  # the same score outputs
+        setattr(fused, buf, getattr(layer, buf))
+    layer.select()  # the top-k lists both paths start from
+    idx0, cnt0 = layer.kept_idx.clone(), layer.kept_cnt.clone()
+    res = {}
+    for name, L in (("rounds", layer), ("fused", fused)):
+        def run():
+            L.kept_idx.copy_(idx0)
+            L.kept_cnt.copy_(cnt0)
+            L.refine()
+        run()
+        res[name] = time_events(run, reps)
+    same = all(torch.equal(getattr(layer, f), getattr(fused, f))
+               for f in ("kept_idx", "kept_cnt", "J_init", "J_final"))
+    layer.kept_idx.copy_(idx0)
+    layer.kept_cnt.copy_(cnt0)
+    layer.refine()
+    res["identical"] = bool(same)
+    res["note"] = "includes restoring the top-k lists before each call"
+    return res
 
 
 def cpu_baseline(w, x, idx, cnt, budget_s=15.0):
@@ -248,6 +295,7 @@ def main():
     cnt = layer.kept_cnt.cpu().numpy()
     kf = kept_flops(w, idx, cnt)
     stages = stage_breakdown(layer, qkv, out, max(3, args.steps // 2))
+    refine_paths = refine_paths_ms(w, x, shape, layer, max(3, args.steps // 2))
     attn_ms = time_events(lambda: layer.attend(q, k, v, out), args.steps)
 
     import block_sparse_global_amd as bsg
@@ -276,7 +324,7 @@ def main():
         # 8 / 32 / 100 views (the headline lines) and 200 views with both
         # scores; each line: layer time, dense time, the attention kernel alone
         lines = [("views8", None), ("views32", None), ("views100", None),
-                 ("views100", "cdf"), ("views100-k64", None),
+                 ("views100", "cdf"), ("views100", "hess"), ("views100-k64", None),
                  ("views200", "prob"), ("views200", "drift")]
         x200 = None
         for name, mode in lines:
@@ -290,11 +338,14 @@ def main():
                     import synth
                     x200 = synth.make_inputs(synth.get_workload(name))
                 # "cdf": probability score, cumulative threshold CDF_TAU with
-                # the workload's budget as the cap
+                # the workload's budget as the cap. "hess": per-head budgets
+                # from head scores (the HeSS allocation), same total budget
+                x_in = x200 if name == "views200" else None
+                if mode == "hess":
+                    x_in = hess_inputs(name)
                 w2, x2, shape2, layer2, (q2, k2, v2), out2 = setup(
-                    name, "prob" if mode == "cdf" else mode,
-                    x200 if name == "views200" else None,
-                    tau=CDF_TAU if mode == "cdf" else None)
+                    name, "prob" if mode == "cdf" else (None if mode == "hess" else mode),
+                    x_in, tau=CDF_TAU if mode == "cdf" else None)
                 for _ in range(2):
                     layer2(q2, k2, v2, out2)
                 reps = 3 if name == "views200" else 10
@@ -309,6 +360,8 @@ def main():
                 sweep[key] = {"layer_ms": l_ms, "dense_ms": d_ms, "attn_ms": a_ms,
                               "select_ms": s_ms, "kept_flop": kf2,
                               "realised_sparsity": sparsity_of(w2, cnt2)}
+                if mode == "hess":
+                    sweep[key]["keep_per_head"] = [int(b) for b in x2["keep"]]
                 del layer2, q2, k2, v2, out2, d2
                 torch.cuda.empty_cache()
             e = sweep[key]
@@ -353,6 +406,7 @@ def main():
         "kept_flop": kf,
         "realised_sparsity": sparsity_of(w, cnt),
         "stages_ms": stages,
+        "refine_paths_ms": refine_paths,
         "views_sweep": sweep,
         "residual_drift": drift_report,
     }

@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     ress_head_budgets,
     ress_last_error,
     ress_refine_dropset,
+    ress_refine_dropset_fused,
+    REFINE_FUSED_MAX_BLOCKS,
     ress_refine_workspace_size,
     ress_residual_drift,
     ress_select_topk,

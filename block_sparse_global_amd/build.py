@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libress.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.hip", "pool.hip", "score.hip", "select.hip", "refine.hip", "attn.hip", "gram.hip", "drift.hip"]
+SOURCES = ["api.hip", "pool.hip", "score.hip", "select.hip", "refine.hip", "refine_fused.hip",
+           "attn.hip", "gram.hip", "drift.hip"]
 ARCH = "gfx950"
 
 

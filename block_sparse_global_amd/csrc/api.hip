@@ -283,6 +283,40 @@ int ress_refine_dropset(const double* P, const double* key,
   return hip_status(e, "refine launch");
 }
 
+int ress_refine_dropset_fused(const double* P, const double* key, const double* vpool,
+                              const double* vout, const double* M, ress_shape shape,
+                              const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                              double rho, double eps, int32_t k_max, int32_t* kept_idx,
+                              int32_t* kept_cnt, double* J_init, double* J_final,
+                              void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if (ress::n_kblocks(shape) > ress::refine_fused_max_blocks())
+    return fail(RESS_ERR_UNSUPPORTED, "n_k=%d key blocks exceed the %d of the fused refinement",
+                ress::n_kblocks(shape), ress::refine_fused_max_blocks());
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(key);
+  REQUIRE_PTR(vpool);
+  REQUIRE_PTR(vout);
+  OPTIONAL_PTR(M);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  OPTIONAL_PTR(J_init);
+  OPTIONAL_PTR(J_final);
+  if (rounds < 0) return fail(RESS_ERR_INVALID_ARG, "rounds=%d < 0", rounds);
+  if (!(rho > 0.0 && rho <= 1.0))
+    return fail(RESS_ERR_INVALID_ARG, "rho must lie in (0, 1]");
+  if (!(eps > 0.0) || !isfinite(eps))
+    return fail(RESS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK)
+    return rc;
+  hipError_t e = ress::launch_refine_fused(P, key, vpool, vout, M, shape, cfg, rounds, rho, eps,
+                                           k_max, kept_idx, kept_cnt, J_init, J_final,
+                                           static_cast<hipStream_t>(stream));
+  return hip_status(e, "fused refine launch");
+}
+
 size_t ress_refine_workspace_size(ress_shape shape) {
   if (check_shape(shape) != RESS_OK) return 0;
   ok();

@@ -98,6 +98,15 @@ hipError_t launch_refine(const double* P, const double* key,
 // rows of all heads, in HBM).
 size_t refine_workspace_bytes(const ress_shape& s);
 
+// The same refinement with every round of a tile of rows on chip (no
+// workspace); rows of at most refine_fused_max_blocks() key blocks.
+hipError_t launch_refine_fused(const double* P, const double* key, const double* vpool,
+                               const double* vout, const double* M, const ress_shape& s,
+                               const SelConfig& cfg, int32_t rounds, double rho, double eps,
+                               int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
+                               double* J_init, double* J_final, hipStream_t st);
+int refine_fused_max_blocks();
+
 hipError_t launch_gram(const void* w_o, int dtype, int d_model, const ress_shape& s, double* M,
                        hipStream_t st);
 

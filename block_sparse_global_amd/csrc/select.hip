@@ -31,6 +31,7 @@ struct SelShared {
   uint32_t hist[256];
   int32_t wave_tot[kWaves];
   double red[kWaves];
+  uint64_t and_[kWaves], or_[kWaves];
   int32_t digit, above, at_digit;
 };
 
@@ -95,9 +96,38 @@ __device__ uint32_t select_top(const uint64_t (&u)[E], uint32_t member, int m,
   uint32_t inplay = member;
   if (m <= 0) return 0u;
   int need = m;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (;;) {
+    // the bits every key still in play shares: the digit of this pass is
+    // the 8 bits just below that common prefix, so no pass is spent on
+    // digits that cannot separate the keys (the leading bits of float64
+    // keys in a narrow range are all equal)
+    uint64_t all1 = ~0ull, any1 = 0ull;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((inplay >> e) & 1u) {
+        all1 &= u[e];
+        any1 |= u[e];
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      all1 &= (uint64_t)__shfl_xor((long long)all1, o, 64);
+      any1 |= (uint64_t)__shfl_xor((long long)any1, o, 64);
+    }
+    if ((t & 63) == 0) {
+      sh.and_[t >> 6] = all1;
+      sh.or_[t >> 6] = any1;
+    }
     for (int k = t; k < 256; k += kThreads) sh.hist[k] = 0u;
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      all1 &= sh.and_[k];
+      any1 |= sh.or_[k];
+    }
+    const uint64_t diff = all1 ^ any1;
+    if (diff == 0ull) break;  // the keys in play are all equal
+    const int top = 63 - __clzll((long long)diff);
+    const int shift = top >= 7 ? top - 7 : 0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if ((inplay >> e) & 1u)

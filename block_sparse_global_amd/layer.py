@@ -15,12 +15,14 @@ import numpy as np
 import torch
 
 from ._lib import (
+    REFINE_FUSED_MAX_BLOCKS,
     RESS_SCORE_DRIFT,
     RESS_SCORE_PROB,
     Shape,
     ress_block_pool,
     ress_block_score,
     ress_refine_dropset,
+    ress_refine_dropset_fused,
     ress_refine_workspace_size,
     ress_select_cdf,
     ress_select_topk,
@@ -32,10 +34,17 @@ class BlockSparseGlobalAttention:
     def __init__(self, shape: Shape, keep, always_keep, mode: str = "prob",
                  rounds: int = 0, rho: float = 0.5, eps: float = 1e-4,
                  scale: Optional[float] = None, M: Optional[torch.Tensor] = None,
-                 device="cuda", with_lse: bool = False, tau: Optional[float] = None):
+                 device="cuda", with_lse: bool = False, tau: Optional[float] = None,
+                 refine_impl: str = "rounds"):
         """``tau`` switches the selection from top-k to the cumulative
         probability threshold (ress_select_cdf, probability scoring only; the
-        budget ``keep`` is then the cap)."""
+        budget ``keep`` is then the cap). ``refine_impl``: "rounds"
+        (ress_refine_dropset, kernels per round and a workspace; the faster
+        one on the MI355X) or "fused" (ress_refine_dropset_fused, one kernel,
+        no workspace, rows of at most REFINE_FUSED_MAX_BLOCKS key blocks);
+        both give the same bits."""
+        if refine_impl not in ("fused", "rounds"):
+            raise ValueError(refine_impl)
         if mode not in ("prob", "drift"):
             raise ValueError(mode)
         if rounds > 0 and mode != "drift":
@@ -68,8 +77,13 @@ class BlockSparseGlobalAttention:
         self.kept_cnt = torch.empty((H, nq), dtype=torch.int32, device=device)
         self.J_init = torch.empty((H, nq), **f64) if rounds > 0 else None
         self.J_final = torch.empty((H, nq), **f64) if rounds > 0 else None
+        if refine_impl == "fused" and rounds > 0 and nk > REFINE_FUSED_MAX_BLOCKS:
+            raise ValueError(f"the fused refinement takes rows of at most "
+                             f"{REFINE_FUSED_MAX_BLOCKS} key blocks (n_k={nk})")
+        self.refine_impl = refine_impl
         self.workspace = (torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
-                                      device=device) if rounds > 0 else None)
+                                      device=device)
+                          if rounds > 0 and refine_impl == "rounds" else None)
         self.lse = (torch.empty((H, Np), dtype=torch.float32, device=device)
                     if with_lse else None)
         self.out = None
@@ -96,6 +110,12 @@ class BlockSparseGlobalAttention:
 
     def refine(self, stream=None):
         if self.rounds <= 0:
+            return
+        if self.refine_impl == "fused":
+            ress_refine_dropset_fused(self.P, self.key, self.vpool, self.vout, self.M,
+                                      self.shape, self.keep, self.always, self.rounds,
+                                      self.rho, self.eps, self.k_max, self.kept_idx,
+                                      self.kept_cnt, self.J_init, self.J_final, stream)
             return
         ress_refine_dropset(self.P, self.key, self.vpool, self.vout, self.M, self.shape,
                             self.keep, self.always, self.rounds, self.rho, self.eps,

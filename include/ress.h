@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RESS_VERSION 2
+#define RESS_VERSION 3
 
 /* Status codes. */
 #define RESS_OK 0
@@ -210,6 +210,27 @@ int ress_refine_dropset(const double* P, const double* key,
                         double eps, int32_t k_max, int32_t* kept_idx,
                         int32_t* kept_cnt, double* J_init, double* J_final,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ress_refine_dropset_fused — the same refinement as ress_refine_dropset
+ * (same arguments apart from the workspace, same results bit for bit),
+ * with the whole of it in one kernel: a workgroup takes 16 consecutive
+ * query-block rows of one head through the starting state, every round and
+ * the final keep lists, holding the gains, the current and best drop sets
+ * and the row state on chip (the fused restoration kernel of ReSS Appendix
+ * E). Only the keep lists and J_init / J_final are written to device memory;
+ * no workspace. Returns RESS_ERR_UNSUPPORTED when n_k > 1088 (a row's gains
+ * must fit in the workgroup's LDS); ress_refine_dropset covers those shapes.
+ * On the MI355X the per-round call is the faster of the two (one such
+ * workgroup fills a CU's LDS, which leaves its latency-bound per-row steps
+ * nothing to overlap with); this one needs no workspace.
+ */
+int ress_refine_dropset_fused(const double* P, const double* key, const double* vpool,
+                              const double* vout, const double* M, ress_shape shape,
+                              const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                              double rho, double eps, int32_t k_max, int32_t* kept_idx,
+                              int32_t* kept_cnt, double* J_init, double* J_final,
+                              void* stream);
 
 /*
  * ress_refine_workspace_size — bytes of device workspace that

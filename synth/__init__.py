@@ -20,5 +20,6 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_inputs,
     make_gram,
+    make_head_scores,
     make_wo,
 )

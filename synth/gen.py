@@ -147,6 +147,15 @@ def make_wo(heads: int, head_dim: int = 64, d_model: int = 1024, seed: int = 2,
     return f32_to_bf16_bits(w)
 
 
+def make_head_scores(heads: int, seed: int = 3, sigma: float = 0.5):
+    """Random per-head importance scores, float64 [heads], log-normal
+    exp(N(0, sigma^2)). Stand in for calibrated head scores (a Fisher trace
+    per head over a calibration set), which need trained weights and data that
+    do not exist here."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.standard_normal(heads) * sigma)
+
+
 def make_gram(heads: int, head_dim: int = 64, width: int = 1024, seed: int = 1):
     """Random symmetric positive semi-definite matrices [H][D][D], float64.
 

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_every_call():
     names = declared_functions()
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk", "ress_select_cdf",
-              "ress_refine_dropset", "ress_refine_workspace_size", "ress_sparse_attn_fwd",
+              "ress_refine_dropset", "ress_refine_dropset_fused", "ress_refine_workspace_size",
+              "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
               "ress_last_error", "ress_version"):
         assert f in names
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(b.LIB_PATH)
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in ress.h but not exported"
-    assert b.ress_version() == 2
+    assert b.ress_version() == 3
     assert set(b.ENTRY_POINTS) == set(declared_functions())
 
 
@@ -193,6 +194,30 @@ def test_refine_workspace_checks():
     assert "256-byte" in b.ress_last_error()
     assert L.ress_refine_dropset(*args, FAKE, need - 1, None) == -1      # too small
     assert "smaller" in b.ress_last_error()
+
+
+def test_fused_refine_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    d = ctypes.c_double
+    _, keep = _arr([2, 3], np.int32)
+    _, alw = _arr([0, 0, 0, 1], np.uint8)
+
+    def call(s, P=FAKE, keep=keep, alw=alw, rounds=2, rho=0.5, eps=1e-4, k_max=3):
+        return L.ress_refine_dropset_fused(P, FAKE, FAKE, FAKE, None, s, keep, alw, rounds,
+                                           d(rho), d(eps), k_max, FAKE, FAKE, None, None, None)
+    # rows longer than the fused kernel's LDS holds: unsupported, nothing launched
+    long = _shape(H=1, N=1089 * 64, N_pad=1089 * 64)
+    _, keep1 = _arr([2], np.int32)
+    assert call(long, keep=keep1, alw=None) == -2
+    assert "1088" in b.ress_last_error()
+    s = _shape(H=2)  # n = 4
+    assert call(s, P=None) == -1 and "P" in b.ress_last_error()
+    assert call(s, rounds=-1) == -1 and "rounds" in b.ress_last_error()
+    assert call(s, rho=0.0) == -1 and "rho" in b.ress_last_error()
+    assert call(s, eps=0.0) == -1 and "eps" in b.ress_last_error()
+    assert call(s, k_max=2) == -1                     # k_max below a budget
+    assert b.REFINE_FUSED_MAX_BLOCKS == 1088
 
 
 def test_error_string_is_cleared_per_thread():

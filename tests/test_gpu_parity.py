@@ -442,6 +442,56 @@ def test_block64_bf16_drift_with_gram_and_refine():
     assert np.mean(g["J_final"] / g["J_init"]) < 1.0
 
 
+def _fused_case(name):
+    if name in ("views100", "views8-k64"):
+        return case_inputs(name) + (None,)
+    if name == "gram":  # block 64, 4 rounds at rho = 1 with a Gram matrix
+        w, x = _small(name="fg", views=4, patches_per_view=300, specials_per_view=5, heads=2,
+                      block=64, sparsity=(0.5, 0.5), score="drift", rounds=4, rho=1.0)
+        return w, x, synth.make_gram(w.heads, w.head_dim)
+    if name == "max1088":  # the longest fused rows; head 0 keeps every block (no swaps)
+        w, x = _small(name="f1088", views=1, patches_per_view=1088 * 64, heads=2, block=64,
+                      sparsity=(0.0, 0.97), score="drift", rounds=3)
+        assert w.n_kblocks == 1088 and x["keep"][0] == 1088
+        return w, x, None
+    if name == "short":  # one 64-block word per row, swaps dying out over 5 rounds
+        w, x = _small(name="fs", views=2, patches_per_view=500, specials_per_view=5, heads=3,
+                      block=64, sparsity=(0.4, 0.8), score="drift", rounds=5)
+        return w, x, None
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["views100", "views8-k64", "gram", "max1088", "short"])
+def test_fused_refine_matches_per_round_kernels(name):
+    """ress_refine_dropset_fused (one kernel, each tile of 16 rows on chip for
+    every round) against ress_refine_dropset (kernels per round): the same
+    keep lists and the same J_init / J_final, bit for bit."""
+    b = _lib()
+    w, x, M = _fused_case(name)
+    print(f"\n[fused-refine] {name}: n_k={w.n_kblocks} n_q={w.n_blocks} H={w.heads} "
+          f"rounds={w.rounds}", flush=True)
+    shape = b.Shape(*w.shape_args())
+    Mt = torch.from_numpy(M).cuda() if M is not None else None
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    res = {}
+    for impl in ("rounds", "fused"):
+        layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode="drift",
+                                             rounds=w.rounds, rho=w.rho, M=Mt,
+                                             refine_impl=impl)
+        layer.pool(q, k, v)
+        layer.score()
+        layer.select()
+        layer.refine()
+        torch.cuda.synchronize()
+        res[impl] = [a.cpu().numpy() for a in (layer.kept_idx, layer.kept_cnt, layer.J_init,
+                                               layer.J_final)]
+        del layer
+    for a, c, what in zip(res["rounds"], res["fused"], ("kept_idx", "kept_cnt", "J_init",
+                                                        "J_final")):
+        assert np.array_equal(a, c), f"{what} differs"
+    assert np.all(res["fused"][3] <= res["fused"][2])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_gram_from_wo_feeds_the_drift_score(dtype):
     """Eq. 8 on the GPU from a 1024 x (16*64) projection, then the drift key

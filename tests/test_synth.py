@@ -100,3 +100,21 @@ def test_tiny_inputs_digest():
 
 
 DIGEST_TINY = "212f3e1bad2de40c"
+
+
+def test_head_scores_and_hess_budget_line():
+    # stand-in head scores: positive, seeded, reproducible
+    s = synth.make_head_scores(16)
+    assert s.shape == (16,) and np.all(s > 0)
+    assert np.array_equal(s, synth.make_head_scores(16))
+    # the bench line's budgets keep the workload's total and lie within the
+    # cap, ordered like the scores (proportional allocation)
+    import bench
+    w = synth.get_workload("views100")
+    x = bench.hess_inputs("views100")
+    base = synth.make_inputs(w)["keep"]
+    assert int(x["keep"].sum()) == int(base.sum())
+    n_alw = int(x["always"].sum())
+    assert np.all(x["keep"] >= n_alw + 1) and np.all(x["keep"] <= w.n_kblocks)
+    order = np.argsort(-s, kind="stable")
+    assert np.all(np.diff(x["keep"][order]) <= 0)
