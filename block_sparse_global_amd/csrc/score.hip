@@ -180,24 +180,42 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
   const double* Ph = P + (size_t)h * nq * nk;
   const double* Vh = vpool + (size_t)h * nk * kD;
   f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+  // chunks of 64 key blocks: P 32 rows x 64 blocks (8 per thread), V 64
+  // blocks x 64 dims (16 per thread); the next chunk's loads are in flight
+  // in registers while the current chunk's products run
+  constexpr int kPE = kVR * kVJ / kThreads, kVE = kVJ * kD / (2 * kThreads);
+  double pr[kPE], vx[kVE], vy[kVE];
+#define RESS_VOUT_LOAD_CHUNK(JC)                                               \
+  do {                                                                         \
+    _Pragma("unroll") for (int e = 0; e < kPE; ++e) {                          \
+      const int idx = tid + e * kThreads;                                      \
+      const int i = min(i0 + (idx >> 6), nq - 1), j = (JC) + (idx & 63);       \
+      const double x = Ph[(size_t)i * nk + min(j, nk - 1)];                    \
+      pr[e] = j < nk ? x : 0.0;                                                \
+    }                                                                          \
+    _Pragma("unroll") for (int e = 0; e < kVE; ++e) {                          \
+      const int idx = tid + e * kThreads;                                      \
+      const int j = min((JC) + (idx >> 5), nk - 1);                            \
+      const double2 v2 = reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[idx & 31]; \
+      vx[e] = v2.x;                                                            \
+      vy[e] = v2.y;                                                            \
+    }                                                                          \
+  } while (0)
+  RESS_VOUT_LOAD_CHUNK(0);
   for (int jc = 0; jc < nk; jc += kVJ) {
-    // P: 32 rows x 64 blocks (8 per thread); V: 64 blocks x 64 dims (16 per thread)
 #pragma unroll
-    for (int e = 0; e < kVR * kVJ / kThreads; ++e) {
+    for (int e = 0; e < kPE; ++e) {
       const int idx = tid + e * kThreads;
-      const int r = idx >> 6, c = idx & 63;
-      const int i = min(i0 + r, nq - 1), j = jc + c;
-      Ps[r][c] = j < nk ? Ph[(size_t)i * nk + j] : 0.0;
+      Ps[idx >> 6][idx & 63] = pr[e];
     }
 #pragma unroll
-    for (int e = 0; e < kVJ * kD / (2 * kThreads); ++e) {
+    for (int e = 0; e < kVE; ++e) {
       const int idx = tid + e * kThreads;
-      const int r = idx >> 5, c2 = idx & 31;
-      const int j = min(jc + r, nk - 1);
-      *reinterpret_cast<double2*>(&Vs[r][2 * c2]) =
-          reinterpret_cast<const double2*>(Vh + (size_t)j * kD)[c2];
+      *reinterpret_cast<double2*>(&Vs[idx >> 5][2 * (idx & 31)]) = double2{vx[e], vy[e]};
     }
     __syncthreads();
+    // (after the last chunk this reloads valid clamped rows, unused)
+    RESS_VOUT_LOAD_CHUNK(jc + kVJ);
 #pragma unroll 4
     for (int s4 = 0; s4 < kVJ / 4; ++s4) {
       const int k = 4 * s4 + (l >> 4);
@@ -218,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
         vout[((size_t)h * nq + i) * kD + dt + 16 * t + (l & 15)] = acc[t][r];
   }
 }
+#undef RESS_VOUT_LOAD_CHUNK
 
 // Drift key of one 64 x 64 tile: w_i = M vout_i (vout_i when M is NULL) is
 // formed while staging, a_i = vout_i . w_i, then per (i, j)
