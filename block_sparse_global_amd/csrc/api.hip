@@ -158,13 +158,17 @@ int ress_block_pool(const void* q, const void* k, const void* v, int dtype,
   }
   if (given == 0) return fail(RESS_ERR_INVALID_ARG, "nothing to pool");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int a = 0; a < 3; ++a) {
-    if (in[a] == nullptr) continue;
-    // queries in blocks of B, keys and values in blocks of Bk
-    const int blk = a == 0 ? shape.B : ress::key_block(shape);
-    const int nb = a == 0 ? ress::n_qblocks(shape) : ress::n_kblocks(shape);
-    hipError_t e = ress::launch_block_pool(in[a], dtype, shape, blk, nb, out[a], st);
+  // queries in blocks of B, keys and values in blocks of Bk: one launch per
+  // distinct block size (a single one on square grids)
+  const int blk[3] = {shape.B, ress::key_block(shape), ress::key_block(shape)};
+  const int nb[3] = {ress::n_qblocks(shape), ress::n_kblocks(shape), ress::n_kblocks(shape)};
+  for (const int size : {shape.B, ress::key_block(shape)}) {
+    ress::PoolJobs jobs{};
+    for (int a = 0; a < 3; ++a)
+      if (in[a] != nullptr && blk[a] == size) jobs.job[jobs.count++] = {in[a], out[a], nb[a]};
+    hipError_t e = ress::launch_block_pool(jobs, dtype, shape, size, st);
     if (e != hipSuccess) return hip_status(e, "block_pool launch");
+    if (size == ress::key_block(shape)) break;  // square grid: one size only
   }
   return ok();
 }

@@ -29,14 +29,19 @@ __device__ inline void load8(const float* p, double (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// One workgroup per (head, block). Thread t reads dims 8*(t%8)..+7 of the
-// rows lo + t/8, lo + t/8 + 32, ...; the 32 row groups are then summed per
-// dim in ascending order.
+// One workgroup per (block, head, tensor): blockIdx.z picks one of up to
+// three tensors pooled in the same launch (the grid covers the largest block
+// count; workgroups past a tensor's own count return). Thread t reads dims
+// 8*(t%8)..+7 of the rows lo + t/8, lo + t/8 + 32, ...; the 32 row groups
+// are then summed per dim in ascending order.
 template <typename T, int BLK>
-__global__ __launch_bounds__(kThreads) void pool_kernel(
-    const T* __restrict__ x, double* __restrict__ out, int N, int N_pad,
-    int n) {
+__global__ __launch_bounds__(kThreads) void pool_kernel(PoolJobs jobs, int N, int N_pad) {
+  const PoolJob job = jobs.job[blockIdx.z];
+  const int n = job.nb;
   const int b = blockIdx.x;
+  if (b >= n) return;
+  const T* __restrict__ x = static_cast<const T*>(job.x);
+  double* __restrict__ out = job.out;
   const int h = blockIdx.y;
   const int t = threadIdx.x;
   const int chunk = t & 7;
@@ -79,25 +84,24 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(
 }
 
 template <typename T>
-hipError_t launch_t(const T* x, const ress_shape& s, int blk, int nb, double* out,
-                    hipStream_t st) {
-  dim3 grid(nb, s.H);
+hipError_t launch_t(const PoolJobs& jobs, const ress_shape& s, int blk, hipStream_t st) {
+  int nb_max = 0;
+  for (int a = 0; a < jobs.count; ++a) nb_max = max(nb_max, jobs.job[a].nb);
+  dim3 grid(nb_max, s.H, jobs.count);
   if (blk == 128)
-    hipLaunchKernelGGL((pool_kernel<T, 128>), grid, dim3(kThreads), 0, st, x,
-                       out, s.N, s.N_pad, nb);
+    hipLaunchKernelGGL((pool_kernel<T, 128>), grid, dim3(kThreads), 0, st, jobs, s.N, s.N_pad);
   else
-    hipLaunchKernelGGL((pool_kernel<T, 64>), grid, dim3(kThreads), 0, st, x,
-                       out, s.N, s.N_pad, nb);
+    hipLaunchKernelGGL((pool_kernel<T, 64>), grid, dim3(kThreads), 0, st, jobs, s.N, s.N_pad);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
-                             int blk, int nb, double* out, hipStream_t st) {
-  if (dtype == RESS_DTYPE_BF16)
-    return launch_t(static_cast<const uint16_t*>(x), s, blk, nb, out, st);
-  return launch_t(static_cast<const float*>(x), s, blk, nb, out, st);
+hipError_t launch_block_pool(const PoolJobs& jobs, int dtype, const ress_shape& s, int blk,
+                             hipStream_t st) {
+  if (jobs.count <= 0) return hipSuccess;
+  if (dtype == RESS_DTYPE_BF16) return launch_t<uint16_t>(jobs, s, blk, st);
+  return launch_t<float>(jobs, s, blk, st);
 }
 
 }  // namespace ress

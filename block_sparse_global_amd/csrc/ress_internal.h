@@ -59,10 +59,20 @@ __device__ inline void wave_lds_sync() {
 
 // Launchers (defined next to their kernels). Each returns hipGetLastError()
 // of its launches.
-// Pools x in blocks of `blk` tokens (nb blocks, the last one partial when
-// N is not a multiple of blk).
-hipError_t launch_block_pool(const void* x, int dtype, const ress_shape& s,
-                             int blk, int nb, double* out, hipStream_t st);
+// Pools up to three tensors of one dtype in blocks of `blk` tokens in one
+// launch; job a has nb blocks (the last one partial when N is not a
+// multiple of blk).
+struct PoolJob {
+  const void* x;
+  double* out;
+  int nb;
+};
+struct PoolJobs {
+  PoolJob job[3];
+  int count;
+};
+hipError_t launch_block_pool(const PoolJobs& jobs, int dtype, const ress_shape& s, int blk,
+                             hipStream_t st);
 
 hipError_t launch_block_map(const double* qpool, const double* kpool,
                             const ress_shape& s, double scale, double* P,
