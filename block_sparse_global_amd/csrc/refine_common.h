@@ -4,6 +4,8 @@
 // select over 64-bit order keys.
 #pragma once
 
+#include <type_traits>
+
 #include "ress_internal.h"
 
 namespace ress {
@@ -90,16 +92,20 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
   // keys per lane: KPL, or the row's 64-block words when they are in LDS
   const int kK = KPL > 0 ? KPL : (n + 63) >> 6;
   constexpr int kU = KPL > 0 ? KPL : 4;  // unroll factor of the per-key loops
-  uint64_t selected = 0, inplay = member;
+  // per-lane membership masks over k: 32 bits hold up to 32 keys per lane
+  using Mask = typename std::conditional<(KPL > 0 && KPL <= 32), uint32_t, uint64_t>::type;
+  Mask selected = 0, inplay = (Mask)member;
   int need = m;
-  for (;;) {
-    uint64_t all1 = ~0ull, any1 = 0ull;
+  // AND and OR of the keys in play; each pass's update loop forms those of
+  // the next pass
+  uint64_t all1 = ~0ull, any1 = 0ull;
 #pragma unroll kU
-    for (int k = 0; k < kK; ++k)
-      if ((inplay >> k) & 1ull) {
-        all1 &= key(k);
-        any1 |= key(k);
-      }
+  for (int k = 0; k < kK; ++k)
+    if ((inplay >> k) & 1u) {
+      all1 &= key(k);
+      any1 |= key(k);
+    }
+  for (;;) {
     const uint64_t diff = wave_and64(all1) ^ wave_or64(any1);
     if (diff == 0ull) break;  // the keys in play are all equal
     const int top = 63 - __clzll((long long)diff);
@@ -108,7 +114,7 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
     wave_lds_sync();
 #pragma unroll kU
     for (int k = 0; k < kK; ++k)
-      if ((inplay >> k) & 1ull) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
+      if ((inplay >> k) & 1u) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
     wave_lds_sync();
     int c[4];
     int s = 0;
@@ -144,27 +150,35 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
     above = __shfl(above, src, 64);
     atd = __shfl(atd, src, 64);
     wave_lds_sync();
+    all1 = ~0ull;
+    any1 = 0ull;
 #pragma unroll kU
     for (int k = 0; k < kK; ++k) {
-      if ((inplay >> k) & 1ull) {
-        const int dig = (int)((uint32_t)(key(k) >> shift) & 255u);
-        if (dig > dsel) selected |= 1ull << k;
-        if (dig != dsel) inplay &= ~(1ull << k);
+      if ((inplay >> k) & 1u) {
+        const uint64_t kv = key(k);
+        const int dig = (int)((uint32_t)(kv >> shift) & 255u);
+        if (dig > dsel) selected |= (Mask)1 << k;
+        if (dig != dsel) {
+          inplay &= ~((Mask)1 << k);
+        } else {
+          all1 &= kv;
+          any1 |= kv;
+        }
       }
     }
     need -= above;
-    if (atd == need) return selected | inplay;
+    if (atd == need) return (uint64_t)(selected | inplay);
   }
   // equal keys remain: take the lowest `need` block indices (k-major order)
   const uint64_t below = (1ull << lane) - 1ull;
   int taken = 0;
   for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
-    const bool b = (inplay >> k) & 1ull;
+    const bool b = (inplay >> k) & 1u;
     const uint64_t mask = __ballot(b);
-    if (b && taken + __popcll(mask & below) < need) selected |= 1ull << k;
+    if (b && taken + __popcll(mask & below) < need) selected |= (Mask)1 << k;
     taken += __popcll(mask);
   }
-  return selected;
+  return (uint64_t)selected;
 }
 
 }  // namespace ress
