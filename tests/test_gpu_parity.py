@@ -133,6 +133,38 @@ def test_pool(case):
         assert np.all(d <= tol), f"{t}: max abs diff {d.max():.3e}"
 
 
+@pytest.mark.parametrize("key_block", [0, 64])
+def test_pool_any_subset_of_tensors_in_one_call(key_block):
+    """ress_block_pool launches the tensors of one block size together; every
+    subset of (q, k, v) gives the same pooled blocks as all three at once."""
+    b = _lib()
+    w, x = _small(name="ps", views=3, patches_per_view=300, specials_per_view=5, heads=2,
+                  block=128, key_block=key_block)
+    shape = b.Shape(*w.shape_args())
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    f64d = dict(dtype=torch.float64, device="cuda")
+
+    def pooled(use):
+        outs = [torch.full((w.heads, shape.nq, 64), np.nan, **f64d),
+                torch.full((w.heads, shape.nk, 64), np.nan, **f64d),
+                torch.full((w.heads, shape.nk, 64), np.nan, **f64d)]
+        ins = (q, k, v)
+        b.ress_block_pool(*(ins[a] if a in use else None for a in range(3)), shape,
+                          *(outs[a] if a in use else None for a in range(3)))
+        torch.cuda.synchronize()
+        return [o.cpu().numpy() for o in outs]
+
+    full = pooled((0, 1, 2))
+    assert all(np.isfinite(o).all() for o in full)
+    for use in ((0,), (1,), (2,), (0, 1), (1, 2), (0, 2)):
+        got = pooled(use)
+        for a in range(3):
+            if a in use:
+                assert np.array_equal(got[a], full[a]), (use, a)
+            else:
+                assert np.isnan(got[a]).all(), (use, a)  # untouched
+
+
 def test_block_map(case):
     name, mode, w, x, g, ref = case
     _close(g["P"], ref["P"], 1e-12, "P")
