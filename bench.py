@@ -52,6 +52,22 @@ ATTN_TRAFFIC = {
 }
 
 
+# The pages' own speed figures, for context only: whole-model forward times
+# of VGGT on NVIDIA GPUs (every layer, not the attention call alone), so not
+# comparable with the attention-layer speedups measured here.
+PAGES_CONTEXT = [
+    {"what": "SparseVGGT vs dense VGGT forward, 100 views, sparsity 0.745",
+     "speedup": round(10.47 / 7.58, 2), "seconds": [10.47, 7.58], "hardware": "RTX 4090",
+     "source": "ReSS page, Table 1 (cost analysis) and Table S7 (dense latency)"},
+    {"what": "ReSS selection (drift score + 5 fused restoration rounds) added to that forward",
+     "seconds_added": 0.24, "seconds_added_unfused": 1.26, "hardware": "RTX 4090",
+     "source": "ReSS page, Table 1 (cost analysis)"},
+    {"what": "VASC vs dense VGGT forward, NRGBD stride-10 sequences, 85% sparsity",
+     "speedup": 2.29, "seconds": [15.631, 6.822], "hardware": "RTX 4090",
+     "source": "VASC page, Table 2 (full-model efficiency on NeuralRGB-D)"},
+]
+
+
 def _valid_tokens(N, blk, nb):
     valid = np.full(nb, blk, dtype=np.int64)
     valid[-1] = N - (nb - 1) * blk
@@ -409,6 +425,7 @@ def main():
         "refine_paths_ms": refine_paths,
         "views_sweep": sweep,
         "residual_drift": drift_report,
+        "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, idx, cnt)
