@@ -25,9 +25,9 @@
 // order, so the two paths give identical bits. The gains of a row must fit
 // in LDS: n_k <= 1088 key blocks.
 //
-// On the MI355X this path is slower than the per-round kernels (1.66 ms
-// against 1.07 ms for 16 heads x 1074 rows x 1074 blocks, 3 rounds): the
-// 157 KB of LDS a tile needs leaves one workgroup per CU, so its
+// On the MI355X this path is slower than the per-round kernels (about
+// 1.7 ms against 1.07 ms for 16 heads x 1074 rows x 1074 blocks, 3 rounds): the
+// 159 KB of LDS a tile needs leaves one workgroup per CU, so its
 // latency-bound per-row steps (the selects, the gathers of the swapped
 // blocks) run with nothing to overlap them, while the per-round kernels
 // keep many workgroups in flight on every CU. It stays as the workspace-free
@@ -42,6 +42,11 @@ constexpr int kRows = 16;               // rows per workgroup = waves
 constexpr int kFThreads = 64 * kRows;
 constexpr int kMaxWords = 17;           // 64-block words per row: n_k <= 1088
 constexpr int kSlotBytes = 1024;        // per-wave scratch
+// LDS strides padded off multiples of 64 banks: the 16 rows' u vectors (read
+// together as matrix operands) and the gains rows (stored four rows at a
+// time) then spread over all banks
+constexpr int kSlotStride = kSlotBytes + 16;
+__host__ __device__ inline int gains_stride(int KW) { return 64 * KW + 16; }  // uint64 words
 constexpr int kChgCap = 128;            // change-list entries per flush
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -52,17 +57,17 @@ struct FusedRow {
 };
 
 // LDS layout for KW = ceil(n / 64) words per row, every region 16-byte
-// aligned (about 157 KB at KW = 17).
+// aligned (about 159 KB at KW = 17).
 struct FusedLds {
   size_t gains, cur, best, cand, slot, rs, total;
   static __host__ __device__ size_t a16(size_t b) { return (b + 15) & ~(size_t)15; }
   explicit __host__ __device__ FusedLds(int KW) {
     size_t off = 0;
-    gains = off; off += a16((size_t)kRows * 64 * KW * 8);  // order keys [kRows][64 KW]
+    gains = off; off += a16((size_t)kRows * gains_stride(KW) * 8);  // order keys [kRows][64 KW]
     cur = off;   off += a16((size_t)kRows * KW * 8);  // D bitmask: bit l of word k = block 64k+l
     best = off;  off += a16((size_t)kRows * KW * 8);  // best D bitmask
     cand = off;  off += a16((size_t)KW * 8);          // candidates: not always kept, j < n
-    slot = off;  off += (size_t)kRows * kSlotBytes;   // per wave: u or g [64] | histogram, changes
+    slot = off;  off += (size_t)kRows * kSlotStride;  // per wave: u or g [64] | histogram, changes
     rs = off;    off += (size_t)kRows * sizeof(FusedRow);
     total = off;
   }
@@ -120,11 +125,11 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
   const double* Prow = P + row * n;
   const double* Vh = vpool + (size_t)h * n * kD;
   const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;
-  unsigned char* slot = smem + L.slot + (size_t)w * kSlotBytes;
+  unsigned char* slot = smem + L.slot + (size_t)w * kSlotStride;
   double* ul = reinterpret_cast<double*>(slot);                 // u or g of this row [64]
   uint32_t* whist = reinterpret_cast<uint32_t*>(slot);          // histogram [256]
   int32_t* chg = reinterpret_cast<int32_t*>(slot + 512);        // changes [kChgCap]
-  uint64_t* myg = gains + (size_t)w * 64 * KW;
+  uint64_t* myg = gains + (size_t)w * gains_stride(KW);
   uint64_t* mycur = curw + (size_t)w * KW;
   uint64_t* mybest = bestw + (size_t)w * KW;
   const uint64_t below = (1ull << lane) - 1ull;
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
 
     // gains of the tile's rows: A = u (row c16, dims 4s + q4), B = V
     // (block 16t + c16, dims 4s + q4); result rows q4 + 4e, block 16t + c16
-    const double* ur = reinterpret_cast<const double*>(smem + L.slot + (size_t)c16 * kSlotBytes);
+    const double* ur = reinterpret_cast<const double*>(smem + L.slot + (size_t)c16 * kSlotStride);
     for (int t = w; t < n_tiles; t += kRows) {
       const int j = 16 * t + c16;
       const int jc = min(j, n - 1);
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
           const double Ku = st.K - p;
           dJ = (Ku > 0.0) ? st.J - (st.G + dG) / (Ku * Ku) : -INFINITY;
         }
-        if (i0 + rl < nq && j < n) gains[(size_t)rl * 64 * KW + j] = order_key(dJ);
+        if (i0 + rl < nq && j < n) gains[(size_t)rl * gains_stride(KW) + j] = order_key(dJ);
       }
     }
     __syncthreads();  // every gain of the tile is in LDS
