@@ -45,6 +45,9 @@ class BlockSparseGlobalAttention:
         both give the same bits."""
         if refine_impl not in ("fused", "rounds"):
             raise ValueError(refine_impl)
+        if refine_impl == "fused" and rounds > 0 and shape.nk > REFINE_FUSED_MAX_BLOCKS:
+            raise ValueError(f"the fused refinement takes rows of at most "
+                             f"{REFINE_FUSED_MAX_BLOCKS} key blocks (n_k={shape.nk})")
         if mode not in ("prob", "drift"):
             raise ValueError(mode)
         if rounds > 0 and mode != "drift":
@@ -77,9 +80,6 @@ class BlockSparseGlobalAttention:
         self.kept_cnt = torch.empty((H, nq), dtype=torch.int32, device=device)
         self.J_init = torch.empty((H, nq), **f64) if rounds > 0 else None
         self.J_final = torch.empty((H, nq), **f64) if rounds > 0 else None
-        if refine_impl == "fused" and rounds > 0 and nk > REFINE_FUSED_MAX_BLOCKS:
-            raise ValueError(f"the fused refinement takes rows of at most "
-                             f"{REFINE_FUSED_MAX_BLOCKS} key blocks (n_k={nk})")
         self.refine_impl = refine_impl
         self.workspace = (torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
                                       device=device)

@@ -220,6 +220,17 @@ def test_fused_refine_argument_checks():
     assert b.REFINE_FUSED_MAX_BLOCKS == 1088
 
 
+def test_layer_argument_checks_before_any_allocation():
+    import block_sparse_global_amd as b
+    s = b.Shape(1, 1089 * 64, 1089 * 64, 64, 64)
+    with pytest.raises(ValueError, match="1088"):
+        b.BlockSparseGlobalAttention(s, [2], None, mode="drift", rounds=1, refine_impl="fused")
+    with pytest.raises(ValueError):
+        b.BlockSparseGlobalAttention(s, [2], None, mode="drift", rounds=1, refine_impl="auto")
+    with pytest.raises(ValueError, match="drift"):
+        b.BlockSparseGlobalAttention(s, [2], None, mode="prob", rounds=1)
+
+
 def test_error_string_is_cleared_per_thread():
     import threading
     import block_sparse_global_amd as b
