@@ -21,6 +21,7 @@
 // accumulates their probabilities in rank order, one float64 addition at a
 // time, so the count matches a sequential scan bit for bit.
 #include "ress_internal.h"
+#include "refine_common.h"
 
 namespace ress {
 namespace {
@@ -241,6 +242,50 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
                 sh);
 }
 
+// One wave per row, four rows per workgroup, for rows of at most 64 KPL key
+// blocks: the row's keys as order keys in registers (block j = lane + 64k),
+// the exact per-wave radix select of the refinement (same tie rule: the
+// lower block index), no workgroup barriers. The keep list is the same as
+// topk_kernel's.
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(
+    const double* __restrict__ key, int nq, int n, SelConfig cfg, int k_max,
+    int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
+  __shared__ uint32_t whist[4][256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + w;
+  const int h = blockIdx.y;
+  if (i >= nq) return;  // whole wave; nothing below waits on other waves
+  const size_t row = (size_t)h * nq + i;
+  SelKeys<KPL> keys(reinterpret_cast<const uint64_t*>(key + row * n), n, lane);
+  uint64_t member = 0, always = 0;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const int j = lane + 64 * k;
+    keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
+    if (j < n) {
+      if (sel_always(cfg, j))
+        always |= 1ull << k;
+      else
+        member |= 1ull << k;
+    }
+  }
+  const int c = cfg.keep[h] - cfg.n_always;
+  const uint64_t kept = wave_select<KPL>(keys, member, n, c, whist[w]) | always;
+  int32_t* out = kept_idx + row * k_max;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0;
+  for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
+    const bool b = (kept >> k) & 1ull;
+    const uint64_t msk = __ballot(b);
+    const int p = pos + __popcll(msk & below);
+    if (b && p < k_max) out[p] = j0 + lane;
+    pos += __popcll(msk);
+  }
+  for (int p = pos + lane; p < k_max; p += 64) out[p] = -1;
+  if (lane == 0) kept_cnt[row] = pos < k_max ? pos : k_max;
+}
+
 // float64 value of an order key (inverse of order_key)
 __device__ inline double order_key_value(uint64_t k) {
   const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
@@ -381,8 +426,18 @@ hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg
 hipError_t launch_topk(const double* key, const ress_shape& s,
                        const SelConfig& cfg, int32_t k_max, int32_t* kept_idx,
                        int32_t* kept_cnt, hipStream_t st) {
-  const int n = n_kblocks(s);
-  dim3 grid(n_qblocks(s), s.H);
+  const int n = n_kblocks(s), nq = n_qblocks(s);
+  if (n <= 64 * 34) {  // one wave per row, the keys in registers
+    const dim3 wgrid((nq + 3) / 4, s.H);
+    if (n <= 64 * 17)
+      hipLaunchKernelGGL((topk_wave_kernel<17>), wgrid, dim3(256), 0, st, key, nq, n, cfg,
+                         k_max, kept_idx, kept_cnt);
+    else
+      hipLaunchKernelGGL((topk_wave_kernel<34>), wgrid, dim3(256), 0, st, key, nq, n, cfg,
+                         k_max, kept_idx, kept_cnt);
+    return hipGetLastError();
+  }
+  dim3 grid(nq, s.H);
   switch (pick_e(n)) {
 #define RESS_CASE(E)                                                        \
   case E:                                                                   \
