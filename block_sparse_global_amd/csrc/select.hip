@@ -294,7 +294,7 @@ __device__ inline double order_key_value(uint64_t k) {
 
 // Dynamic LDS of cdf_kernel for up to `cap` selected candidates: their order
 // keys, their probabilities in rank order and their ranks.
-inline size_t cdf_smem_bytes(int cap) {
+__host__ __device__ inline size_t cdf_smem_bytes(int cap) {
   return (size_t)cap * (sizeof(uint64_t) + sizeof(double) + sizeof(int32_t));
 }
 
@@ -389,6 +389,129 @@ int pick_e(int n) {
   return e;
 }
 
+// LDS of one wave of cdf_wave_kernel: the radix histogram, then the
+// candidate tables, rounded up to 16 bytes so that every wave's tables stay
+// 8-byte aligned.
+__host__ __device__ inline size_t cdf_wave_stride(int cap) {
+  return (1024 + cdf_smem_bytes(cap) + 15) & ~(size_t)15;
+}
+
+// The cumulative threshold with one wave per row, four rows per workgroup,
+// for rows of at most 64 KPL key blocks: the c_h best candidates by the
+// per-wave radix select, compacted in ascending block order into the wave's
+// LDS, ranked exactly by (P descending, index ascending), and one lane adds
+// the always-kept mass and then the ranked probabilities, in the same order
+// and with the same float64 additions as cdf_kernel, so the counts agree.
+template <int KPL>
+__global__ __launch_bounds__(256) void cdf_wave_kernel(
+    const double* __restrict__ P, int nq, int n, SelConfig cfg, double tau, int cap,
+    int k_max, int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cdf_smem[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  unsigned char* mine = cdf_smem + (size_t)w * cdf_wave_stride(cap);
+  uint32_t* whist = reinterpret_cast<uint32_t*>(mine);                  // [256]
+  uint64_t* ck = reinterpret_cast<uint64_t*>(mine + 1024);              // [cap] keys, block order
+  double* sp = reinterpret_cast<double*>(ck + cap);                     // [cap] P in rank order
+  int32_t* rk = reinterpret_cast<int32_t*>(sp + cap);                   // [cap] rank of ck[a]
+  const int i = blockIdx.x * 4 + w;
+  const int h = blockIdx.y;
+  if (i >= nq) return;  // whole wave; nothing below waits on other waves
+  const size_t row = (size_t)h * nq + i;
+  const double* prow = P + row * n;
+  SelKeys<KPL> keys(reinterpret_cast<const uint64_t*>(prow), n, lane);
+  uint64_t member = 0, always = 0;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const int j = lane + 64 * k;
+    keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
+    if (j < n) {
+      if (sel_always(cfg, j))
+        always |= 1ull << k;
+      else
+        member |= 1ull << k;
+    }
+  }
+  const int c = cfg.keep[h] - cfg.n_always;
+  const uint64_t sel = wave_select<KPL>(keys, member, n, c, whist);
+  // the c best candidates, compacted in ascending block order
+  const uint64_t below = (1ull << lane) - 1ull;
+  int pos = 0;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const bool b = (sel >> k) & 1ull;
+    const uint64_t msk = __ballot(b);
+    if (b) ck[pos + __popcll(msk & below)] = keys.v[k];
+    pos += __popcll(msk);
+  }
+  wave_lds_sync();
+  // rank by probability descending; equal probabilities by block index,
+  // which is the compacted position
+  for (int a = lane; a < c; a += 64) {
+    const uint64_t ka = ck[a];
+    int r = 0;
+    for (int b = 0; b < c; ++b) {
+      const uint64_t kb = ck[b];
+      r += (kb > ka) || (kb == ka && b < a);
+    }
+    rk[a] = r;
+    sp[r] = order_key_value(ka);
+  }
+  wave_lds_sync();
+  int taken = 0;
+  if (lane == 0) {
+    double s = 0.0;
+    for (int wd = 0; wd * 64 < n; ++wd) {
+      uint64_t bits = cfg.always_bits[wd];
+      while (bits != 0) {
+        const int j = wd * 64 + __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (j < n) s += prow[j];
+      }
+    }
+    int m = 0;
+    while (s < tau && m < c) s += sp[m++];
+    m = max(m, 2 - cfg.n_always);
+    taken = min(m, c);
+  }
+  taken = __shfl(taken, 0, 64);
+  uint64_t kept = always;
+  pos = 0;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const bool b = (sel >> k) & 1ull;
+    const uint64_t msk = __ballot(b);
+    if (b && rk[pos + __popcll(msk & below)] < taken) kept |= 1ull << k;
+    pos += __popcll(msk);
+  }
+  int32_t* out = kept_idx + row * k_max;
+  pos = 0;
+  for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
+    const bool b = (kept >> k) & 1ull;
+    const uint64_t msk = __ballot(b);
+    const int p = pos + __popcll(msk & below);
+    if (b && p < k_max) out[p] = j0 + lane;
+    pos += __popcll(msk);
+  }
+  for (int p = pos + lane; p < k_max; p += 64) out[p] = -1;
+  if (lane == 0) kept_cnt[row] = pos < k_max ? pos : k_max;
+}
+
+template <int KPL>
+hipError_t launch_cdf_wave(const double* P, int nq, int n, int H, const SelConfig& cfg,
+                           double tau, int cap, int32_t k_max, int32_t* kept_idx,
+                           int32_t* kept_cnt, hipStream_t st) {
+  const size_t smem = 4 * cdf_wave_stride(cap);
+  if (smem > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&cdf_wave_kernel<KPL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((cdf_wave_kernel<KPL>), dim3((nq + 3) / 4, H), dim3(256), smem, st, P, nq,
+                     n, cfg, tau, cap, k_max, kept_idx, kept_cnt);
+  return hipGetLastError();
+}
+
 template <int E>
 hipError_t launch_cdf_e(const double* P, int nq, int n, int H, const SelConfig& cfg,
                         double tau, int cap, int32_t k_max, int32_t* kept_idx,
@@ -413,6 +536,14 @@ hipError_t launch_cdf(const double* P, const ress_shape& s, const SelConfig& cfg
   const int nq = n_qblocks(s), n = n_kblocks(s);
   int cap = 1;
   for (int h = 0; h < s.H; ++h) cap = max(cap, cfg.keep[h] - cfg.n_always);
+  // one wave per row for long rows and small budgets (the rank count costs
+  // a single wave c^2/64 comparisons per lane, against c^2/256 with four)
+  if (n > 512 && cap <= 256 && 4 * cdf_wave_stride(cap) <= 160 * 1024) {
+    if (n <= 64 * 17)
+      return launch_cdf_wave<17>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+    if (n <= 64 * 34)
+      return launch_cdf_wave<34>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
+  }
   switch (pick_e(n)) {
     case 1: return launch_cdf_e<1>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
     case 2: return launch_cdf_e<2>(P, nq, n, s.H, cfg, tau, cap, k_max, kept_idx, kept_cnt, st);
