@@ -175,10 +175,11 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
     const double* __restrict__ P, const double* __restrict__ key,
     const double* __restrict__ vpool, int nq, int nk, SelConfig cfg, int round, double rho,
     double eps, RefineWs ws) {
-  const int h = blockIdx.z;
+  const TileIdx tid3 = xcd_tile_order();
+  const int h = tid3.z;
   if (swaps_of(cfg, h, round, rho) <= 0) return;  // no swaps for this head
   __shared__ TileF64Smem sm;
-  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
+  const int j0 = tid3.x * kTF, i0 = tid3.y * kTF;
   const double* Uh = ws.u + (size_t)h * nq * kD;
   const double* Vh = vpool + (size_t)h * nk * kD;
   f64x4 acc[2][2];

@@ -52,8 +52,9 @@ __global__ __launch_bounds__(kThreads) void logits_kernel(
     const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int nq,
     int nk, double* __restrict__ P) {
   __shared__ TileF64Smem sm;
-  const int h = blockIdx.z;
-  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
+  const TileIdx tid3 = xcd_tile_order();
+  const int h = tid3.z;
+  const int j0 = tid3.x * kTF, i0 = tid3.y * kTF;
   const double* qh = qpool + (size_t)h * nq * kD;
   const double* kh = kpool + (size_t)h * nk * kD;
   f64x4 acc[2][2];
@@ -172,8 +173,9 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
     double* __restrict__ vout) {
   __shared__ double Ps[kVR][kVJ + 2];
   __shared__ double Vs[kVJ][kD + 16];
-  const int h = blockIdx.y;
-  const int i0 = blockIdx.x * kVR;
+  const TileIdx tid3 = xcd_tile_order();  // row tiles of a head together
+  const int h = tid3.y;
+  const int i0 = tid3.x * kVR;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int rt = 16 * (w >> 1), dt = 32 * (w & 1);
@@ -247,8 +249,9 @@ __global__ __launch_bounds__(kThreads) void key_kernel(
     const double* __restrict__ vout, int nq, int nk, double eps, double* __restrict__ key) {
   __shared__ TileF64Smem sm;
   __shared__ double apart[2][kTF][4];
-  const int h = blockIdx.z;
-  const int j0 = blockIdx.x * kTF, i0 = blockIdx.y * kTF;
+  const TileIdx tid3 = xcd_tile_order();
+  const int h = tid3.z;
+  const int j0 = tid3.x * kTF, i0 = tid3.y * kTF;
   const double* voh = vout + (size_t)h * nq * kD;
   const double* vph = vpool + (size_t)h * nk * kD;
   const double* Mh = M ? M + (size_t)h * kD * kD : nullptr;

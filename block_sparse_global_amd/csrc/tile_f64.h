@@ -44,6 +44,22 @@ struct TileF64Map {
   __device__ int col_of(int tc) const { return wc + 16 * tc + lc; }
 };
 
+// XCD-aware tile order for a 3-D grid of tiles (x fastest): workgroups go
+// round-robin to the 8 XCDs, so the k-th workgroup an XCD receives takes the
+// k-th tile of that XCD's contiguous share of the tiles. Neighbouring tiles,
+// which read the same operand rows, then run on one XCD and share its L2.
+struct TileIdx {
+  int x, y, z;
+};
+__device__ inline TileIdx xcd_tile_order() {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int T = gx * gy * gridDim.z;
+  const int bid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xcd = bid & 7, k = bid >> 3;
+  const int logical = xcd * (T >> 3) + min(xcd, T & 7) + k;
+  return TileIdx{logical % gx, (logical / gx) % gy, logical / (gx * gy)};
+}
+
 // stage_a(r, d0, x[8]) / stage_b(r, d0, x[8]) return dims d0 .. d0+7 of the
 // tile's row r of A / B (callers clamp rows past the end to a valid row).
 template <typename StageA, typename StageB>
