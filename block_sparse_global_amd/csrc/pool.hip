@@ -12,8 +12,12 @@ constexpr int kThreads = 256;
 constexpr int kD = 64;
 
 // 8 consecutive elements of one token row, widened exactly to float64.
+// Every input byte is read once, so the loads are non-temporal (streamed
+// past the caches' retention policy).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ inline void load8(const uint16_t* p, double (&v)[8]) {
-  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -23,8 +27,8 @@ __device__ inline void load8(const uint16_t* p, double (&v)[8]) {
 }
 
 __device__ inline void load8(const float* p, double (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
