@@ -165,8 +165,14 @@ __global__ __launch_bounds__(kThreads) void vmv_kernel(
 // tiles); the key blocks stream through LDS 64 at a time, 4 per MFMA step.
 // Row padding: 66 doubles for P (a half-wave reads 16 rows x 2 columns) and
 // 80 for V (2 rows x 16 columns), so both reads are free of bank conflicts.
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(double* __restrict__ p, size_t n) {
+  const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e < n) p[e] = 0.0;
+}
+
 constexpr int kVR = 32;  // rows per workgroup
-constexpr int kVJ = 64;  // key blocks per LDS stage
+constexpr int kVJ = 32;  // key blocks per LDS stage
+constexpr int kVParts = 2;  // key-block halves per row tile (grid z)
 
 __global__ __launch_bounds__(kThreads) void vout_kernel(
     const double* __restrict__ P, const double* __restrict__ vpool, int nq, int nk,
@@ -176,6 +182,9 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
   const TileIdx tid3 = xcd_tile_order();  // row tiles of a head together
   const int h = tid3.y;
   const int i0 = tid3.x * kVR;
+  // this workgroup's share of the key-block chunks
+  const int nch = (nk + kVJ - 1) / kVJ;
+  const int c_lo = tid3.z * nch / kVParts, c_hi = (tid3.z + 1) * nch / kVParts;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int rt = 16 * (w >> 1), dt = 32 * (w & 1);
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
   do {                                                                         \
     _Pragma("unroll") for (int e = 0; e < kPE; ++e) {                          \
       const int idx = tid + e * kThreads;                                      \
-      const int i = min(i0 + (idx >> 6), nq - 1), j = (JC) + (idx & 63);       \
+      const int i = min(i0 + idx / kVJ, nq - 1), j = (JC) + idx % kVJ;         \
       const double x = Ph[(size_t)i * nk + min(j, nk - 1)];                    \
       pr[e] = j < nk ? x : 0.0;                                                \
     }                                                                          \
@@ -203,12 +212,12 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
       vy[e] = v2.y;                                                            \
     }                                                                          \
   } while (0)
-  RESS_VOUT_LOAD_CHUNK(0);
-  for (int jc = 0; jc < nk; jc += kVJ) {
+  RESS_VOUT_LOAD_CHUNK(c_lo * kVJ);
+  for (int jc = c_lo * kVJ; jc < c_hi * kVJ; jc += kVJ) {
 #pragma unroll
     for (int e = 0; e < kPE; ++e) {
       const int idx = tid + e * kThreads;
-      Ps[idx >> 6][idx & 63] = pr[e];
+      Ps[idx / kVJ][idx % kVJ] = pr[e];
     }
 #pragma unroll
     for (int e = 0; e < kVE; ++e) {
@@ -232,10 +241,12 @@ __global__ __launch_bounds__(kThreads) void vout_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = i0 + rt + (l >> 4) + 4 * r;
+    // the two halves' sums add into the zeroed output; 0 + a + b is the
+    // same in either order, so the result does not depend on scheduling
     if (i < nq)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        vout[((size_t)h * nq + i) * kD + dt + 16 * t + (l & 15)] = acc[t][r];
+        atomicAdd(&vout[((size_t)h * nq + i) * kD + dt + 16 * t + (l & 15)], acc[t][r]);
   }
 }
 #undef RESS_VOUT_LOAD_CHUNK
@@ -352,8 +363,11 @@ hipError_t launch_drift(const double* P, const double* vpool, const double* M,
                         const double* vmv, const ress_shape& s, double eps,
                         double* key, double* vout, hipStream_t st) {
   const int nq = n_qblocks(s), nk = n_kblocks(s);
-  hipLaunchKernelGGL(vout_kernel, dim3((nq + kVR - 1) / kVR, s.H), dim3(kThreads), 0, st, P,
-                     vpool, nq, nk, vout);
+  const size_t nv = (size_t)s.H * nq * kD;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((nv + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, vout, nv);
+  hipLaunchKernelGGL(vout_kernel, dim3((nq + kVR - 1) / kVR, s.H, kVParts), dim3(kThreads), 0,
+                     st, P, vpool, nq, nk, vout);
   const dim3 tiles((nk + kTF - 1) / kTF, (nq + kTF - 1) / kTF, s.H);
   hipLaunchKernelGGL(key_kernel, tiles, dim3(kThreads), 0, st, P, vpool, M, vmv, vout, nq, nk,
                      eps, key);
