@@ -108,21 +108,30 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
   const uint64_t below = (1ull << lane) - 1ull;
   double ks = 0.0;
   int nD = 0, nS = 0, pos = 0;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const bool in = j < n;
-    const uint8_t f = in ? flags[j] : 0;
-    if (in) {
-      fc[j] = f;
-      fb[j] = f;
+  // the P row is read in batches of 8 chunks of 64 blocks (clamped
+  // addresses, all loads in flight together); the sum takes the same order
+  constexpr int kPre = 8;
+  for (int c0 = 0; c0 < n; c0 += 64 * kPre) {
+    double pv[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) pv[u] = Prow[min(c0 + 64 * u + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int j = c0 + 64 * u + lane;
+      const bool in = j < n;
+      const uint8_t f = in ? flags[j] : 0;
+      if (in) {
+        fc[j] = f;
+        fb[j] = f;
+      }
+      const bool inD = in && f != 0, kept = in && f == 0;
+      if (inD) ks += pv[u];
+      nD += inD;
+      nS += kept && !sel_always(cfg, j);
+      const uint64_t msk = __ballot(kept);
+      if (kept) slist[pos + __popcll(msk & below)] = j;
+      pos += __popcll(msk);
     }
-    const bool inD = in && f != 0, kept = in && f == 0;
-    if (inD) ks += Prow[j];
-    nD += inD;
-    nS += kept && !sel_always(cfg, j);
-    const uint64_t msk = __ballot(kept);
-    if (kept) slist[pos + __popcll(msk & below)] = j;
-    pos += __popcll(msk);
   }
   const double K = 1.0 - wave_sum64(ks);
   nD = wave_isum64(nD);
