@@ -47,8 +47,8 @@ CDF_TAU = 0.05
 ATTN_TRAFFIC = {
     "workload": "views100",
     "source_sha256": "f2550d696f457638dec8475fab88a1be5918e0440e6531ef6cb2d1160362011a",
-    "read_bytes": 4708016605,
-    "write_bytes": 281542976,
+    "read_bytes": 4716950798,
+    "write_bytes": 281543328,
 }
 
 
