@@ -146,11 +146,14 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
     const int j = slist[q];
     acc += Prow[j] * (Vh[(size_t)j * kD + d] - vod);
   }
-  gl[d] = acc;
+  // the sum over S equals the one over D (Eq. 10) up to the rounding of
+  // vout; an empty D is the empty sum, exactly zero
+  const double g = nD > 0 ? acc : 0.0;
+  gl[d] = g;
   wave_lds_sync();
   double G, vu;
-  const double u = gram_apply(M ? M + (size_t)h * kD * kD : nullptr, gl, acc, vod, &G, &vu);
-  ws.g[row * kD + d] = acc;
+  const double u = gram_apply(M ? M + (size_t)h * kD * kD : nullptr, gl, g, vod, &G, &vu);
+  ws.g[row * kD + d] = g;
   ws.u[row * kD + d] = u;
   if (lane == 0) {
     RowState st;

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
       for (int t = 0; t < 16; ++t)
         if (q0 + t < pos) acc += pv[t] * (vv[t] - vod);
     }
-    g = acc;
+    g = nD > 0 ? acc : 0.0;  // an empty D: the empty sum of Eq. 10
     ul[d] = g;
     wave_lds_sync();
     double G, vu;

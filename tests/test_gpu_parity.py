@@ -605,3 +605,82 @@ def test_reruns_are_bit_identical_on_a_side_stream():
     for k in a:
         if isinstance(a[k], np.ndarray):
             assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+# ---------------------------------------------------------------------------
+# Seeded random shapes, end to end
+# ---------------------------------------------------------------------------
+
+def _random_workload(idx: int):
+    """A valid small workload drawn from a seeded generator: token counts that
+    leave ragged last blocks, both block grids, 1-3 heads with unequal
+    budgets, special-token blocks or none, bf16 or float32 inputs, either
+    score, 0-3 refinement rounds."""
+    rng = np.random.default_rng(7000 + idx)
+    for _ in range(100):
+        block = int(rng.choice([64, 128]))
+        kw = dict(
+            views=int(rng.integers(1, 5)), patches_per_view=int(rng.integers(1, 700)),
+            specials_per_view=int(rng.choice([0, 1, 5])), heads=int(rng.integers(1, 4)),
+            block=block, key_block=int(rng.choice([0, 64])) if block == 128 else 0,
+            dtype=str(rng.choice(["bf16", "f32"])),
+            sparsity=tuple(sorted(float(s) for s in rng.uniform(0.0, 0.95, 2))),
+            score=str(rng.choice(["prob", "drift"])),
+            generator=str(rng.choice(["low_rank", "shared_vector"])),
+            rho=float(rng.uniform(0.2, 1.0)), seed=int(rng.integers(1 << 30)))
+        kw["rounds"] = int(rng.integers(0, 4)) if kw["score"] == "drift" else 0
+        w = custom(name=f"rand{idx}", **kw)
+        if w.n_kblocks < 2:
+            continue
+        try:
+            return w, synth.make_inputs(w)
+        except ValueError:  # budgets that do not fit this block count
+            continue
+    raise RuntimeError("no valid random workload")
+
+
+@pytest.mark.parametrize("idx", range(12))
+def test_random_shapes_end_to_end(idx):
+    """Every step of the path on a seeded random small shape against the
+    oracle: pooled tensors, block map and drift key, top-k and refined keep
+    sets (equal up to near-ties), J values, and the attention output and
+    log-sum-exp of every query block."""
+    w, x = _random_workload(idx)
+    print(f"\n[random {idx}] N={w.N} B={w.block} Bk={w.kblock} H={w.heads} dtype={w.dtype} "
+          f"score={w.score} rounds={w.rounds} keep={[int(k) for k in x['keep']]} "
+          f"always={int(x['always'].sum())}", flush=True)
+    g = run_gpu(w, x, w.score)
+    N, B, Bk, n = w.N, w.block, w.kblock, w.n_kblocks
+    qf, kf, vf = (f64(x[t], w) for t in ("q", "k", "v"))
+    qp, kp = oracle.block_pool(qf, N, B), oracle.block_pool(kf, N, Bk)
+    _close(g["qpool"], qp, 1e-12, "qpool")
+    _close(g["kpool"], kp, 1e-12, "kpool")
+    P = oracle.block_map(qp, kp, 0.125)
+    _close(g["P"], P, 1e-12, "P")
+    key = P
+    if w.score == "drift":
+        vp = oracle.block_pool(vf, N, Bk)
+        _close(g["vpool"], vp, 1e-12, "vpool")
+        key, vout, _ = oracle.drift_key(P, vp, None, 1e-4)
+        _close(g["key"], key, 1e-10, "drift key")
+        _close(g["vout"], vout, 1e-12, "vout")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    check_lists_wellformed(g["topk_idx"], g["topk_cnt"], x["keep"], x["always"], n)
+    start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
+    compare_masks(start, kept, key, x["always"], x["keep"])
+    final = kept_mask_from_lists(g["idx"], g["cnt"], n)
+    check_lists_wellformed(g["idx"], g["cnt"], x["keep"], x["always"], n)
+    if w.rounds:
+        kr, J0, J1, mg = oracle.refine_dropset(P, vp, vout, None, x["keep"], x["always"], start,
+                                               w.rounds, w.rho)
+        same = np.all(final == kr, axis=-1)
+        assert np.all(same | (mg < 1e-6)), "a refined set differs without a near-tie"
+        assert np.allclose(g["J_init"], J0, rtol=1e-9, atol=0)
+        assert np.allclose(g["J_final"][same], J1[same], rtol=1e-9, atol=0)
+        assert np.all(g["J_final"] <= g["J_init"])
+    O, lse = oracle.masked_attention(qf, kf, vf, final, N, B, 0.125, Bk=Bk)
+    mx, mean, _ = attn_errors(g["out"][:, :N], O[:, :N])
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
+    assert np.all(g["out"][:, N:] == 0), "padded rows must be zero"
+    dl = np.abs(g["lse"][:, :N] - lse[:, :N])
+    assert dl.max() <= LSE_TOL[w.dtype], dl.max()
