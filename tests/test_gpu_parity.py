@@ -26,6 +26,7 @@ import pytest
 
 import oracle
 import synth
+from synth.gen import bf16_bits_to_f32, f32_to_bf16_bits
 from synth.workloads import custom
 from tests.helpers import (
     attn_errors,
@@ -639,7 +640,7 @@ def _random_workload(idx: int):
     raise RuntimeError("no valid random workload")
 
 
-@pytest.mark.parametrize("idx", range(12))
+@pytest.mark.parametrize("idx", range(48))
 def test_random_shapes_end_to_end(idx):
     """Every step of the path on a seeded random small shape against the
     oracle: pooled tensors, block map and drift key, top-k and refined keep
@@ -663,7 +664,10 @@ def test_random_shapes_end_to_end(idx):
         _close(g["vpool"], vp, 1e-12, "vpool")
         key, vout, _ = oracle.drift_key(P, vp, None, 1e-4)
         _close(g["key"], key, 1e-10, "drift key")
-        _close(g["vout"], vout, 1e-12, "vout")
+        # each component of vout sums terms of both signs: its error is bounded
+        # by the sum of their magnitudes (float64, another summation order)
+        mag = np.einsum("hij,hjd->hid", P, np.abs(vp))
+        assert np.all(np.abs(g["vout"] - vout) <= 1e-12 * mag), "vout"
     kept, _ = oracle.select_topk(key, x["keep"], x["always"])
     check_lists_wellformed(g["topk_idx"], g["topk_cnt"], x["keep"], x["always"], n)
     start = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)
@@ -678,9 +682,17 @@ def test_random_shapes_end_to_end(idx):
         assert np.allclose(g["J_init"], J0, rtol=1e-9, atol=0)
         assert np.allclose(g["J_final"][same], J1[same], rtol=1e-9, atol=0)
         assert np.all(g["J_final"] <= g["J_init"])
-    O, lse = oracle.masked_attention(qf, kf, vf, final, N, B, 0.125, Bk=Bk)
+    # the attention call rounds float32 inputs to bf16 (nearest even) as it
+    # stages them, so the oracle takes the same rounded values; the selection
+    # above saw the float32 values themselves
+    if w.dtype == "f32":
+        qa, ka, va = (bf16_bits_to_f32(f32_to_bf16_bits(x[t])).astype(np.float64)
+                      for t in ("q", "k", "v"))
+    else:
+        qa, ka, va = qf, kf, vf
+    O, lse = oracle.masked_attention(qa, ka, va, final, N, B, 0.125, Bk=Bk)
     mx, mean, _ = attn_errors(g["out"][:, :N], O[:, :N])
     assert mx <= MAX_ABS and mean <= MEAN_ABS, (mx, mean)
     assert np.all(g["out"][:, N:] == 0), "padded rows must be zero"
     dl = np.abs(g["lse"][:, :N] - lse[:, :N])
-    assert dl.max() <= LSE_TOL[w.dtype], dl.max()
+    assert dl.max() <= LSE_TOL["bf16"], dl.max()
