@@ -696,3 +696,75 @@ def test_random_shapes_end_to_end(idx):
     assert np.all(g["out"][:, N:] == 0), "padded rows must be zero"
     dl = np.abs(g["lse"][:, :N] - lse[:, :N])
     assert dl.max() <= LSE_TOL["bf16"], dl.max()
+
+
+@pytest.mark.parametrize("idx", range(24))
+def test_random_shapes_gram_fused_cdf(idx):
+    """Seeded random shapes in drift mode with a Gram matrix and 1-4 rounds:
+    the drift key and the refined keep sets against the oracle, the fused
+    refinement against the per-round kernels bit for bit, and the CDF
+    selection on the oracle's map against the oracle exactly."""
+    import dataclasses
+    b = _lib()
+    w, _ = _random_workload(1000 + idx)
+    rng = np.random.default_rng(9000 + idx)
+    w = dataclasses.replace(w, score="drift", rounds=int(rng.integers(1, 5)))
+    x = synth.make_inputs(w)
+    M = synth.make_gram(w.heads, w.head_dim, seed=idx)
+    print(f"\n[random-gram {idx}] N={w.N} B={w.block} Bk={w.kblock} H={w.heads} "
+          f"dtype={w.dtype} rounds={w.rounds} rho={w.rho:.2f} keep={[int(k) for k in x['keep']]}",
+          flush=True)
+    shape = b.Shape(*w.shape_args())
+    Mt = torch.from_numpy(M).cuda()
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    res = {}
+    for impl in ("rounds", "fused"):
+        layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode="drift",
+                                             rounds=w.rounds, rho=w.rho, M=Mt,
+                                             refine_impl=impl)
+        layer.pool(q, k, v)
+        layer.score()
+        layer.select()
+        torch.cuda.synchronize()
+        start = kept_mask_from_lists(layer.kept_idx.cpu().numpy(), layer.kept_cnt.cpu().numpy(),
+                                     w.n_kblocks)
+        gkey = layer.key.cpu().numpy()
+        layer.refine()
+        torch.cuda.synchronize()
+        res[impl] = [a.cpu().numpy() for a in (layer.kept_idx, layer.kept_cnt, layer.J_init,
+                                               layer.J_final)]
+        del layer
+    for a, c, what in zip(res["rounds"], res["fused"], ("kept_idx", "kept_cnt", "J_init",
+                                                        "J_final")):
+        assert np.array_equal(a, c), f"fused refinement: {what} differs"
+    N, B, Bk, n = w.N, w.block, w.kblock, w.n_kblocks
+    qp = oracle.block_pool(f64(x["q"], w), N, B)
+    kp = oracle.block_pool(f64(x["k"], w), N, Bk)
+    vp = oracle.block_pool(f64(x["v"], w), N, Bk)
+    P = oracle.block_map(qp, kp, 0.125)
+    key, vout, _ = oracle.drift_key(P, vp, M, 1e-4)
+    _close(gkey, key, 1e-10, "drift key with M")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    compare_masks(start, kept, key, x["always"], x["keep"])
+    kr, J0, J1, mg = oracle.refine_dropset(P, vp, vout, M, x["keep"], x["always"], start,
+                                           w.rounds, w.rho)
+    gi, gc, gJ0, gJ1 = res["rounds"]
+    check_lists_wellformed(gi, gc, x["keep"], x["always"], n)
+    same = np.all(kept_mask_from_lists(gi, gc, n) == kr, axis=-1)
+    assert np.all(same | (mg < 1e-6)), "a refined set differs without a near-tie"
+    assert np.allclose(gJ0, J0, rtol=1e-9, atol=0)
+    assert np.allclose(gJ1[same], J1[same], rtol=1e-9, atol=0)
+    assert np.all(gJ1 <= gJ0)
+    # CDF selection on the oracle's own map: identical sets at three thresholds
+    Pt = torch.from_numpy(P).cuda()
+    k_max = int(np.max(x["keep"]))
+    alw = int(np.sum(x["always"]))
+    for tau in (1e-9, float(rng.uniform(0.01, 0.5)), 2.0):
+        idx_t = torch.full((w.heads, w.n_blocks, k_max), 7, dtype=torch.int32, device="cuda")
+        cnt_t = torch.full((w.heads, w.n_blocks), -5, dtype=torch.int32, device="cuda")
+        b.ress_select_cdf(Pt, shape, x["keep"], x["always"], tau, k_max, idx_t, cnt_t)
+        torch.cuda.synchronize()
+        ci, cc = idx_t.cpu().numpy(), cnt_t.cpu().numpy()
+        ck, taken, _ = oracle.select_cdf(P, x["keep"], x["always"], tau)
+        assert np.array_equal(cc, taken + alw), f"cdf counts at tau={tau}"
+        assert np.array_equal(kept_mask_from_lists(ci, cc, n), ck), f"cdf sets at tau={tau}"
