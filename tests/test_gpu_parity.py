@@ -768,3 +768,48 @@ def test_random_shapes_gram_fused_cdf(idx):
         ck, taken, _ = oracle.select_cdf(P, x["keep"], x["always"], tau)
         assert np.array_equal(cc, taken + alw), f"cdf counts at tau={tau}"
         assert np.array_equal(kept_mask_from_lists(ci, cc, n), ck), f"cdf sets at tau={tau}"
+
+
+@pytest.mark.parametrize("n", [1088, 1089, 2176, 2177])
+def test_row_length_boundaries(n):
+    """Rows on either side of the selection kernels' register limits (17 and
+    34 keys per lane; longer rows keep their keys in LDS): top-k, two
+    refinement rounds and the CDF selection on sampled rows against the
+    oracle."""
+    b = _lib()
+    w, x = _small(name=f"len{n}", views=1, patches_per_view=n * 64 - 37, heads=1, block=64,
+                  sparsity=(0.9, 0.9), score="drift", rounds=2, seed=n)
+    assert w.n_kblocks == n
+    g = run_gpu(w, x, "drift")
+    N, B = w.N, w.block
+    qp = oracle.block_pool(f64(x["q"], w), N, B)
+    kp = oracle.block_pool(f64(x["k"], w), N, B)
+    vp = oracle.block_pool(f64(x["v"], w), N, B)
+    P = oracle.block_map(qp, kp, 0.125)
+    rows = [0, 1, n // 3, n // 2, n - 2, n - 1]
+    key, vout, _ = oracle.drift_key(P[:, rows], vp, None, 1e-4)
+    _close(g["key"][:, rows], key, 1e-10, "drift key rows")
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    check_lists_wellformed(g["topk_idx"], g["topk_cnt"], x["keep"], x["always"], n)
+    topk = kept_mask_from_lists(g["topk_idx"], g["topk_cnt"], n)[:, rows]
+    compare_masks(topk, kept, key, x["always"], x["keep"])
+    kr, J0, J1, mg = oracle.refine_dropset(P[:, rows], vp, vout, None, x["keep"], x["always"],
+                                           topk, w.rounds, w.rho)
+    assert np.allclose(g["J_init"][:, rows], J0, rtol=1e-9, atol=0)
+    same = np.all(kept_mask_from_lists(g["idx"], g["cnt"], n)[:, rows] == kr, axis=-1)
+    assert np.all(same | (mg < 1e-6))
+    assert np.allclose(g["J_final"][:, rows][same], J1[same], rtol=1e-9, atol=0)
+    shape = b.Shape(*w.shape_args())
+    k_max = int(np.max(x["keep"]))
+    Pt = torch.from_numpy(P).cuda()
+    for tau in (0.05, 0.3):
+        idx_t = torch.full((1, n, k_max), 7, dtype=torch.int32, device="cuda")
+        cnt_t = torch.full((1, n), -5, dtype=torch.int32, device="cuda")
+        b.ress_select_cdf(Pt, shape, x["keep"], x["always"], tau, k_max, idx_t, cnt_t)
+        torch.cuda.synchronize()
+        ci, cc = idx_t.cpu().numpy(), cnt_t.cpu().numpy()
+        ck, taken, _ = oracle.select_cdf(P, x["keep"], x["always"], tau,
+                                         rows=[(0, i) for i in rows])
+        for i in rows:
+            assert cc[0, i] == taken[0, i], f"cdf count row {i} tau={tau}"
+            assert set(ci[0, i, :cc[0, i]].tolist()) == set(np.nonzero(ck[0, i])[0].tolist())
