@@ -547,6 +547,20 @@ def test_refine_zero_rounds_is_identity():
     assert np.array_equal(J0, J1)
 
 
+def test_refine_row_keeping_every_block_has_zero_objective():
+    """An empty drop set: g and K of Eq. 10 are the empty sum and 1 - 0, so
+    J = 0 exactly, no swap is possible and the set stays as it is."""
+    P, V = _random_map(301, 2, 6, 4)
+    always = np.zeros(6, np.uint8); always[5] = 1
+    key, vout, _ = oracle.drift_key(P, V, None)
+    keep = np.array([6, 3])
+    kept, _ = oracle.select_topk(key, keep, always)
+    kr, J0, J1, _ = oracle.refine_dropset(P, V, vout, None, keep, always, kept, 3, 1.0)
+    assert np.all(kr[0]) and np.array_equal(kr[0], kept[0])
+    assert np.all(J0[0] == 0.0) and np.all(J1[0] == 0.0)
+    assert np.all(J0[1] > 0.0)
+
+
 # ---------------------------------------------------------------------------
 # Attention over the kept blocks (the four checks of the hot-path contract)
 # ---------------------------------------------------------------------------
