@@ -13,7 +13,6 @@ from .ress_oracle import (  # noqa: F401
     pooled_output,
     drift_key,
     gram_from_wo,
-    score_key,
     select_topk,
     select_cdf,
     kept_lists,

@@ -133,17 +133,6 @@ def drift_key(P: np.ndarray, vpool: np.ndarray, M: Optional[np.ndarray],
     return key, vout, q
 
 
-def score_key(P, vpool, M, mode: str, eps: float = 1e-4):
-    """Ranking key of every (h, i, j): the pooled probability ("prob",
-    SparseVGGT/HeSS as described in the ReSS page §3 "The Probability
-    Assumption") or the drift key ("drift", ReSS page Eq. 7)."""
-    if mode == "prob":
-        return P.copy()
-    if mode == "drift":
-        return drift_key(P, vpool, M, eps)[0]
-    raise ValueError(mode)
-
-
 # ---------------------------------------------------------------------------
 # Step 3: per-row top-k selection (ReSS page, §3 step (2) and §4.1 Eq. 2)
 # ---------------------------------------------------------------------------

@@ -694,3 +694,86 @@ def test_attention_ignores_padding_garbage():
         t[:, N:, :] = 1e6
     O2, _ = oracle.masked_attention(q, k, v, kept, N, B, 0.5)
     assert np.array_equal(O1, O2)
+
+
+# ---------------------------------------------------------------------------
+# The whole selection path on tokens (ReSS page §3 steps (1)-(2), §4.2-§4.3)
+# ---------------------------------------------------------------------------
+
+def _selection_by_hand(q, k, v, N, B, Bk, keep, always, scale):
+    """Independent restatement on token tensors: pooled means by a torch loop,
+    the map by torch.softmax, the drift key by explicitly deleting one block
+    from the pooled map and renormalising (Eq. 3-4), and top-k sets by brute
+    force over all candidate subsets (the one with the largest key sum)."""
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    H = q.shape[0]
+
+    def pool(t, blk):
+        nb = -(-N // blk)
+        return torch.stack([torch.stack([t[h, b * blk:min(N, (b + 1) * blk)].mean(0)
+                                         for b in range(nb)]) for h in range(H)])
+
+    qp, kp, vp = pool(tq, B), pool(tk, Bk), pool(tv, Bk)
+    P = torch.softmax(scale * torch.einsum("hid,hjd->hij", qp, kp), dim=-1).numpy()
+    vp = vp.numpy()
+    nq, nk = P.shape[1], P.shape[2]
+    key = np.zeros_like(P)
+    for h in range(H):
+        for i in range(nq):
+            vbar = P[h, i] @ vp[h]
+            for j in range(nk):
+                w = P[h, i].copy()
+                w[j] = 0.0
+                key[h, i, j] = np.linalg.norm(w @ vp[h] / w.sum() - vbar)
+    cand = [j for j in range(nk) if not always[j]]
+    n_alw = nk - len(cand)
+
+    def brute(score):
+        kept = np.zeros(score.shape, bool)
+        for h in range(H):
+            c = int(keep[h]) - n_alw
+            for i in range(nq):
+                best = max(itertools.combinations(cand, c),
+                           key=lambda S: sum(score[h, i, j] for j in S))
+                kept[h, i, list(best)] = True
+                kept[h, i, always != 0] = True
+        return kept
+
+    return P, vp, key, brute
+
+
+@pytest.mark.parametrize("Bk", [4, 2])
+def test_run_selection_equals_independent_steps_on_tokens(Bk):
+    H, D, N, N_pad, B = 2, 3, 22, 24, 4
+    r = rng(77 + Bk)
+    q, k, v = (r.standard_normal((H, N_pad, D)) for _ in range(3))
+    for t in (q, k, v):
+        t[:, N:] = 1e6                                      # padding is ignored
+    nk = -(-N // Bk)
+    always = np.zeros(nk, np.uint8)
+    always[nk - 1] = 1
+    keep = np.array([3, 4])
+    scale = 0.6
+    P, vp, key, brute = _selection_by_hand(q, k, v, N, B, Bk, keep, always, scale)
+    prob = oracle.run_selection(q, k, v, N, B, keep, always, "prob", scale=scale, Bk=Bk)
+    np.testing.assert_allclose(prob["P"], P, rtol=1e-12, atol=0)
+    assert np.array_equal(prob["kept"], brute(P))
+    drift = oracle.run_selection(q, k, v, N, B, keep, always, "drift", rounds=3, rho=1.0,
+                                 scale=scale, Bk=Bk)
+    # the drift key is the norm of the explicit single-block masking change
+    np.testing.assert_allclose(drift["key"], key, rtol=1e-10, atol=1e-14)
+    assert np.array_equal(drift["kept"], brute(key))
+    cand = always == 0
+    for h in range(H):
+        c = int(keep[h]) - 1
+        for i in range(P.shape[1]):
+            kr = drift["kept_refined"][h, i]
+            assert kr.sum() == keep[h] and kr[nk - 1]                   # |S| = c_h
+            J0 = _explicit_J(P[h, i], vp[h], np.eye(D), cand & ~drift["kept"][h, i])
+            J1 = _explicit_J(P[h, i], vp[h], np.eye(D), cand & ~kr)
+            assert drift["J_init"][h, i] == pytest.approx(J0, rel=1e-9, abs=1e-300)
+            assert drift["J_final"][h, i] == pytest.approx(J1, rel=1e-9, abs=1e-300)
+            assert J1 <= J0 * (1 + 1e-12)
+            bmin = _brute_min_J(P[h, i], vp[h], np.eye(D), list(np.nonzero(cand)[0]),
+                                int(cand.sum()) - c)
+            assert J1 >= bmin * (1 - 1e-9)
