@@ -14,9 +14,20 @@
 //   O^T += V^T P^T (A = V^T read from the row-major V tile with LDS
 //                  transpose reads, B = P^T taken directly from the S^T
 //                  accumulators after the softmax)
-// so that each lane owns one query column: the running max, the running sum
-// and the rescaling of O are per-lane scalars (the two lane halves holding
-// the same query exchange one value per block).
+// so that each lane owns one query column: the reference subtracted from the
+// logits, the running sum and the rescaling of O are per-lane scalars (the
+// two lane halves holding the same query exchange one value when needed).
+//
+// Softmax in two passes only when needed. The first pass takes the weights
+// as p = exp2(scale * log2(e) * S), with no max subtracted at all: O / l
+// does not depend on a common offset of the logits, and float32 and bf16
+// hold any p in [2^-126, 2^127] to full relative precision. That is valid as
+// long as the row sum l stays within [2^-64, 2^64]: then no weight exceeds
+// 2^64, and the largest one is at least 2^-64 / (keys in the row), so the
+// weights that matter never underflow. A workgroup with any valid row
+// outside that range (logits beyond roughly +-44 in natural units) discards
+// its result and runs its rows again as a classical online softmax (running
+// max, lazy rescaling): the second pass below.
 //
 // MFMA 32x32x16 operand convention used here: lane l supplies 8 consecutive
 // k-slots of row/column (l % 32); lanes l and l+32 cover the two halves of
@@ -47,17 +58,6 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 __device__ inline uint4 load_row8(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
-__device__ inline uint4 load_row8(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  uint4 r;
-  r.x = (uint32_t)f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
-  r.y = (uint32_t)f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
-  r.z = (uint32_t)f32_to_bf16_rne(b.x) | ((uint32_t)f32_to_bf16_rne(b.y) << 16);
-  r.w = (uint32_t)f32_to_bf16_rne(b.z) | ((uint32_t)f32_to_bf16_rne(b.w) << 16);
-  return r;
-}
-
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -110,11 +110,11 @@ __device__ inline float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Running-max slack before O is rescaled (log2 units of the scaled scores):
-// a new block whose row max exceeds the one in use by less than this keeps
-// the old max, so p may reach 2^kRescaleSlack; float32 and bf16 hold that
-// exactly as well as values below 1, and the final O / l uses the same max
-// for numerator and denominator.
+// Range of the row sum accepted from the pass without a max (see the header).
+constexpr float kSumMin = 0x1p-64f;
+constexpr float kSumMax = 0x1p64f;
+// Slack of the online softmax of the second pass (log2 units): a block whose
+// max exceeds the one in use by less than this keeps it, so p <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
 template <int BLK, int KBLK, typename Tin, typename Tout>
@@ -149,6 +149,7 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   const size_t head_off = (size_t)h * N_pad * kD;
   const int qrow = i * BLK + 32 * w + l32;
 
+  const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e)
   // Q^T operand: dims 16*ks + 8*half + 0..7 of this lane's query row.
   bf16x8 qb[4];
   {
@@ -156,15 +157,15 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = as_bf16x8(load_row8(qp + 16 * ks));
   }
+  const bool qvalid = qrow < N;
 
   f32x16 o[2];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_use = -INFINITY;  // running max in use, in scaled log2 units
+  float m_use = 0.f;  // running max in use (second pass), scaled log2 units
   float l_run = 0.f;
-  const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e)
   const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // The keep list is read through the constant address space so that its
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     return is_v ? vgo0 + 8 * it * kD : ((it & 1) ? kgo1 : kgo0) + 16 * (it >> 1) * kD;
   };
   auto issue_tile = [&](const Tin* X, uint16_t* dst, int j, bool is_v) {
-    if constexpr (sizeof(Tin) == 2) {
+    {
       // block base (uniform) + 32-bit per-lane byte offset: the copies use
       // the scalar-base addressing form
       const char* base = reinterpret_cast<const char*>(
@@ -232,18 +233,6 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
                       dst + (kWin * w + it) * 512);
         }
       }
-    } else {
-      // float32 inputs: rounded to bf16 (nearest even) through registers
-      const Tin* base = X + head_off + (size_t)j * KBLK * kD;
-#pragma unroll
-      for (int it = 0; it < KBLK * 8 / kThreads; ++it) {
-        const int idx = tid + it * kThreads;
-        const int r = idx >> 3, c = idx & 7;
-        const int rr = min(r, N - 1 - j * KBLK);
-        const int sw = is_v ? v_swz(r) : k_swz(r);
-        *reinterpret_cast<uint4*>(&dst[r * kD + ((c ^ sw) * 8)]) =
-            load_row8(base + (size_t)rr * kD + c * 8);
-      }
     }
   };
 
@@ -263,9 +252,11 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   }
 
   // ---- one kept block, V from buffer B (compile-time, so all LDS offsets
-  // are immediates); returns the next list position
-  auto process = [&](auto bufc, int kb) {
+  // are immediates); ONLINE: the second pass, with a running max. Returns
+  // the next list position.
+  auto process = [&](auto bufc, auto onlinec, int kb) {
     constexpr int B = decltype(bufc)::value;
+    constexpr bool ONLINE = decltype(onlinec)::value;
     const int j = block_of(kb);
     const int kb_next = next_valid(kb + 1);
     const bool more = kb_next < cnt;
@@ -314,23 +305,24 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
           if (kc >= lim) s[kt][r] = -INFINITY;
         }
     }
-    // online softmax (per lane = per query), lazy rescaling
-    float mloc = -INFINITY;
+    if constexpr (ONLINE) {
+      // online softmax (per lane = per query), lazy rescaling
+      float mb = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
-    mloc = max_halves(mloc);
-    const float m_blk = mloc * sl2;
-    if (__any(m_blk > m_use + kRescaleSlack)) {
-      const float m_new = fmaxf(m_use, m_blk);
-      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[kt][r]);
+      mb = max_halves(mb) * sl2;
+      if (__any(mb > m_use + kRescaleSlack)) {
+        const float m_new = fmaxf(m_use, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_use = m_new;
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_use = m_new;
+      }
     }
     // per 16-key step: P = exp2(S*scale*log2e - m) as bf16, then
     // O^T += V^T P^T with the V^T operand read transposed from LDS
@@ -355,15 +347,19 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     // order; measured 4-5% faster at 100 views.
     bf16x8 vops[2][2];
     bf16x8 pall[2 * kKT];
+    // p = exp2(S * scale * log2 e) (first pass) or exp2(S * scale * log2 e
+    // - m) (online pass) as bf16, and the
+    // row sum of the very bf16 weights the PV product uses, two per
+    // instruction (bf16 dot product with (1, 1), float32 accumulation)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int step = 0; step < 2 * kKT; ++step) {
       const int kt = step >> 1, hf = step & 1;
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        pall[step][r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * hf + r], sl2, -m_use));
-      // row sum of the very bf16 weights the PV product uses, two per
-      // instruction (bf16 dot product with (1, 1), float32 accumulation)
+      for (int r = 0; r < 8; ++r) {
+        const float x = ONLINE ? fmaf(s[kt][8 * hf + r], sl2, -m_use) : s[kt][8 * hf + r] * sl2;
+        pall[step][r] = (__bf16)__builtin_amdgcn_exp2f(x);
+      }
 #pragma unroll
       for (int r = 0; r < 8; r += 2) {
         const bf16x2 pp = {pall[step][r], pall[step][r + 1]};
@@ -387,22 +383,45 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     return kb_next;
   };
 
-  int kb = next_valid(0);
-  if (kb < cnt) {
-    issue_tile(Kx, Ks, block_of(kb), false);
-    issue_tile(Vx, Vs[0], block_of(kb), true);
-    wait_vmem();
+  // ---- the row, first without a max; again with one if any valid row of
+  // the workgroup left the accepted range of the row sum
+  __shared__ int rerun;
+  if (tid == 0) rerun = 0;
+  const int kb0 = next_valid(0);
+  auto run_row = [&](auto onlinec) {
+    int kb = kb0;
+    if (kb < cnt) {
+      issue_tile(Kx, Ks, block_of(kb), false);
+      issue_tile(Vx, Vs[0], block_of(kb), true);
+      wait_vmem();
+    }
+    lds_barrier();
+    while (kb < cnt) {
+      kb = process(std::integral_constant<int, 0>{}, onlinec, kb);
+      if (kb >= cnt) break;
+      kb = process(std::integral_constant<int, 1>{}, onlinec, kb);
+    }
+  };
+  run_row(std::false_type{});
+  {
+    const float lt = l_run + __shfl_xor(l_run, 32, 64);
+    const bool bad = qvalid && kb0 < cnt && !(lt >= kSumMin && lt <= kSumMax);
+    if (__any(bad) && lane == 0) rerun = 1;
   }
   lds_barrier();
-  while (kb < cnt) {
-    kb = process(std::integral_constant<int, 0>{}, kb);
-    if (kb >= cnt) break;
-    kb = process(std::integral_constant<int, 1>{}, kb);
+  if (rerun) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    l_run = 0.f;
+    m_use = -INFINITY;
+    run_row(std::true_type{});
   }
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool valid = qrow < N;
+  const bool valid = qvalid;
   const float inv = (valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   Tout* op = out + head_off + (size_t)qrow * kD;
 #pragma unroll
@@ -468,9 +487,9 @@ hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
                     static_cast<const uint16_t*>(k),
                     static_cast<const uint16_t*>(v), s, kept_idx, kept_cnt,
                     k_max, scale, out, lse, st);
-  return launch_t(static_cast<const float*>(q), static_cast<const float*>(k),
-                  static_cast<const float*>(v), s, kept_idx, kept_cnt, k_max,
-                  scale, out, lse, st);
+  return launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                         static_cast<const float*>(v), s, kept_idx, kept_cnt, k_max, scale,
+                         static_cast<float*>(out), lse, st);
 }
 
 }  // namespace ress

@@ -75,10 +75,13 @@ struct WsLayout {
 // ---------------------------------------------------------------- init
 // One wave per (row i, head h): D_i = candidates not in the keep list,
 // K = 1 - sum_{j in D} P_ij, and g_i = sum_{j in D} P_ij (vout_i - V_j)
-// (Eq. 5, 10) formed from the kept blocks S_i instead: sum over all j of
-// P_ij (vout_i - V_j) is zero (the row of P sums to one and vout_i is
-// sum_j P_ij V_j), so g_i = sum_{j in S_i} P_ij (V_j - vout_i), about an
-// order of magnitude fewer terms at high sparsity; the two agree to rounding.
+// (Eq. 5, 10). The sum over all j of P_ij (vout_i - V_j) is zero (the row of
+// P sums to one and vout_i is sum_j P_ij V_j), so g_i also equals
+// sum_{j in S_i} P_ij (V_j - vout_i) over the kept blocks, up to rounding. g
+// is summed over whichever of D and S has fewer blocks: S at high sparsity
+// (about a tenth of the terms at 90%), D when few blocks are dropped, where
+// the S form would leave a rounding residue of vout (~1e-16 |V|) that can
+// dwarf a g of dropped blocks of tiny probability. Both lists ascend.
 __global__ __launch_bounds__(64) void refine_init_kernel(
     const double* __restrict__ P, const double* __restrict__ vpool,
     const double* __restrict__ vout, const double* __restrict__ M, int n,
@@ -86,6 +89,8 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
     const int32_t* __restrict__ kept_cnt, RefineWs ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint8_t* flags = smem;                                                 // [n]
+  // kept blocks ascending from the front, dropped ones ascending from the
+  // back (entry n-1-q is the q-th dropped block)
   int32_t* slist = reinterpret_cast<int32_t*>(smem + ((n + 15) & ~15));  // [n]
   double* gl = reinterpret_cast<double*>(slist + ((n + 3) & ~3));        // [64]
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
   uint8_t* fb = ws.fbest + row * flag_stride(n);
   const uint64_t below = (1ull << lane) - 1ull;
   double ks = 0.0;
-  int nD = 0, nS = 0, pos = 0;
+  int nD = 0, nS = 0, pos = 0, dpos = 0;
   // the P row is read in batches of 8 chunks of 64 blocks (clamped
   // addresses, all loads in flight together); the sum takes the same order
   constexpr int kPre = 8;
@@ -131,6 +136,9 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
       const uint64_t msk = __ballot(kept);
       if (kept) slist[pos + __popcll(msk & below)] = j;
       pos += __popcll(msk);
+      const uint64_t dmsk = __ballot(inD);
+      if (inD) slist[n - 1 - (dpos + __popcll(dmsk & below))] = j;
+      dpos += __popcll(dmsk);
     }
   }
   const double K = 1.0 - wave_sum64(ks);
@@ -141,14 +149,21 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
   const int d = lane;
   const double vod = vout[row * kD + d];
   double acc = 0.0;
+  if (dpos < pos) {
+    // over D, Eq. 10 itself (an empty D: exactly zero)
 #pragma unroll 8
-  for (int q = 0; q < pos; ++q) {
-    const int j = slist[q];
-    acc += Prow[j] * (Vh[(size_t)j * kD + d] - vod);
+    for (int q = 0; q < dpos; ++q) {
+      const int j = slist[n - 1 - q];
+      acc += Prow[j] * (vod - Vh[(size_t)j * kD + d]);
+    }
+  } else {
+#pragma unroll 8
+    for (int q = 0; q < pos; ++q) {
+      const int j = slist[q];
+      acc += Prow[j] * (Vh[(size_t)j * kD + d] - vod);
+    }
   }
-  // the sum over S equals the one over D (Eq. 10) up to the rounding of
-  // vout; an empty D is the empty sum, exactly zero
-  const double g = nD > 0 ? acc : 0.0;
+  const double g = acc;
   gl[d] = g;
   wave_lds_sync();
   double G, vu;
@@ -316,6 +331,7 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
   const double* Vh = vpool + (size_t)h * n * kD;
   const double vod = vout[row * kD + d];
   double g = ws.g[row * kD + d];
+  double mag = fabs(g);  // what g is formed from, for the cancellation guard
   double dk = 0.0;
   // batches of 16 changes: all loads of a batch are issued before its sums
   for (int q0 = 0; q0 < nchg; q0 += 16) {
@@ -334,9 +350,12 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
       if (q0 + t >= nchg) break;
       const double dj = pv[t] * (vod - vv[t]);
       g = (ev[t] > 0) ? g + dj : g - dj;
+      mag += fabs(dj);
       dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
     }
   }
+  if (g_cancelled(g, mag))
+    g = g_from_sets([&](int j) { return flags[j] != 0; }, n, st.nD, Prow, Vh, vod);
   gl[d] = g;
   wave_lds_sync();
   double G, vu;

@@ -39,6 +39,33 @@ __device__ inline double gram_apply(const double* __restrict__ Mh, const double*
   return u;
 }
 
+// Cancellation guard of the incremental update of g (Eq. 13: each round g
+// moves by the d_j of the swapped blocks). When the result is below 2^-20 of
+// the magnitudes it was formed from (per dim: |g| before the round plus the
+// swapped |d_j|), the update has cancelled most of its bits (a drop set that
+// returns to blocks of tiny probability, say), and g is summed again from its
+// definition (Eq. 10): over the smaller of D and the kept blocks S (the sum of
+// d_j over all blocks is zero), ascending, as the starting state does. Its
+// rounding is then relative to g itself. Both refinement paths apply it.
+__device__ inline bool g_cancelled(double g, double mag) {
+  return wave_sum64(g * g) < 0x1p-40 * wave_sum64(mag * mag);
+}
+
+template <typename InD>
+__device__ inline double g_from_sets(InD in_drop, int n, int nD, const double* __restrict__ Prow,
+                                     const double* __restrict__ Vh, double vod) {
+  const int d = threadIdx.x & 63;
+  const bool overD = nD < n - nD;
+  double acc = 0.0;
+  for (int j = 0; j < n; ++j) {
+    if (in_drop(j) != overD) continue;  // the same block for every lane
+    const double pj = Prow[j];
+    const double vj = Vh[(size_t)j * kD + d];
+    acc += overD ? pj * (vod - vj) : pj * (vj - vod);
+  }
+  return acc;
+}
+
 // Bitwise AND / OR of a 64-bit value over the wave.
 __device__ inline uint64_t wave_and64(uint64_t v) {
 #pragma unroll

@@ -78,7 +78,8 @@ struct FusedLds {
 // the change dk of K, in batches of 8 whose loads are all issued before
 // their sums.
 __device__ __attribute__((always_inline)) void apply_changes(const int32_t* chg, int nchg, const double* Prow,
-                                     const double* Vh, double vod, double& g, double& dk) {
+                                     const double* Vh, double vod, double& g, double& mag,
+                                     double& dk) {
   const int d = threadIdx.x & 63;
   for (int q0 = 0; q0 < nchg; q0 += 8) {
     int ev[8];
@@ -96,6 +97,7 @@ __device__ __attribute__((always_inline)) void apply_changes(const int32_t* chg,
       if (q0 + t >= nchg) break;
       const double dj = pv[t] * (vod - vv[t]);
       g = (ev[t] > 0) ? g + dj : g - dj;
+      mag += fabs(dj);
       dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
     }
   }
@@ -145,7 +147,9 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
   double g = 0.0, vod = 0.0, Jbest = 0.0, J0 = 0.0, Kc = 1.0;
   int nD = 0, nS = 0;
   if (live) {
-    // scratch in this row's gains area: byte flags [fs], then kept list [n]
+    // scratch in this row's gains area: byte flags [fs], then the kept
+    // blocks ascending from the front of a list of n, the dropped ones
+    // ascending from its back (as the per-round path's init)
     uint8_t* flags = reinterpret_cast<uint8_t*>(myg);
     int32_t* slist = reinterpret_cast<int32_t*>(flags + flag_stride(n));
     for (int j = lane; j < n; j += 64) flags[j] = sel_always(cfg, j) ? 0 : 1;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
     }
     wave_lds_sync();
     double ks = 0.0;
-    int pos = 0;
+    int pos = 0, dpos = 0;
     for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
       const int j = j0 + lane;
       const bool in = j < n;
@@ -175,6 +179,8 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
       const uint64_t msk = __ballot(kept);
       if (kept) slist[pos + __popcll(msk & below)] = j;
       pos += __popcll(msk);
+      if (inD) slist[n - 1 - (dpos + __popcll(dm & below))] = j;
+      dpos += __popcll(dm);
     }
     Kc = 1.0 - wave_sum64(ks);
     nD = wave_isum64(nD);
@@ -182,21 +188,25 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
     wave_lds_sync();
     vod = vout[row * kD + d];
     double acc = 0.0;
-    // batches of 16 kept blocks, all loads of a batch issued before its
-    // sums, which keep the ascending order
-    for (int q0 = 0; q0 < pos; q0 += 16) {
+    // g over whichever of D and S has fewer blocks (Eq. 10 over D; over S
+    // by the zero total), ascending; batches of 16 blocks, all loads of a
+    // batch issued before its sums, which keep the order
+    const bool overD = dpos < pos;
+    const int len = overD ? dpos : pos;
+    for (int q0 = 0; q0 < len; q0 += 16) {
       double pv[16], vv[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int j = slist[min(q0 + t, pos - 1)];
+        const int qq = min(q0 + t, len - 1);
+        const int j = slist[overD ? n - 1 - qq : qq];
         pv[t] = Prow[j];
         vv[t] = Vh[(size_t)j * kD + d];
       }
 #pragma unroll
       for (int t = 0; t < 16; ++t)
-        if (q0 + t < pos) acc += pv[t] * (vv[t] - vod);
+        if (q0 + t < len) acc += overD ? pv[t] * (vod - vv[t]) : pv[t] * (vv[t] - vod);
     }
-    g = nD > 0 ? acc : 0.0;  // an empty D: the empty sum of Eq. 10
+    g = acc;  // an empty D: the empty sum of Eq. 10
     ul[d] = g;
     wave_lds_sync();
     double G, vu;
@@ -289,6 +299,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
       // changes in ascending block order, flushed kChgCap at a time; the
       // drop set loses the restores and gains the drops
       double dk = 0.0;
+      double mag = fabs(g);  // what g is formed from, for the cancellation guard
       int nchg = 0;
       for (int k = 0; k < KW; ++k) {
         const bool rb = (restore >> k) & 1ull, db = (drop >> k) & 1ull;
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
         if (msk == 0ull) continue;
         if (nchg + __popcll(msk) > kChgCap) {
           wave_lds_sync();
-          apply_changes(chg, nchg, Prow, Vh, vod, g, dk);
+          apply_changes(chg, nchg, Prow, Vh, vod, g, mag, dk);
           wave_lds_sync();
           nchg = 0;
         }
@@ -307,7 +318,10 @@ __global__ __launch_bounds__(kFThreads) void refine_fused_kernel(
         if (lane == 0) mycur[k] = (mycur[k] & ~rm) | dm;
       }
       wave_lds_sync();
-      apply_changes(chg, nchg, Prow, Vh, vod, g, dk);
+      apply_changes(chg, nchg, Prow, Vh, vod, g, mag, dk);
+      if (g_cancelled(g, mag))
+        g = g_from_sets([&](int j) { return ((mycur[j >> 6] >> (j & 63)) & 1ull) != 0; }, n, nD,
+                        Prow, Vh, vod);
       if (m > 0) {
         wave_lds_sync();
         ul[d] = g;

@@ -123,6 +123,10 @@ hipError_t launch_gram(const void* w_o, int dtype, int d_model, const ress_shape
 hipError_t launch_residual_drift(const void* os, const void* od, int dtype, const double* M,
                                  const ress_shape& s, double* drift, hipStream_t st);
 
+// float32 inputs: float32 matrix cores (attn_f32.hip)
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const ress_shape& s,
+                           const int32_t* kept_idx, const int32_t* kept_cnt, int32_t k_max,
+                           float scale, float* out, float* lse, hipStream_t st);
 hipError_t launch_attn(const void* q, const void* k, const void* v, int dtype,
                        const ress_shape& s, const int32_t* kept_idx,
                        const int32_t* kept_cnt, int32_t k_max, float scale,

@@ -30,6 +30,17 @@ from ._lib import (
 )
 
 
+def refine_path(shape: Shape, refine_impl: str) -> str:
+    """The refinement call used for ``refine_impl`` on ``shape``: "fused" rows
+    longer than REFINE_FUSED_MAX_BLOCKS key blocks take the per-round kernels
+    (the same results, bit for bit)."""
+    if refine_impl not in ("fused", "rounds"):
+        raise ValueError(refine_impl)
+    if refine_impl == "fused" and shape.nk > REFINE_FUSED_MAX_BLOCKS:
+        return "rounds"
+    return refine_impl
+
+
 class BlockSparseGlobalAttention:
     def __init__(self, shape: Shape, keep, always_keep, mode: str = "prob",
                  rounds: int = 0, rho: float = 0.5, eps: float = 1e-4,
@@ -41,13 +52,11 @@ class BlockSparseGlobalAttention:
         budget ``keep`` is then the cap). ``refine_impl``: "rounds"
         (ress_refine_dropset, kernels per round and a workspace; the faster
         one on the MI355X) or "fused" (ress_refine_dropset_fused, one kernel,
-        no workspace, rows of at most REFINE_FUSED_MAX_BLOCKS key blocks);
-        both give the same bits."""
-        if refine_impl not in ("fused", "rounds"):
-            raise ValueError(refine_impl)
-        if refine_impl == "fused" and rounds > 0 and shape.nk > REFINE_FUSED_MAX_BLOCKS:
-            raise ValueError(f"the fused refinement takes rows of at most "
-                             f"{REFINE_FUSED_MAX_BLOCKS} key blocks (n_k={shape.nk})")
+        no workspace, rows of at most REFINE_FUSED_MAX_BLOCKS key blocks;
+        longer rows fall back to the per-round kernels, as the fused
+        restoration kernel of ReSS Appendix E falls back to its unfused path
+        outside its limits); both give the same bits."""
+        refine_impl = refine_path(shape, refine_impl)
         if mode not in ("prob", "drift"):
             raise ValueError(mode)
         if rounds > 0 and mode != "drift":

@@ -293,9 +293,14 @@ int ress_gram_from_wo(const void* w_o, int dtype, int32_t d_model, ress_shape sh
  *   out[h][t] = sum_u softmax_u(scale q[h][t] . k[h][u]) v[h][u]
  *
  * over the valid keys u < N of the blocks kept_idx[h][i][0 .. kept_cnt-1]
- * of t's query block i. QK^T and PV run on bf16 matrix cores with float32
- * accumulation and a float32 online softmax; float32 inputs are rounded to
- * bf16 (nearest-even) when staged. Rows t >= N are written as zeros.
+ * of t's query block i. bf16 inputs: QK^T and PV run on bf16 matrix cores
+ * with float32 accumulation, the weights rounded to bf16 for PV (the row sum
+ * is taken over those same weights); a first pass takes the weights without
+ * subtracting a running max and is kept when every row sum lies in
+ * [2^-64, 2^64], else the workgroup reruns as a classical online softmax
+ * (same accuracy either way). float32 inputs: QK^T and PV on float32 matrix
+ * cores with float32 weights (float32 accuracy). Rows t >= N are written as
+ * zeros.
  *
  * Query block i holds tokens i*B .. i*B+B-1 and key block j tokens
  * j*Bk .. j*Bk+Bk-1. q, k, v: device [H][N_pad][D] of `dtype`. kept_idx:

@@ -97,3 +97,57 @@ def sample_blocks(H: int, n: int, count: int, seed: int = 0, must=()):
 
 def row_rms(x: np.ndarray) -> float:
     return float(math.sqrt(np.mean(np.square(x))))
+
+
+def worker_count() -> int:
+    """Threads for the oracle comparisons: the CPUs this process may use,
+    at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def parallel_map(fn, items, threads=None):
+    """fn over items on a thread pool, each BLAS call single-threaded (numpy
+    releases the GIL inside BLAS and large ufunc loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    with threadpool_limits(1), ThreadPoolExecutor(threads or worker_count()) as ex:
+        return list(ex.map(fn, items))
+
+
+def attention_parity(qf, kf, vf, kept, out, lse, N, B, Bk, scale, heads, chunk=64):
+    """Every valid query row of every query block of `heads`: the oracle's
+    masked attention (float64, one head at a time) against the GPU output and
+    log-sum-exp. Returns max-abs, mean-abs, rel-rms of O, the max-abs LSE
+    error and the number of query blocks compared; padded rows of `out` must
+    be zero."""
+    import oracle
+    n = qf.shape[1] // B
+    tasks = [(h, list(range(i0, min(n, i0 + chunk)))) for h in heads
+             for i0 in range(0, n, chunk)]
+
+    def one(task):
+        h, rows = task
+        sl = slice(h, h + 1)
+        O, L = oracle.masked_attention(qf[sl], kf[sl], vf[sl], kept[sl], N, B, scale,
+                                       blocks=[(0, i) for i in rows], Bk=Bk)
+        t0, t1 = rows[0] * B, min((rows[-1] + 1) * B, N)
+        if t1 <= t0:
+            return 0.0, 0.0, 0.0, 0.0, 0, 0.0, True
+        d = np.abs(out[h, t0:t1].astype(np.float64) - O[0, t0:t1])
+        dl = np.abs(lse[h, t0:t1].astype(np.float64) - L[0, t0:t1]) if lse is not None else \
+            np.zeros(1)
+        pad_ok = bool(np.all(out[h, t1:(rows[-1] + 1) * B] == 0))
+        return (float(d.max()), float(d.sum()), float(np.sum(d * d)),
+                float(np.sum(O[0, t0:t1] ** 2)), d.size, float(dl.max()), pad_ok)
+
+    res = parallel_map(one, tasks)
+    mx = max(r[0] for r in res)
+    cnt = sum(r[4] for r in res)
+    mean = sum(r[1] for r in res) / cnt
+    rel = math.sqrt(sum(r[2] for r in res) / sum(r[3] for r in res))
+    lmax = max(r[5] for r in res)
+    assert all(r[6] for r in res), "padded rows must be zero"
+    return mx, mean, rel, lmax, len(heads) * n

@@ -222,9 +222,14 @@ def test_fused_refine_argument_checks():
 
 def test_layer_argument_checks_before_any_allocation():
     import block_sparse_global_amd as b
+    from block_sparse_global_amd.layer import refine_path
     s = b.Shape(1, 1089 * 64, 1089 * 64, 64, 64)
-    with pytest.raises(ValueError, match="1088"):
-        b.BlockSparseGlobalAttention(s, [2], None, mode="drift", rounds=1, refine_impl="fused")
+    # rows beyond the fused kernel's limit fall back to the per-round kernels
+    assert refine_path(s, "fused") == "rounds"
+    assert refine_path(b.Shape(1, 1088 * 64, 1088 * 64, 64, 64), "fused") == "fused"
+    assert refine_path(s, "rounds") == "rounds"
+    with pytest.raises(ValueError):
+        refine_path(s, "auto")
     with pytest.raises(ValueError):
         b.BlockSparseGlobalAttention(s, [2], None, mode="drift", rounds=1, refine_impl="auto")
     with pytest.raises(ValueError, match="drift"):
