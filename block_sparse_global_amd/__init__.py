@@ -29,7 +29,9 @@ from ._lib import (  # noqa: F401
     ress_last_error,
     ress_refine_dropset,
     ress_refine_dropset_fused,
+    ress_refine_dropset_noalloc,
     REFINE_FUSED_MAX_BLOCKS,
+    RESS_NOALLOC_SCRATCH_BYTES,
     ress_refine_workspace_size,
     ress_residual_drift,
     ress_select_topk,

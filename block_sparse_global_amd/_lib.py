@@ -39,6 +39,7 @@ ENTRY_POINTS = (
     "ress_select_cdf",
     "ress_refine_dropset",
     "ress_refine_dropset_fused",
+    "ress_refine_dropset_noalloc",
     "ress_refine_workspace_size",
     "ress_gram_from_wo",
     "ress_head_budgets",
@@ -112,6 +113,9 @@ def _load():
     lib.ress_refine_dropset_fused.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
                                               ctypes.c_double, ctypes.c_double, i32, ip, ip,
                                               dp, dp, vp]
+    lib.ress_refine_dropset_noalloc.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
+                                                ctypes.c_double, ctypes.c_double, i32, ip, ip,
+                                                dp, dp, vp]
     lib.ress_refine_workspace_size.argtypes = [ress_shape]
     lib.ress_refine_workspace_size.restype = ctypes.c_size_t
     lib.ress_sparse_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, ress_shape, ip, ip, i32,
@@ -121,7 +125,7 @@ def _load():
     lib.ress_residual_drift.argtypes = [vp, vp, ctypes.c_int, dp, ress_shape, dp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
               "ress_select_cdf", "ress_refine_dropset", "ress_refine_dropset_fused",
-              "ress_sparse_attn_fwd",
+              "ress_refine_dropset_noalloc", "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ress_last_error.restype = ctypes.c_char_p
@@ -309,6 +313,32 @@ def ress_refine_dropset_fused(P, key, vpool, vout, M, shape: Shape, keep, always
     if alw_arr is not None and alw_arr.shape != (nk,):
         raise ValueError(f"always_keep must have shape ({nk},)")
     _check("ress_refine_dropset_fused", LIB.ress_refine_dropset_fused(
+        _ptr(P, "P", f64, (H, nq, nk)), _ptr(key, "key", f64, (H, nq, nk)),
+        _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(vout, "vout", f64, (H, nq, D)),
+        _ptr(M, "M", f64, (H, D, D)), shape.c(), keep_p, alw_p, int(rounds), float(rho),
+        float(eps), int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)),
+        _ptr(J_init, "J_init", f64, (H, nq)), _ptr(J_final, "J_final", f64, (H, nq)),
+        _stream(stream)))
+
+
+RESS_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ress_refine_dropset_noalloc(P, key, vpool, vout, M, shape: Shape, keep, always_keep,
+                                rounds: int, rho: float, eps: float, k_max: int, kept_idx,
+                                kept_cnt, J_init=None, J_final=None, stream=None):
+    """ress_refine_dropset with its state in the library's fixed per-GPU
+    scratch (no workspace, no allocation); calls on one GPU must not overlap."""
+    H, nq, nk, D = shape.H, shape.nq, shape.nk, shape.D
+    f64 = torch.float64
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
+    _check("ress_refine_dropset_noalloc", LIB.ress_refine_dropset_noalloc(
         _ptr(P, "P", f64, (H, nq, nk)), _ptr(key, "key", f64, (H, nq, nk)),
         _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(vout, "vout", f64, (H, nq, D)),
         _ptr(M, "M", f64, (H, D, D)), shape.c(), keep_p, alw_p, int(rounds), float(rho),

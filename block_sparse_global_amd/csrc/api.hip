@@ -321,6 +321,68 @@ int ress_refine_dropset_fused(const double* P, const double* key, const double* 
   return hip_status(e, "fused refine launch");
 }
 
+int ress_refine_dropset_noalloc(const double* P, const double* key, const double* vpool,
+                                const double* vout, const double* M, ress_shape shape,
+                                const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                                double rho, double eps, int32_t k_max, int32_t* kept_idx,
+                                int32_t* kept_cnt, double* J_init, double* J_final,
+                                void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(key);
+  REQUIRE_PTR(vpool);
+  REQUIRE_PTR(vout);
+  OPTIONAL_PTR(M);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  OPTIONAL_PTR(J_init);
+  OPTIONAL_PTR(J_final);
+  if (rounds < 0) return fail(RESS_ERR_INVALID_ARG, "rounds=%d < 0", rounds);
+  if (!(rho > 0.0 && rho <= 1.0))
+    return fail(RESS_ERR_INVALID_ARG, "rho must lie in (0, 1]");
+  if (!(eps > 0.0) || !isfinite(eps))
+    return fail(RESS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK) return rc;
+  // heads per group: the most whose refinement state fits the scratch
+  const size_t cap = RESS_NOALLOC_SCRATCH_BYTES;
+  int group = 0;
+  for (int g = shape.H; g >= 1; --g) {
+    ress_shape sg = shape;
+    sg.H = g;
+    if (ress::refine_workspace_bytes(sg) <= cap) {
+      group = g;
+      break;
+    }
+  }
+  if (group == 0) {
+    ress_shape s1 = shape;
+    s1.H = 1;
+    return fail(RESS_ERR_UNSUPPORTED,
+                "one head's refinement state takes %zu bytes, more than the %zu of the scratch",
+                ress::refine_workspace_bytes(s1), cap);
+  }
+  void* scratch = nullptr;
+  hipError_t e = ress::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "scratch address");
+  const size_t nq = ress::n_qblocks(shape), nk = ress::n_kblocks(shape), D = shape.D;
+  for (int h0 = 0; h0 < shape.H; h0 += group) {
+    ress_shape sg = shape;
+    sg.H = shape.H - h0 < group ? shape.H - h0 : group;
+    ress::SelConfig cg;
+    if ((rc = make_sel_config(sg, keep + h0, always_keep, k_max, &cg)) != RESS_OK) return rc;
+    const size_t hq = (size_t)h0 * nq;
+    e = ress::launch_refine(P + hq * nk, key + hq * nk, vpool + (size_t)h0 * nk * D,
+                            vout + hq * D, M ? M + (size_t)h0 * D * D : nullptr, sg, cg, rounds,
+                            rho, eps, k_max, kept_idx + hq * k_max, kept_cnt + hq,
+                            J_init ? J_init + hq : nullptr, J_final ? J_final + hq : nullptr,
+                            scratch, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "noalloc refine launch");
+  }
+  return ok();
+}
+
 size_t ress_refine_workspace_size(ress_shape shape) {
   if (check_shape(shape) != RESS_OK) return 0;
   ok();

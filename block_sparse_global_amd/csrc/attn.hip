@@ -125,7 +125,6 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     float scale, Tout* __restrict__ out, float* __restrict__ lse) {
   // n: key blocks (of KBLK keys) per head; gridDim.x: query blocks per head
   static_assert(KBLK <= BLK && BLK % KBLK == 0, "key blocks no larger than query blocks");
-  constexpr int kThreads = BLK * 2;  // BLK/32 waves of 64
   constexpr int kKT = KBLK / 32;     // 32-key tiles per key block
   constexpr int kTile = KBLK * kD;   // elements per K or V tile
   constexpr int kRowsPerWave = KBLK / (BLK / 32);  // tile rows each wave copies

@@ -123,6 +123,11 @@ hipError_t launch_gram(const void* w_o, int dtype, int d_model, const ress_shape
 hipError_t launch_residual_drift(const void* os, const void* od, int dtype, const double* M,
                                  const ress_shape& s, double* drift, hipStream_t st);
 
+// Device address of this GPU's fixed refinement scratch (noalloc.hip),
+// RESS_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned; looked up once per
+// device.
+hipError_t noalloc_scratch(void** ptr);
+
 // float32 inputs: float32 matrix cores (attn_f32.hip)
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const ress_shape& s,
                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t k_max,

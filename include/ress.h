@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RESS_VERSION 3
+#define RESS_VERSION 4
 
 /* Status codes. */
 #define RESS_OK 0
@@ -231,6 +231,33 @@ int ress_refine_dropset_fused(const double* P, const double* key, const double* 
                               double rho, double eps, int32_t k_max, int32_t* kept_idx,
                               int32_t* kept_cnt, double* J_init, double* J_final,
                               void* stream);
+
+/* Bytes of the fixed device scratch of ress_refine_dropset_noalloc (64 MiB;
+ * each GPU that loads the library holds one such array). */
+#define RESS_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * ress_refine_dropset_noalloc — ress_refine_dropset (same arguments apart
+ * from the workspace, same results bit for bit) for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation. Its refinement state lives in a fixed
+ * array of RESS_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU;
+ * the call allocates nothing and calls no allocating routine. The heads are
+ * refined in groups of as many heads as the scratch holds (the state of g
+ * heads takes ress_refine_workspace_size of the shape with H = g), one group
+ * after another on `stream`. RESS_ERR_UNSUPPORTED when a single head's state
+ * exceeds the scratch (about 10 n_q n_k + 1100 n_q bytes: square grids up to
+ * n = 2535 blocks fit; the 128 x 64 grid at 100 views takes 23 MB a head).
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU (other streams, other threads) race and give undefined results.
+ */
+int ress_refine_dropset_noalloc(const double* P, const double* key, const double* vpool,
+                                const double* vout, const double* M, ress_shape shape,
+                                const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                                double rho, double eps, int32_t k_max, int32_t* kept_idx,
+                                int32_t* kept_cnt, double* J_init, double* J_final,
+                                void* stream);
 
 /*
  * ress_refine_workspace_size — bytes of device workspace that

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_every_call():
     names = declared_functions()
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk", "ress_select_cdf",
-              "ress_refine_dropset", "ress_refine_dropset_fused", "ress_refine_workspace_size",
+              "ress_refine_dropset", "ress_refine_dropset_fused", "ress_refine_dropset_noalloc",
+              "ress_refine_workspace_size",
               "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
               "ress_last_error", "ress_version"):
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(b.LIB_PATH)
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in ress.h but not exported"
-    assert b.ress_version() == 3
+    assert b.ress_version() == 4
     assert set(b.ENTRY_POINTS) == set(declared_functions())
 
 
@@ -218,6 +219,34 @@ def test_fused_refine_argument_checks():
     assert call(s, eps=0.0) == -1 and "eps" in b.ress_last_error()
     assert call(s, k_max=2) == -1                     # k_max below a budget
     assert b.REFINE_FUSED_MAX_BLOCKS == 1088
+
+
+def test_noalloc_refine_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    d = ctypes.c_double
+    _, keep = _arr([2, 3], np.int32)
+    _, alw = _arr([0, 0, 0, 1], np.uint8)
+
+    def call(s, P=FAKE, keep=keep, alw=alw, rounds=2, rho=0.5, eps=1e-4, k_max=3):
+        return L.ress_refine_dropset_noalloc(P, FAKE, FAKE, FAKE, None, s, keep, alw, rounds,
+                                             d(rho), d(eps), k_max, FAKE, FAKE, None, None, None)
+    s = _shape(H=2)  # n = 4
+    assert call(s, P=None) == -1 and "P" in b.ress_last_error()
+    assert call(s, P=MISALIGNED) == -1 and "aligned" in b.ress_last_error()
+    assert call(s, rounds=-1) == -1 and "rounds" in b.ress_last_error()
+    assert call(s, rho=1.5) == -1 and "rho" in b.ress_last_error()
+    assert call(s, eps=0.0) == -1 and "eps" in b.ress_last_error()
+    assert call(s, k_max=2) == -1                     # k_max below a budget
+    # a single head whose refinement state exceeds the fixed scratch:
+    # unsupported, reported before any HIP call
+    big = _shape(H=1, N=2536 * 64, N_pad=2536 * 64)
+    _, keep1 = _arr([2], np.int32)
+    assert call(big, keep=keep1, alw=None, k_max=2) == -2
+    assert "scratch" in b.ress_last_error()
+    assert b.RESS_NOALLOC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert "#define RESS_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr
 
 
 def test_layer_argument_checks_before_any_allocation():
