@@ -34,6 +34,8 @@ from ._lib import (  # noqa: F401
     RESS_NOALLOC_SCRATCH_BYTES,
     ress_refine_workspace_size,
     ress_residual_drift,
+    ress_qkv_project,
+    ress_out_project,
     ress_select_topk,
     ress_select_cdf,
     ress_sparse_attn_fwd,

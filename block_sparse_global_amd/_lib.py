@@ -44,6 +44,8 @@ ENTRY_POINTS = (
     "ress_gram_from_wo",
     "ress_head_budgets",
     "ress_residual_drift",
+    "ress_qkv_project",
+    "ress_out_project",
     "ress_sparse_attn_fwd",
     "ress_last_error",
     "ress_version",
@@ -123,10 +125,13 @@ def _load():
     lib.ress_gram_from_wo.argtypes = [vp, ctypes.c_int, i32, ress_shape, dp, vp]
     lib.ress_head_budgets.argtypes = [vp, i32, i32, vp, ctypes.c_int64, vp]
     lib.ress_residual_drift.argtypes = [vp, vp, ctypes.c_int, dp, ress_shape, dp, vp]
+    lib.ress_qkv_project.argtypes = [vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp, vp, vp]
+    lib.ress_out_project.argtypes = [vp, vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
               "ress_select_cdf", "ress_refine_dropset", "ress_refine_dropset_fused",
               "ress_refine_dropset_noalloc", "ress_sparse_attn_fwd",
-              "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift"):
+              "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
+              "ress_qkv_project", "ress_out_project"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ress_last_error.restype = ctypes.c_char_p
     lib.ress_last_error.argtypes = []
@@ -393,3 +398,32 @@ def ress_sparse_attn_fwd(q, k, v, shape: Shape, kept_idx, kept_cnt, k_max: int,
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)) if kept_cnt is not None else None,
         int(k_max), float(scale), _ptr(out, "out", q.dtype, tok),
         _ptr(lse, "lse", torch.float32, (H, shape.N_pad)), _stream(stream)))
+
+
+def ress_qkv_project(x, w_qkv, b_qkv, shape: Shape, q, k, v, stream=None):
+    """q, k, v [H][N_pad][D] from x [N_pad][d_model] and a linear layer's weight
+    w_qkv [3 H D][d_model] (optional bias [3 H D]); bf16 tensors."""
+    if x.dim() != 2 or x.shape[0] != shape.N_pad:
+        raise ValueError(f"x must have shape [N_pad={shape.N_pad}][d_model]")
+    d_model = int(x.shape[1])
+    HD = shape.H * shape.D
+    tok = (shape.H, shape.N_pad, shape.D)
+    bf = torch.bfloat16
+    _check("ress_qkv_project", LIB.ress_qkv_project(
+        _ptr(x, "x", bf), _ptr(w_qkv, "w_qkv", bf, (3 * HD, d_model)),
+        _ptr(b_qkv, "b_qkv", bf, (3 * HD,)), _dtype_code(x), d_model, shape.c(),
+        _ptr(q, "q", bf, tok), _ptr(k, "k", bf, tok), _ptr(v, "v", bf, tok), _stream(stream)))
+
+
+def ress_out_project(o, w_o, b_o, residual, shape: Shape, y, stream=None):
+    """y [N_pad][d_model] = residual + b_o + o W_O^T, with o [H][N_pad][D] read as
+    [N_pad][H D] and W_O [d_model][H D]; y may be the residual tensor itself."""
+    if w_o.dim() != 2 or w_o.shape[1] != shape.H * shape.D:
+        raise ValueError(f"w_o must have shape [d_model][{shape.H * shape.D}]")
+    d_model = int(w_o.shape[0])
+    bf = torch.bfloat16
+    _check("ress_out_project", LIB.ress_out_project(
+        _ptr(o, "o", bf, (shape.H, shape.N_pad, shape.D)), _ptr(w_o, "w_o", bf),
+        _ptr(b_o, "b_o", bf, (d_model,)),
+        _ptr(residual, "residual", bf, (shape.N_pad, d_model)), _dtype_code(o), d_model,
+        shape.c(), _ptr(y, "y", bf, (shape.N_pad, d_model)), _stream(stream)))

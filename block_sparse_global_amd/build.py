@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libress.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.hip", "pool.hip", "score.hip", "select.hip", "refine.hip", "refine_fused.hip",
-           "attn.hip", "attn_f32.hip", "gram.hip", "drift.hip", "noalloc.hip"]
+           "attn.hip", "attn_f32.hip", "gram.hip", "drift.hip", "noalloc.hip", "proj.hip"]
 ARCH = "gfx950"
 
 

@@ -383,6 +383,57 @@ int ress_refine_dropset_noalloc(const double* P, const double* key, const double
   return ok();
 }
 
+namespace {
+
+int check_projection(int dtype, int32_t d_model) {
+  if (dtype != RESS_DTYPE_BF16)
+    return dtype == RESS_DTYPE_F32 ? fail(RESS_ERR_UNSUPPORTED, "projections take bf16 only")
+                                   : fail(RESS_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  if (d_model < 64 || d_model % 64 != 0 || d_model > 65536)
+    return fail(RESS_ERR_INVALID_ARG, "d_model=%d must be a positive multiple of 64, <= 65536",
+                d_model);
+  return RESS_OK;
+}
+
+}  // namespace
+
+int ress_qkv_project(const void* x, const void* w_qkv, const void* b_qkv, int dtype,
+                     int32_t d_model, ress_shape shape, void* q, void* k, void* v,
+                     void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_projection(dtype, d_model)) != RESS_OK) return rc;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_qkv);
+  OPTIONAL_PTR(b_qkv);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  hipError_t e = ress::launch_qkv_project(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qkv),
+      static_cast<const uint16_t*>(b_qkv), d_model, shape, static_cast<uint16_t*>(q),
+      static_cast<uint16_t*>(k), static_cast<uint16_t*>(v), static_cast<hipStream_t>(stream));
+  return hip_status(e, "qkv projection launch");
+}
+
+int ress_out_project(const void* o, const void* w_o, const void* b_o, const void* residual,
+                     int dtype, int32_t d_model, ress_shape shape, void* y, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if ((rc = check_projection(dtype, d_model)) != RESS_OK) return rc;
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(w_o);
+  OPTIONAL_PTR(b_o);
+  OPTIONAL_PTR(residual);
+  REQUIRE_PTR(y);
+  if (y == o || y == w_o) return fail(RESS_ERR_INVALID_ARG, "y must not alias o or w_o");
+  hipError_t e = ress::launch_out_project(
+      static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(w_o),
+      static_cast<const uint16_t*>(b_o), static_cast<const uint16_t*>(residual), d_model, shape,
+      static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream));
+  return hip_status(e, "output projection launch");
+}
+
 size_t ress_refine_workspace_size(ress_shape shape) {
   if (check_shape(shape) != RESS_OK) return 0;
   ok();

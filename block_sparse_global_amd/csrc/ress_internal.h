@@ -128,6 +128,14 @@ hipError_t launch_residual_drift(const void* os, const void* od, int dtype, cons
 // device.
 hipError_t noalloc_scratch(void** ptr);
 
+// QKV projection and output projection with residual add (proj.hip)
+hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w_qkv, const uint16_t* b_qkv,
+                              int d_model, const ress_shape& s, uint16_t* q, uint16_t* k,
+                              uint16_t* v, hipStream_t st);
+hipError_t launch_out_project(const uint16_t* o, const uint16_t* w_o, const uint16_t* b_o,
+                              const uint16_t* residual, int d_model, const ress_shape& s,
+                              uint16_t* y, hipStream_t st);
+
 // float32 inputs: float32 matrix cores (attn_f32.hip)
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const ress_shape& s,
                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t k_max,

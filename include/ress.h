@@ -363,6 +363,52 @@ int ress_sparse_attn_fwd(const void* q, const void* k, const void* v,
 int ress_residual_drift(const void* out_sparse, const void* out_dense, int dtype,
                         const double* M, ress_shape shape, double* drift, void* stream);
 
+/*
+ * ress_qkv_project — the QKV projection in front of the attention call: the
+ * per-head queries, keys and values the path consumes, from the token
+ * features of the attention sublayer (ReSS page §3, a pre-LN residual
+ * sublayer; §4.2 names the per-head Q, K, V). A linear layer y = x W^T + b
+ * with W = w_qkv, split by output channel c = which * H*D + h*D + d into
+ * q, k, v (which = 0, 1, 2) in the path's layout:
+ *
+ *   {q,k,v}[h][t][d] = b_qkv[c] + sum_e x[t][e] w_qkv[c][e]   (t < N)
+ *
+ * bf16 matrix cores with float32 accumulation, each output rounded once to
+ * bf16 (nearest even). Rows t >= N of q, k, v are written as zeros.
+ *
+ * x: device bf16 [N_pad][d_model]. w_qkv: device bf16 [3*H*D][d_model] (a
+ * linear layer's weight, [out][in]). b_qkv: device bf16 [3*H*D] or NULL.
+ * q, k, v: device bf16 [H][N_pad][D]. dtype: RESS_DTYPE_BF16 only.
+ * d_model: a positive multiple of 64, at most 65536.
+ */
+int ress_qkv_project(const void* x, const void* w_qkv, const void* b_qkv, int dtype,
+                     int32_t d_model, ress_shape shape, void* q, void* k, void* v,
+                     void* stream);
+
+/*
+ * ress_out_project — the output projection with the residual add behind the
+ * attention call: every head's output o^h enters the residual stream as
+ * W_O^h o^h (ReSS page §4.2 "Mapping to the residual space", Eq. 6 and 8;
+ * W_O^h is the slice of W_O that ress_gram_from_wo turns into M_h):
+ *
+ *   y[t][c] = residual[t][c] + b_o[c] + sum_{h,d} o[h][t][d] w_o[c][h*D + d]
+ *
+ * bf16 matrix cores with float32 accumulation; the sum, the bias and the
+ * residual are added in float32 and rounded once to bf16 (nearest even).
+ * Every row t < N_pad is computed (the attention call writes padded rows of
+ * o as zeros).
+ *
+ * o: device bf16 [H][N_pad][D] (ress_sparse_attn_fwd's output). w_o: device
+ * bf16 [d_model][H*D] (a linear layer's weight). b_o: device bf16 [d_model]
+ * or NULL. residual: device bf16 [N_pad][d_model] or NULL (then no residual
+ * is added). y: device bf16 [N_pad][d_model]; y may be the residual buffer
+ * itself (an in-place residual add: each element is read and then written by
+ * the same thread), but must not alias o or w_o. dtype: RESS_DTYPE_BF16
+ * only. d_model: a positive multiple of 64, at most 65536.
+ */
+int ress_out_project(const void* o, const void* w_o, const void* b_o, const void* residual,
+                     int dtype, int32_t d_model, ress_shape shape, void* y, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* ress_last_error(void);
 

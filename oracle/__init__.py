@@ -24,5 +24,7 @@ from .ress_oracle import (  # noqa: F401
     masked_attention,
     dense_attention,
     residual_drift,
+    qkv_project,
+    out_project,
     run_selection,
 )

@@ -496,6 +496,47 @@ def residual_drift(O_sparse, O_dense, M, N: int, B: int):
 
 
 # ---------------------------------------------------------------------------
+# The linear maps around the attention call (ReSS page §3: pre-LN residual
+# sublayer; §4.2 "Mapping to the residual space", Eq. 6 and 8)
+# ---------------------------------------------------------------------------
+
+def qkv_project(x, W, b, H: int, D: int, N: int):
+    """Per-head Q, K, V from the token features: the linear layer
+    y = x W^T + b with output channel c = which * H*D + h*D + d (which = 0, 1,
+    2 for Q, K, V). x: float64 [N_pad][d_model]; W: [3 H D][d_model]; b:
+    [3 H D] or None. Returns q, k, v float64 [H][N_pad][D], rows t >= N zero."""
+    y = x @ W.T
+    if b is not None:
+        y = y + b[None, :]
+    N_pad = x.shape[0]
+    out = []
+    for which in range(3):
+        t = np.zeros((H, N_pad, D), dtype=np.float64)
+        for h in range(H):
+            c0 = which * H * D + h * D
+            t[h, :N] = y[:N, c0:c0 + D]
+        out.append(t)
+    return tuple(out)
+
+
+def out_project(o, W, b, residual):
+    """The output projection with the residual add: head h's output o[h]
+    enters the residual stream as W_O^h o^h (Eq. 6, 8), W_O^h the columns
+    h*D .. h*D+D-1 of W [d_model][H D]:
+    y[t] = residual[t] + b + sum_h W_O^h o[h][t]. o: float64 [H][N_pad][D];
+    b: [d_model] or None; residual: [N_pad][d_model] or None."""
+    H, N_pad, D = o.shape
+    y = np.zeros((N_pad, W.shape[0]), dtype=np.float64)
+    for h in range(H):
+        y += o[h] @ W[:, h * D:(h + 1) * D].T
+    if b is not None:
+        y = y + b[None, :]
+    if residual is not None:
+        y = y + residual
+    return y
+
+
+# ---------------------------------------------------------------------------
 # The whole selection path for one workload
 # ---------------------------------------------------------------------------
 

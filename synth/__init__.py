@@ -21,5 +21,6 @@ from .gen import (  # noqa: F401
     make_inputs,
     make_gram,
     make_head_scores,
+    make_sublayer,
     make_wo,
 )

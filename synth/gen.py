@@ -147,6 +147,27 @@ def make_wo(heads: int, head_dim: int = 64, d_model: int = 1024, seed: int = 2,
     return f32_to_bf16_bits(w)
 
 
+def make_sublayer(n_tokens: int, heads: int, head_dim: int = 64, d_model: int = 1024,
+                  seed: int = 4):
+    """Random token features and linear-layer weights of one attention
+    sublayer, all rounded once to bf16 and returned as bf16 bit patterns
+    (uint16): x [n_tokens][d_model] ~ N(0, 1); w_qkv [3 H D][d_model] and
+    w_o [d_model][H D] with entries N(0, 1/d_model) and N(0, 1/(H D)), so
+    that projected values stay of order one; b_qkv [3 H D] and b_o [d_model]
+    ~ N(0, 0.1^2). They stand in for a trained layer and its inputs, which do
+    not exist here."""
+    rng = np.random.default_rng(seed)
+    hd = heads * head_dim
+    g = lambda shape, sd: f32_to_bf16_bits((rng.standard_normal(shape) * sd).astype(np.float32))
+    return {
+        "x": g((n_tokens, d_model), 1.0),
+        "w_qkv": g((3 * hd, d_model), d_model ** -0.5),
+        "b_qkv": g((3 * hd,), 0.1),
+        "w_o": g((d_model, hd), hd ** -0.5),
+        "b_o": g((d_model,), 0.1),
+    }
+
+
 def make_head_scores(heads: int, seed: int = 3, sigma: float = 0.5):
     """Random per-head importance scores, float64 [heads], log-normal
     exp(N(0, sigma^2)). Stand in for calibrated head scores (a Fisher trace

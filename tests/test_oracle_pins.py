@@ -777,3 +777,67 @@ def test_run_selection_equals_independent_steps_on_tokens(Bk):
             bmin = _brute_min_J(P[h, i], vp[h], np.eye(D), list(np.nonzero(cand)[0]),
                                 int(cand.sum()) - c)
             assert J1 >= bmin * (1 - 1e-9)
+
+
+# ---------------------------------------------------------------------------
+# The linear maps around the attention call (ReSS page §3, §4.2 Eq. 6 and 8)
+# ---------------------------------------------------------------------------
+
+def test_qkv_project_identity_permutation_and_bias():
+    H, D, N_pad, N = 2, 4, 9, 7
+    dm = 3 * H * D
+    x = rng(90).standard_normal((N_pad, dm))
+    # identity weights: q, k, v are slices of x, head-major
+    q, k, v = oracle.qkv_project(x, np.eye(dm), None, H, D, N)
+    for which, t in enumerate((q, k, v)):
+        for h in range(H):
+            c0 = which * H * D + h * D
+            assert np.array_equal(t[h, :N], x[:N, c0:c0 + D])
+            assert np.all(t[h, N:] == 0)
+    # a permutation of the weight rows permutes the output channels
+    perm = rng(91).permutation(dm)
+    qp, kp, vp = oracle.qkv_project(x, np.eye(dm)[perm], None, H, D, N)
+    flat = lambda a, b, c: np.concatenate([np.concatenate(list(t), axis=1) for t in (a, b, c)],
+                                          axis=1)  # [N_pad][3 H D] in channel order
+    assert np.array_equal(flat(qp, kp, vp)[:N], x[:N][:, perm])
+    # zero input: the bias alone
+    b = rng(92).standard_normal(dm)
+    q0, k0, v0 = oracle.qkv_project(np.zeros((N_pad, 5)), np.ones((dm, 5)), b, H, D, N)
+    assert np.array_equal(flat(q0, k0, v0)[:N], np.broadcast_to(b, (N, dm)))
+
+
+def test_out_project_sums_the_heads_and_adds_residual():
+    H, D, N_pad, dm = 3, 4, 6, 5
+    o = rng(93).standard_normal((H, N_pad, D))
+    W = rng(94).standard_normal((dm, H * D))
+    b = rng(95).standard_normal(dm)
+    res = rng(96).standard_normal((N_pad, dm))
+    y = oracle.out_project(o, W, b, res)
+    # element by element: residual + bias + sum over heads and dims
+    for t in range(N_pad):
+        for c in range(dm):
+            want = res[t, c] + b[c] + sum(o[h, t, d] * W[c, h * D + d]
+                                          for h in range(H) for d in range(D))
+            assert y[t, c] == pytest.approx(want, rel=1e-12, abs=1e-12)
+    # identity weights with d_model = H D: the heads concatenated
+    yi = oracle.out_project(o, np.eye(H * D), None, None)
+    assert np.array_equal(yi, np.concatenate(list(o), axis=1))
+
+
+def test_residual_stream_change_is_the_gram_norm():
+    # Eq. 6/8 at token level: changing head h's output by e moves the
+    # residual stream by W_O^h e, whose squared norm is e^T M_h e with M_h from
+    # gram_from_wo; residual_drift averages exactly that over a block
+    H, D, N_pad, B, dm = 2, 4, 8, 4, 6
+    W = rng(97).standard_normal((dm, H * D))
+    o_d = rng(98).standard_normal((H, N_pad, D))
+    o_s = o_d.copy()
+    o_s[1] += rng(99).standard_normal((N_pad, D))       # only head 1 differs
+    res = rng(100).standard_normal((N_pad, dm))
+    dy = oracle.out_project(o_s, W, None, res) - oracle.out_project(o_d, W, None, res)
+    M = oracle.gram_from_wo(W, H, D)
+    drift = oracle.residual_drift(o_s, o_d, M, N_pad, B)
+    for i in range(N_pad // B):
+        want = np.mean(np.sum(dy[i * B:(i + 1) * B] ** 2, axis=1))
+        assert drift[1, i] == pytest.approx(want, rel=1e-12)
+        assert drift[0, i] == 0.0
