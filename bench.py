@@ -143,6 +143,7 @@ def attn_traffic(workload):
 
 
 def time_events(fn, reps):
+    """Mean ms per call over `reps` back-to-back calls (one event pair)."""
     import torch
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -154,12 +155,73 @@ def time_events(fn, reps):
     return s.elapsed_time(e) / reps
 
 
+def time_median(fn, reps=20):
+    """Median ms of `reps` calls, each between its own pair of HIP events on
+    the launch stream (torch's current stream, which the binding passes)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def measured_peaks():
+    """This GPU's measured bf16 matrix-core rate and HBM copy bandwidth, next
+    to the published peaks: an MFMA loop (v_mfma_f32_32x32x16_bf16 on
+    independent accumulators, two workgroups of four waves per CU) with the
+    shader clock read from the core-cycle and 100 MHz counters, and a 2 GiB
+    device-to-device copy (read + write bytes)."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "block_sparse_global_amd", "libress_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.ress_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.ress_probe_mfma.restype = ctypes.c_int
+    props = torch.cuda.get_device_properties(0)
+    wgs = 2 * props.multi_processor_count
+    iters = 20000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert lib.ress_probe_mfma(wgs, iters, sink.data_ptr(), clocks.data_ptr(), st) == 0
+    run()
+    ms = time_median(run, 5)
+    flops = wgs * 4 * iters * 8 * (32 * 32 * 16 * 2)
+    cyc, ref = (int(v) for v in clocks.cpu().tolist())
+    clock_ghz = cyc / (ref / 100e6) / 1e9 if ref > 0 else None
+    nb = 1 << 31
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    cms = time_median(lambda: dst.copy_(src), 5)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": flops / (ms * 1e-3) / 1e12,
+            "shader_clock_ghz_under_mfma": clock_ghz,
+            "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 independent "
+                          f"v_mfma_f32_32x32x16_bf16, median of 5",
+            "hbm_copy_gbs": 2 * nb / (cms * 1e-3) / 1e9,
+            "hbm_probe": "2 GiB device-to-device copy (read + write), median of 5",
+            "published": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                          "clock_ghz": 2.4}}
+
+
 def stage_breakdown(layer, qkv, out, reps):
-    """Average ms per stage, HIP events between stages on the launch stream."""
+    """Median ms per stage over `reps` steps, HIP events between the stages on
+    the launch stream."""
     import torch
     q, k, v = qkv
     names = ["pool", "score", "select", "refine", "attend"]
-    acc = {n: 0.0 for n in names}
+    acc = {n: [] for n in names}
     for _ in range(reps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         ev[0].record()
@@ -170,8 +232,56 @@ def stage_breakdown(layer, qkv, out, reps):
         layer.attend(q, k, v, out); ev[5].record()
         torch.cuda.synchronize()
         for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1])
-    return {n: acc[n] / reps for n in names}
+            acc[n].append(ev[i].elapsed_time(ev[i + 1]))
+    return {n: float(np.median(acc[n])) for n in names}
+
+
+def scoring_memory(layer):
+    """Device bytes the selection step keeps besides Q, K, V and the output,
+    by buffer (the page's Table 1 reports the same quantity as scoring
+    memory): pooled blocks, the block map P and the key, the pooled output
+    and V^T M V, the keep lists, J, and the refinement workspace."""
+    parts = {}
+    for name in ("qpool", "kpool", "vpool", "P", "key", "vout", "vmv", "kept_idx", "kept_cnt",
+                 "J_init", "J_final", "workspace"):
+        t = getattr(layer, name, None)
+        if t is not None:
+            parts[name] = int(t.numel() * t.element_size())
+    return {"bytes": sum(parts.values()), "by_buffer": parts}
+
+
+def projections(w, reps=20):
+    """The linear maps around the attention call at this workload's token
+    count with a 1024-wide model (16 heads x 64): the QKV projection and the
+    output projection with the residual add, on synthetic bf16 weights;
+    median ms and TFLOP/s (2 N_pad d_model 3 H D and 2 N_pad d_model H D)."""
+    import torch
+
+    import block_sparse_global_amd as bsg
+    import synth
+    dm = 1024
+    shape = bsg.Shape(*w.shape_args())
+    L = synth.make_sublayer(w.N_pad, w.heads, w.head_dim, dm, seed=11)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+        torch.bfloat16).cuda()
+    x, wq, bq, wo, bo = (t(L[n]) for n in ("x", "w_qkv", "b_qkv", "w_o", "b_o"))
+    q, k, v = (torch.empty((w.heads, w.N_pad, w.head_dim), dtype=torch.bfloat16, device="cuda")
+               for _ in range(3))
+    y = torch.empty_like(x)
+    f_qkv = lambda: bsg.ress_qkv_project(x, wq, bq, shape, q, k, v)  # noqa: E731
+    f_out = lambda: bsg.ress_out_project(q, wo, bo, x, shape, y)  # noqa: E731
+    f_qkv()
+    f_out()
+    a, b = time_median(f_qkv, reps), time_median(f_out, reps)
+    fa = 2.0 * w.N_pad * dm * 3 * w.heads * w.head_dim
+    fb = 2.0 * w.N_pad * dm * w.heads * w.head_dim
+    res = {"d_model": dm, "qkv_ms": a, "qkv_tflops": fa / (a * 1e-3) / 1e12,
+           "out_ms": b, "out_tflops": fb / (b * 1e-3) / 1e12}
+    res["qkv_frac_of_peak"] = res["qkv_tflops"] / PEAK_BF16_TFLOPS
+    res["out_frac_of_peak"] = res["out_tflops"] / PEAK_BF16_TFLOPS
+    del x, wq, bq, wo, bo, q, k, v, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def refine_paths_ms(w, x, shape, layer, reps):
@@ -208,17 +318,20 @@ def refine_paths_ms(w, x, shape, layer, reps):
     return res
 
 
-def cpu_baseline(w, x, idx, cnt, budget_s=15.0):
-    """The oracle's masked attention on sampled query blocks with the GPU's
-    kept lists, until about budget_s seconds of CPU work; returns TFLOP/s."""
-    import oracle
-    import synth
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    rng = np.random.default_rng(11)
+        return len(os.sched_getaffinity(0))
+
+
+def _oracle_attention_rate(w, x, idx, cnt, budget_s, seed=11):
+    """The oracle's masked attention on random query blocks of w with the
+    GPU's kept lists, until about budget_s seconds: (TFLOP/s, blocks, s)."""
+    import oracle
+    import synth
+    rng = np.random.default_rng(seed)
     n, B = w.n_blocks, w.block
     qf = synth.as_f64(x["q"], w.dtype)
     kf = synth.as_f64(x["k"], w.dtype)
@@ -228,19 +341,76 @@ def cpu_baseline(w, x, idx, cnt, budget_s=15.0):
     flops, spent, blocks = 0.0, 0.0, 0
     while spent < budget_s and blocks < w.heads * n:
         h, i = int(rng.integers(w.heads)), int(rng.integers(n))
-        kept = np.zeros((w.heads, n, w.n_kblocks), bool)
-        kept[h, i, idx[h, i, : cnt[h, i]]] = True
+        kept = np.zeros((1, n, w.n_kblocks), bool)
+        kept[0, i, idx[h, i, : cnt[h, i]]] = True
         t0 = time.perf_counter()
-        oracle.masked_attention(qf, kf, vf, kept, w.N, B, 1.0 / math.sqrt(w.head_dim),
-                                blocks=[(h, i)], Bk=w.kblock)
+        oracle.masked_attention(qf[h:h + 1], kf[h:h + 1], vf[h:h + 1], kept, w.N, B,
+                                1.0 / math.sqrt(w.head_dim), blocks=[(0, i)], Bk=w.kblock)
         spent += time.perf_counter() - t0
         flops += 4.0 * w.head_dim * vq[i] * vk[idx[h, i, : cnt[h, i]]].sum()
         blocks += 1
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 numpy oracle, masked attention of {blocks} random query "
-                      f"blocks (kept lists from the GPU selection) of {w.name}, "
-                      f"{spent:.1f} s"}
+    return flops / spent / 1e12, blocks, spent
+
+
+def _oracle_selection_rate(w, x, rows_max=64, seed=12):
+    """The oracle's selection (pool -> map -> key -> top-k -> refine) for a
+    sample of query-block rows of w: pooling is timed over the whole tensors,
+    the per-row steps on the sampled rows. Returns seconds for the whole
+    workload (scaled from the sample) and the sample description."""
+    import oracle
+    import synth
+    rng = np.random.default_rng(seed)
+    f = lambda a: synth.as_f64(a, w.dtype)  # noqa: E731
+    t0 = time.perf_counter()
+    qp = oracle.block_pool(f(x["q"]), w.N, w.block)
+    kp = oracle.block_pool(f(x["k"]), w.N, w.kblock)
+    vp = oracle.block_pool(f(x["v"]), w.N, w.kblock) if w.score != "prob" else None
+    t_pool = time.perf_counter() - t0
+    H, n = w.heads, w.n_blocks
+    rows = sorted({(int(rng.integers(H)), int(rng.integers(n))) for _ in range(rows_max)})
+    t0 = time.perf_counter()
+    for h, i in rows:
+        P = oracle.block_map(qp[h:h + 1, i:i + 1], kp[h:h + 1], 1.0 / math.sqrt(w.head_dim))
+        if w.score == "prob":
+            key = P
+        else:
+            key, vout, _ = oracle.drift_key(P, vp[h:h + 1], None)
+        kept, _ = oracle.select_topk(key, x["keep"][h:h + 1], x["always"])
+        if w.rounds > 0 and w.score != "prob":
+            oracle.refine_dropset(P, vp[h:h + 1], vout, None, x["keep"][h:h + 1], x["always"],
+                                  kept, w.rounds, w.rho)
+    t_rows = time.perf_counter() - t0
+    total = t_pool + t_rows * (H * n) / len(rows)
+    return total, (f"pooling of all tokens ({t_pool:.1f} s) plus map, key, top-k"
+                   f"{' and refinement' if w.rounds else ''} of {len(rows)} random rows "
+                   f"({t_rows:.1f} s), scaled to all {H * n} rows")
+
+
+def cpu_baseline(w, x, idx, cnt, extra=(), budget_s=12.0):
+    """The oracle timed on the host: masked attention on a bounded sample of
+    query blocks of w (the headline figure, TFLOP/s on kept FLOPs), the
+    selection step scaled from a row sample, attention of the other
+    workloads in `extra` [(w, x, idx, cnt)], and a one-thread run on the
+    tiny and 8-view workloads."""
+    from threadpoolctl import threadpool_limits
+    threads = _oracle_threads()
+    rate, blocks, spent = _oracle_attention_rate(w, x, idx, cnt, budget_s)
+    sel_s, sel_what = _oracle_selection_rate(w, x)
+    res = {"value": rate, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"float64 numpy oracle, masked attention of {blocks} random query blocks "
+                     f"(kept lists from the GPU selection) of {w.name}, {spent:.1f} s",
+           "selection_s_full_workload": sel_s, "selection_sample": sel_what,
+           "per_workload": {}}
+    for w2, x2, i2, c2 in extra:
+        r2, b2, s2 = _oracle_attention_rate(w2, x2, i2, c2, 4.0)
+        entry = {"attention_tflops": r2, "blocks": b2, "seconds": s2}
+        if w2.name in ("tiny", "views8"):
+            with threadpool_limits(1):
+                r1, b1, s1 = _oracle_attention_rate(w2, x2, i2, c2, 3.0)
+                entry["attention_tflops_1_thread"] = r1
+                entry["selection_s_1_thread"] = _oracle_selection_rate(w2, x2, rows_max=16)[0]
+        res["per_workload"][w2.name] = entry
+    return res
 
 
 def residual_drift_report(w, x, shape, qkv, out, dense_out):
@@ -297,6 +467,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    peaks = measured_peaks()
     w, x, shape, layer, qkv, out = setup(args.workload)
     q, k, v = qkv
     step = lambda: layer(q, k, v, out)  # noqa: E731
@@ -306,13 +477,23 @@ def main():
     t_wall = time.perf_counter()
     ms_step = time_events(step, args.steps)
     t_wall = (time.perf_counter() - t_wall) / args.steps * 1e3
+    ms_step_median = time_median(step, max(20, args.steps))
 
     idx = layer.kept_idx.cpu().numpy()
     cnt = layer.kept_cnt.cpu().numpy()
     kf = kept_flops(w, idx, cnt)
-    stages = stage_breakdown(layer, qkv, out, max(3, args.steps // 2))
+    objective = None
+    if layer.rounds > 0:
+        J0, J1 = layer.J_init.cpu().numpy(), layer.J_final.cpu().numpy()
+        objective = {"J_init_mean": float(J0.mean()), "J_final_mean": float(J1.mean()),
+                     "J_final_over_J_init_mean": float(np.mean(J1 / J0)),
+                     "rows": int(J0.size)}
+    stages = stage_breakdown(layer, qkv, out, max(20, args.steps))
     refine_paths = refine_paths_ms(w, x, shape, layer, max(3, args.steps // 2))
-    attn_ms = time_events(lambda: layer.attend(q, k, v, out), args.steps)
+    attn_reps = max(20, args.steps)
+    attn_ms = time_events(lambda: layer.attend(q, k, v, out), attn_reps)
+    attn_median = time_median(lambda: layer.attend(q, k, v, out), attn_reps)
+    mem = scoring_memory(layer)
 
     import block_sparse_global_amd as bsg
     df = dense_flops(w)
@@ -334,8 +515,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    proj = None if args.no_sweep else projections(w)
 
     sweep = {}
+    cpu_extra = []
     if not args.no_sweep:
         # 8 / 32 / 100 views (the headline lines) and 200 views with both
         # scores; each line: layer time, dense time, the attention kernel alone
@@ -362,16 +545,19 @@ def main():
                 w2, x2, shape2, layer2, (q2, k2, v2), out2 = setup(
                     name, "prob" if mode == "cdf" else (None if mode == "hess" else mode),
                     x_in, tau=CDF_TAU if mode == "cdf" else None)
-                for _ in range(2):
+                for _ in range(3):
                     layer2(q2, k2, v2, out2)
-                reps = 3 if name == "views200" else 10
-                l_ms = time_events(lambda: layer2(q2, k2, v2, out2), reps)
-                a_ms = time_events(lambda: layer2.attend(q2, k2, v2, out2), reps)
-                s_ms = time_events(lambda: layer2.select(), reps)
+                reps = 5 if name == "views200" else 20
+                l_ms = time_median(lambda: layer2(q2, k2, v2, out2), reps)
+                a_ms = time_median(lambda: layer2.attend(q2, k2, v2, out2), reps)
+                s_ms = time_median(lambda: layer2.select(), reps)
+                idx2 = layer2.kept_idx.cpu().numpy()
                 cnt2 = layer2.kept_cnt.cpu().numpy()
-                kf2 = kept_flops(w2, layer2.kept_idx.cpu().numpy(), cnt2)
+                kf2 = kept_flops(w2, idx2, cnt2)
+                if mode is None and name in ("views8", "views32"):
+                    cpu_extra.append((w2, x2, idx2, cnt2))
                 d2 = torch.empty_like(q2)
-                d_ms = time_events(lambda: bsg.dense_attention(q2, k2, v2, shape2, d2),
+                d_ms = time_median(lambda: bsg.dense_attention(q2, k2, v2, shape2, d2),
                                    2 if name == "views200" else 5)
                 sweep[key] = {"layer_ms": l_ms, "dense_ms": d_ms, "attn_ms": a_ms,
                               "select_ms": s_ms, "kept_flop": kf2,
@@ -384,6 +570,10 @@ def main():
             e["speedup_vs_dense"] = e["dense_ms"] / e["layer_ms"]
             e["attn_tflops"] = e["kept_flop"] / (e["attn_ms"] * 1e-3) / 1e12
         x200 = None
+        # the tiny workload (float32 inputs) for the oracle's one-thread line
+        wt, xt, _, lt, qkvt, outt = setup("tiny")
+        lt(*qkvt, outt)
+        cpu_extra.insert(0, (wt, xt, lt.kept_idx.cpu().numpy(), lt.kept_cnt.cpu().numpy()))
 
     achieved = kf / (attn_ms * 1e-3) / 1e12
     res = {
@@ -409,10 +599,15 @@ def main():
             "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
             "traffic": attn_traffic(w.name), "traffic_unit": "bytes per launch (HBM, counters)",
-            "kernel": "attn_kernel<128, bf16> (ress_sparse_attn_fwd)",
-            "flop_per_launch": kf, "avg_launch_ms": attn_ms,
+            "kernel": "attn_kernel<128, 128> (ress_sparse_attn_fwd)",
+            "flop_per_launch": kf, "avg_launch_ms": attn_ms, "median_launch_ms": attn_median,
+            "launches_timed": attn_reps,
+            "measured_peak": peaks["mfma_bf16_tflops"],
+            "frac_of_measured_peak": achieved / peaks["mfma_bf16_tflops"],
         },
+        "measured_peaks": peaks,
         "layer_ms": ms_step,
+        "layer_ms_median": ms_step_median,
         "layer_ms_wall": t_wall,
         "dense_ms": None if args.no_dense else dense_ms,
         "dense_tflops": None if args.no_dense else df / (dense_ms * 1e-3) / 1e12,
@@ -422,13 +617,17 @@ def main():
         "kept_flop": kf,
         "realised_sparsity": sparsity_of(w, cnt),
         "stages_ms": stages,
+        "selection_ms": sum(stages[n] for n in ("pool", "score", "select", "refine")),
+        "refine_objective": objective,
+        "scoring_memory": mem,
         "refine_paths_ms": refine_paths,
+        "projections": proj,
         "views_sweep": sweep,
         "residual_drift": drift_report,
         "pages_context": PAGES_CONTEXT,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x, idx, cnt)
+        res["cpu_baseline"] = cpu_baseline(w, x, idx, cnt, extra=cpu_extra)
     print(json.dumps(res), flush=True)
 
 

@@ -38,6 +38,8 @@ from ._lib import (  # noqa: F401
     ress_out_project,
     ress_select_topk,
     ress_select_cdf,
+    ress_select_fused,
+    SELECT_FUSED_MAX_BLOCKS,
     ress_sparse_attn_fwd,
     ress_version,
 )

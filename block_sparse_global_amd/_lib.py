@@ -37,6 +37,7 @@ ENTRY_POINTS = (
     "ress_block_score",
     "ress_select_topk",
     "ress_select_cdf",
+    "ress_select_fused",
     "ress_refine_dropset",
     "ress_refine_dropset_fused",
     "ress_refine_dropset_noalloc",
@@ -109,6 +110,8 @@ def _load():
                                      ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, vp]
     lib.ress_select_topk.argtypes = [dp, ress_shape, ip, vp, i32, ip, ip, vp]
     lib.ress_select_cdf.argtypes = [dp, ress_shape, ip, vp, ctypes.c_double, i32, ip, ip, vp]
+    lib.ress_select_fused.argtypes = [dp, dp, dp, dp, ress_shape, ctypes.c_int, ctypes.c_double,
+                                      ctypes.c_double, ip, vp, i32, dp, ip, ip, vp]
     lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
                                         ctypes.c_double, ctypes.c_double, i32, ip, ip,
                                         dp, dp, vp, ctypes.c_size_t, vp]
@@ -128,7 +131,7 @@ def _load():
     lib.ress_qkv_project.argtypes = [vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp, vp, vp]
     lib.ress_out_project.argtypes = [vp, vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
-              "ress_select_cdf", "ress_refine_dropset", "ress_refine_dropset_fused",
+              "ress_select_cdf", "ress_select_fused", "ress_refine_dropset", "ress_refine_dropset_fused",
               "ress_refine_dropset_noalloc", "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
               "ress_qkv_project", "ress_out_project"):
@@ -261,6 +264,31 @@ def ress_select_cdf(P, shape: Shape, keep: Sequence[int], always_keep, tau: floa
     _check("ress_select_cdf", LIB.ress_select_cdf(
         _ptr(P, "P", torch.float64, (H, nq, nk)), shape.c(), keep_p, alw_p, float(tau),
         int(k_max), _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)), _stream(stream)))
+
+
+# key blocks per row up to which ress_select_fused applies
+SELECT_FUSED_MAX_BLOCKS = 2176
+
+
+def ress_select_fused(qpool, kpool, vpool, M, shape: Shape, mode: int, scale: float, eps: float,
+                      keep, always_keep, k_max: int, vmv, kept_idx, kept_cnt, stream=None):
+    """Score and top-k in one pass per row tile, the map and key on chip;
+    vmv [H][n_k] (drift) is written with V_j^T M V_j."""
+    H, nq, nk, D = shape.H, shape.nq, shape.nk, shape.D
+    f64 = torch.float64
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
+    _check("ress_select_fused", LIB.ress_select_fused(
+        _ptr(qpool, "qpool", f64, (H, nq, D)), _ptr(kpool, "kpool", f64, (H, nk, D)),
+        _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(M, "M", f64, (H, D, D)), shape.c(),
+        int(mode), float(scale), float(eps), keep_p, alw_p, int(k_max),
+        _ptr(vmv, "vmv", f64, (H, nk)),
+        _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)), _stream(stream)))
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libress.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.hip", "pool.hip", "score.hip", "select.hip", "refine.hip", "refine_fused.hip",
-           "attn.hip", "attn_f32.hip", "gram.hip", "drift.hip", "noalloc.hip", "proj.hip"]
+           "attn.hip", "attn_f32.hip", "gram.hip", "drift.hip", "noalloc.hip", "proj.hip", "select_fused.hip"]
 ARCH = "gfx950"
 
 
@@ -48,6 +48,17 @@ def command(out: str = LIB):
     ] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
+PROBE_LIB = os.path.join(HERE, "libress_probe.so")
+PROBE_SOURCES = [os.path.join("probe", "peak.hip")]
+
+
+def probe_command(out: str = PROBE_LIB):
+    """The benchmark's peak probe (libress_probe.so): not part of libress."""
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out] + \
+        [os.path.join(CSRC, s) for s in PROBE_SOURCES]
+
+
 def build(verbose: bool = False) -> str:
     """Compiles the library (always) and returns its path."""
     tmp = LIB + ".tmp"
@@ -64,6 +75,10 @@ def build(verbose: bool = False) -> str:
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     os.replace(tmp, LIB)
+    res = subprocess.run(probe_command(PROBE_LIB + ".tmp"), capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probe ({res.returncode}):\n{res.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

@@ -248,6 +248,43 @@ int ress_select_cdf(const double* P, ress_shape shape, const int32_t* keep,
   return hip_status(e, "cdf launch");
 }
 
+int ress_select_fused(const double* qpool, const double* kpool, const double* vpool,
+                      const double* M, ress_shape shape, int mode, double scale, double eps,
+                      const int32_t* keep, const uint8_t* always_keep, int32_t k_max,
+                      double* vmv, int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if (mode != RESS_SCORE_PROB && mode != RESS_SCORE_DRIFT)
+    return fail(RESS_ERR_INVALID_ARG, "bad score mode %d", mode);
+  if (ress::n_kblocks(shape) > ress::select_fused_max_blocks())
+    return fail(RESS_ERR_UNSUPPORTED, "n_k=%d key blocks exceed the %d of the fused selection",
+                ress::n_kblocks(shape), ress::select_fused_max_blocks());
+  REQUIRE_PTR(qpool);
+  REQUIRE_PTR(kpool);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  OPTIONAL_PTR(M);
+  const bool drift = mode == RESS_SCORE_DRIFT;
+  if (drift) {
+    REQUIRE_PTR(vpool);
+    REQUIRE_PTR(vmv);
+  }
+  if (!(scale > 0.0) || !isfinite(scale))
+    return fail(RESS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (drift && (!(eps > 0.0) || !isfinite(eps)))
+    return fail(RESS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (drift) e = ress::launch_vmv(vpool, M, shape, vmv, st);
+  if (e == hipSuccess)
+    e = ress::launch_select_fused(qpool, kpool, drift ? vpool : nullptr, M, drift ? vmv : nullptr,
+                                  shape, scale, eps, drift ? 1 : 0, cfg, k_max, kept_idx,
+                                  kept_cnt, st);
+  return hip_status(e, "fused selection launch");
+}
+
 int ress_refine_dropset(const double* P, const double* key,
                         const double* vpool, const double* vout,
                         const double* M, ress_shape shape, const int32_t* keep,

@@ -128,6 +128,15 @@ hipError_t launch_residual_drift(const void* os, const void* od, int dtype, cons
 // device.
 hipError_t noalloc_scratch(void** ptr);
 
+// Fused selection, pooled blocks to keep lists (select_fused.hip); rows of
+// at most select_fused_max_blocks() key blocks.
+int select_fused_max_blocks();
+hipError_t launch_select_fused(const double* qpool, const double* kpool, const double* vpool,
+                               const double* M, const double* vmv, const ress_shape& s,
+                               double scale, double eps, int drift, const SelConfig& cfg,
+                               int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
+                               hipStream_t st);
+
 // QKV projection and output projection with residual add (proj.hip)
 hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w_qkv, const uint16_t* b_qkv,
                               int d_model, const ress_shape& s, uint16_t* q, uint16_t* k,

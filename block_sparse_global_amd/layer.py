@@ -16,6 +16,7 @@ import torch
 
 from ._lib import (
     REFINE_FUSED_MAX_BLOCKS,
+    SELECT_FUSED_MAX_BLOCKS,
     RESS_SCORE_DRIFT,
     RESS_SCORE_PROB,
     Shape,
@@ -25,9 +26,24 @@ from ._lib import (
     ress_refine_dropset_fused,
     ress_refine_workspace_size,
     ress_select_cdf,
+    ress_select_fused,
     ress_select_topk,
     ress_sparse_attn_fwd,
 )
+
+
+def select_path(shape: Shape, select_impl: str, rounds: int, tau) -> str:
+    """The selection calls used for ``select_impl`` on ``shape``: "fused"
+    (ress_select_fused: score and top-k in one pass, the block map and key
+    never written) applies to top-k selection without refinement (the
+    refinement reads P and the key) on rows of at most SELECT_FUSED_MAX_BLOCKS
+    key blocks; otherwise ress_block_score + ress_select_topk / _cdf."""
+    if select_impl not in ("fused", "unfused"):
+        raise ValueError(select_impl)
+    if select_impl == "fused" and (rounds > 0 or tau is not None
+                                   or shape.nk > SELECT_FUSED_MAX_BLOCKS):
+        return "unfused"
+    return select_impl
 
 
 def refine_path(shape: Shape, refine_impl: str) -> str:
@@ -46,7 +62,7 @@ class BlockSparseGlobalAttention:
                  rounds: int = 0, rho: float = 0.5, eps: float = 1e-4,
                  scale: Optional[float] = None, M: Optional[torch.Tensor] = None,
                  device="cuda", with_lse: bool = False, tau: Optional[float] = None,
-                 refine_impl: str = "rounds"):
+                 refine_impl: str = "rounds", select_impl: str = "unfused"):
         """``tau`` switches the selection from top-k to the cumulative
         probability threshold (ress_select_cdf, probability scoring only; the
         budget ``keep`` is then the cap). ``refine_impl``: "rounds"
@@ -55,8 +71,13 @@ class BlockSparseGlobalAttention:
         no workspace, rows of at most REFINE_FUSED_MAX_BLOCKS key blocks;
         longer rows fall back to the per-round kernels, as the fused
         restoration kernel of ReSS Appendix E falls back to its unfused path
-        outside its limits); both give the same bits."""
+        outside its limits); both give the same bits. ``select_impl``:
+        "unfused" (ress_block_score then ress_select_topk) or "fused"
+        (ress_select_fused, the map and key never written; top-k selection
+        without refinement only, rows of at most SELECT_FUSED_MAX_BLOCKS key
+        blocks, else the unfused calls)."""
         refine_impl = refine_path(shape, refine_impl)
+        self.select_impl = select_path(shape, select_impl, int(rounds), tau)
         if mode not in ("prob", "drift"):
             raise ValueError(mode)
         if rounds > 0 and mode != "drift":
@@ -81,9 +102,10 @@ class BlockSparseGlobalAttention:
         self.kpool = torch.empty((H, nk, D), **f64)
         need_v = mode == "drift"
         self.vpool = torch.empty((H, nk, D), **f64) if need_v else None
-        self.P = torch.empty((H, nq, nk), **f64)
-        self.key = torch.empty((H, nq, nk), **f64) if mode == "drift" else None
-        self.vout = torch.empty((H, nq, D), **f64) if need_v else None
+        fused = self.select_impl == "fused"
+        self.P = None if fused else torch.empty((H, nq, nk), **f64)
+        self.key = torch.empty((H, nq, nk), **f64) if mode == "drift" and not fused else None
+        self.vout = torch.empty((H, nq, D), **f64) if need_v and not fused else None
         self.vmv = torch.empty((H, nk), **f64) if need_v else None
         self.kept_idx = torch.empty((H, nq, self.k_max), dtype=torch.int32, device=device)
         self.kept_cnt = torch.empty((H, nq), dtype=torch.int32, device=device)
@@ -103,12 +125,20 @@ class BlockSparseGlobalAttention:
                         self.qpool, self.kpool, self.vpool, stream)
 
     def score(self, stream=None):
+        if self.select_impl == "fused":
+            return  # the fused selection scores on chip
         mode = RESS_SCORE_DRIFT if self.mode == "drift" else RESS_SCORE_PROB
         ress_block_score(self.qpool, self.kpool, self.vpool, self.M, self.shape, mode,
                          self.scale, self.eps, self.P, self.key, self.vout, self.vmv,
                          stream)
 
     def select(self, stream=None):
+        if self.select_impl == "fused":
+            mode = RESS_SCORE_DRIFT if self.mode == "drift" else RESS_SCORE_PROB
+            ress_select_fused(self.qpool, self.kpool, self.vpool, self.M, self.shape, mode,
+                              self.scale, self.eps, self.keep, self.always, self.k_max,
+                              self.vmv, self.kept_idx, self.kept_cnt, stream)
+            return
         if self.tau is not None:
             ress_select_cdf(self.P, self.shape, self.keep, self.always, self.tau,
                             self.k_max, self.kept_idx, self.kept_cnt, stream)

@@ -145,6 +145,27 @@ int ress_select_topk(const double* key, ress_shape shape, const int32_t* keep,
                      int32_t* kept_idx, int32_t* kept_cnt, void* stream);
 
 /*
+ * ress_select_fused — ress_block_score followed by ress_select_topk as one
+ * pass per tile of query-block rows, the block map and the key of a row
+ * never leaving the chip (the fused, one-sweep-per-row selection of the ReSS
+ * page's Appendix E; §3 steps (1)-(2), §4.1-§4.2 Eq. 1-9). The same keep
+ * sets as the two calls (equal up to ties whose keys differ by float64
+ * rounding: the sums are taken in another fixed order).
+ *
+ * qpool, kpool, vpool, M, mode, scale, eps: as for ress_block_score (vpool
+ * and vmv required in drift mode, ignored in probability mode). keep,
+ * always_keep, k_max, kept_idx, kept_cnt: as for ress_select_topk. vmv:
+ * device float64 [H][n_k], written first with V_j^T M_h V_j (Eq. 9's last
+ * term, a vector per head; the only other buffer the call writes). Rows of
+ * at most 2176 key blocks (RESS_ERR_UNSUPPORTED beyond: use the two calls).
+ * Each workgroup keeps up to 156 KB of LDS.
+ */
+int ress_select_fused(const double* qpool, const double* kpool, const double* vpool,
+                      const double* M, ress_shape shape, int mode, double scale, double eps,
+                      const int32_t* keep, const uint8_t* always_keep, int32_t k_max,
+                      double* vmv, int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
  * ress_select_cdf — per (head, query-block row) keep set under a cumulative
  * probability (top-p, "CDF") threshold, with the per-head budget as a cap:
  * the probability selection the ReSS page compares against (related work on
