@@ -33,22 +33,22 @@ METRIC = "kept-block attention TFLOP/s + layer latency (ms) vs dense at 8/32/100
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes of one attention launch on the 100-view workload, from two
-# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch, median over dispatches), scaled by what the same counters read for
-# a 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0). The figures hold only
-# for the kernel source they were taken on; any other source reports null.
 # Cumulative-probability threshold of the "views100-cdf" line. The synthetic
 # pooled maps are flat (the 107 best of 1074 blocks hold ~10% of a row's
 # mass), so a threshold that binds below the 10% cap is small: 0.05 keeps
 # about 53 blocks per row, a data-dependent count (46..48 candidates + 5).
 CDF_TAU = 0.05
 
+# HBM bytes of one attention launch on the 100-view workload, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, median over dispatches), scaled by what the same counters read for
+# a 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0). The figures hold only
+# for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "f2550d696f457638dec8475fab88a1be5918e0440e6531ef6cb2d1160362011a",
-    "read_bytes": 4716950798,
-    "write_bytes": 281543328,
+    "source_sha256": "0996fb866fa51de9d5ab466ccd2055a1e07d3f79f19c75349a9628ac703f0b51",
+    "read_bytes": 8833912192,
+    "write_bytes": 334332960,
 }
 
 
@@ -203,14 +203,28 @@ def measured_peaks():
     dst = torch.empty_like(src)
     dst.copy_(src)
     cms = time_median(lambda: dst.copy_(src), 5)
-    del src, dst, sink
+    del dst
+    lib.ress_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.ress_probe_hbm_read.restype = ctypes.c_int
+    rwg = 8 * props.multi_processor_count
+    rsink = torch.empty(rwg * 256, dtype=torch.int32, device="cuda")
+
+    def read():
+        assert lib.ress_probe_hbm_read(src.data_ptr(), nb, rwg, rsink.data_ptr(), st) == 0
+    read()
+    rms = time_median(read, 5)
+    del src, sink, rsink
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": flops / (ms * 1e-3) / 1e12,
             "shader_clock_ghz_under_mfma": clock_ghz,
             "mfma_probe": f"{wgs} workgroups x 4 waves x {iters} x 8 independent "
                           f"v_mfma_f32_32x32x16_bf16, median of 5",
+            "hbm_read_gbs": nb / (rms * 1e-3) / 1e9,
             "hbm_copy_gbs": 2 * nb / (cms * 1e-3) / 1e9,
-            "hbm_probe": "2 GiB device-to-device copy (read + write), median of 5",
+            "hbm_probe": "2 GiB streaming read (non-temporal 16-byte loads, "
+                         f"{rwg} workgroups) and a 2 GiB device-to-device copy (read + write "
+                         "bytes), medians of 5",
             "published": {"mfma_bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
                           "clock_ghz": 2.4}}
 

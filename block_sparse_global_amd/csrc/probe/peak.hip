@@ -1,9 +1,11 @@
 // Measured peaks of this GPU for the benchmark's roofline lines, next to the
 // published ones: the bf16 matrix-core issue rate (v_mfma_f32_32x32x16_bf16,
-// the instruction of the attention kernel, on independent accumulators) and
-// the shader clock while it runs (s_memtime counts core cycles, s_memrealtime
-// a constant 100 MHz). Built into libress_probe.so, which only the benchmark
-// loads; it is not part of the attention library.
+// the instruction of the attention kernel, on independent accumulators), the
+// shader clock while it runs (s_memtime counts core cycles, s_memrealtime a
+// constant 100 MHz), and the HBM read bandwidth (a streaming sum over a
+// buffer much larger than the caches, non-temporal 16-byte loads). Built into
+// libress_probe.so, which only the benchmark loads; it is not part of the
+// attention library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,5 +54,36 @@ extern "C" int ress_probe_mfma(int workgroups, int iters, float* sink, unsigned 
                                void* stream) {
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(workgroups), dim3(256), 0,
                      static_cast<hipStream_t>(stream), iters, sink, clocks);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Every thread sums the 16-byte words i, i + stride, ... of the buffer (all
+// loads in flight in batches of 8); one partial per thread keeps them live.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                       unsigned int* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  unsigned int acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+extern "C" int ress_probe_hbm_read(const void* src, size_t bytes, int workgroups, void* sink,
+                                   void* stream) {
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(workgroups), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16,
+                     static_cast<unsigned int*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
