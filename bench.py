@@ -96,7 +96,7 @@ def dense_flops(w):
     return 4.0 * w.head_dim * w.heads * float(w.N) * float(w.N)
 
 
-def setup(name, mode=None, x=None, tau=None):
+def setup(name, mode=None, x=None, tau=None, select_impl="auto"):
     import torch
 
     import block_sparse_global_amd as bsg
@@ -112,7 +112,7 @@ def setup(name, mode=None, x=None, tau=None):
         mode = "drift" if w.score in ("drift", "both") else "prob"
     layer = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
                                            rounds=w.rounds if mode == "drift" else 0,
-                                           rho=w.rho, tau=tau)
+                                           rho=w.rho, tau=tau, select_impl=select_impl)
     out = torch.empty_like(q)
     return w, x, shape, layer, (q, k, v), out
 
@@ -262,6 +262,66 @@ def scoring_memory(layer):
         if t is not None:
             parts[name] = int(t.numel() * t.element_size())
     return {"bytes": sum(parts.values()), "by_buffer": parts}
+
+
+def select_paths(names=("views8", "views32"), reps=20):
+    """Score + top-k by the split calls (block map and key written, then
+    read back) and by the fused pass (ress_select_fused), median ms on the
+    same pooled blocks, with whether the two keep lists agree."""
+    import torch
+    res = {}
+    for name in names:
+        w, x, shape, a, qkv, _ = setup(name, select_impl="unfused")
+        _, _, _, b, _, _ = setup(name, x=x, select_impl="fused")
+        entry = {}
+        for impl, L in (("unfused", a), ("fused", b)):
+            L.pool(*qkv)
+
+            def run(L=L):
+                L.score()
+                L.select()
+            run()
+            entry[impl] = time_median(run, reps)
+        torch.cuda.synchronize()
+        entry["identical_lists"] = bool(torch.equal(a.kept_idx, b.kept_idx)
+                                        and torch.equal(a.kept_cnt, b.kept_cnt))
+        entry["key_blocks"] = shape.nk
+        res[name] = entry
+        del a, b, qkv
+        torch.cuda.empty_cache()
+    return res
+
+
+def budget_sweep(name, budgets, x=None, reps=10):
+    """The attention kernel alone at one workload's token count with a
+    uniform budget of c kept key blocks per row (probability top-k, the
+    always-kept blocks included), for each c: median ms and TFLOP/s, and a
+    least-squares line ms = fixed + per_block * c, which separates the cost
+    of one more kept block in every row from what a launch costs regardless
+    of the budget (reading Q, writing O, launch and ramp)."""
+    import torch
+
+    import synth
+    w = synth.get_workload(name)
+    if x is None:
+        x = synth.make_inputs(w)
+    pts = []
+    for c in budgets:
+        x2 = dict(x)
+        x2["keep"] = np.full(w.heads, int(c), dtype=np.int32)
+        _, _, _, lay, (q, k, v), out = setup(name, mode="prob", x=x2)
+        lay(q, k, v, out)
+        ms = time_median(lambda: lay.attend(q, k, v, out), reps)
+        kf = kept_flops(w, lay.kept_idx.cpu().numpy(), lay.kept_cnt.cpu().numpy())
+        pts.append({"keep": int(c), "attn_ms": ms, "tflops": kf / (ms * 1e-3) / 1e12})
+        del lay, q, k, v, out
+        torch.cuda.empty_cache()
+    cs = np.array([p["keep"] for p in pts], dtype=np.float64)
+    ms = np.array([p["attn_ms"] for p in pts])
+    per_block, fixed = np.polyfit(cs, ms, 1)
+    return {"workload": name, "points": pts, "fit_fixed_ms": float(fixed),
+            "fit_ms_per_kept_block": float(per_block),
+            "rows": int(w.heads * w.n_blocks)}
 
 
 def projections(w, reps=20):
@@ -530,8 +590,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     proj = None if args.no_sweep else projections(w)
+    sel_paths = None if args.no_sweep else select_paths()
 
     sweep = {}
+    budgets = None
     cpu_extra = []
     if not args.no_sweep:
         # 8 / 32 / 100 views (the headline lines) and 200 views with both
@@ -544,7 +606,9 @@ def main():
             key = name if mode is None else f"{name}-{mode}"
             if name == args.workload and mode is None and not args.no_dense:
                 sweep[key] = {"layer_ms": ms_step, "dense_ms": dense_ms, "attn_ms": attn_ms,
-                              "select_ms": stages["select"], "kept_flop": kf,
+                              "select_ms": stages["select"],
+                              "score_select_ms": stages["score"] + stages["select"],
+                              "select_impl": layer.select_impl, "kept_flop": kf,
                               "realised_sparsity": sparsity_of(w, cnt)}
             else:
                 if name == "views200" and x200 is None:
@@ -565,6 +629,7 @@ def main():
                 l_ms = time_median(lambda: layer2(q2, k2, v2, out2), reps)
                 a_ms = time_median(lambda: layer2.attend(q2, k2, v2, out2), reps)
                 s_ms = time_median(lambda: layer2.select(), reps)
+                ss_ms = time_median(lambda: (layer2.score(), layer2.select()), reps)
                 idx2 = layer2.kept_idx.cpu().numpy()
                 cnt2 = layer2.kept_cnt.cpu().numpy()
                 kf2 = kept_flops(w2, idx2, cnt2)
@@ -574,7 +639,8 @@ def main():
                 d_ms = time_median(lambda: bsg.dense_attention(q2, k2, v2, shape2, d2),
                                    2 if name == "views200" else 5)
                 sweep[key] = {"layer_ms": l_ms, "dense_ms": d_ms, "attn_ms": a_ms,
-                              "select_ms": s_ms, "kept_flop": kf2,
+                              "select_ms": s_ms, "score_select_ms": ss_ms,
+                              "select_impl": layer2.select_impl, "kept_flop": kf2,
                               "realised_sparsity": sparsity_of(w2, cnt2)}
                 if mode == "hess":
                     sweep[key]["keep_per_head"] = [int(b) for b in x2["keep"]]
@@ -584,6 +650,9 @@ def main():
             e["speedup_vs_dense"] = e["dense_ms"] / e["layer_ms"]
             e["attn_tflops"] = e["kept_flop"] / (e["attn_ms"] * 1e-3) / 1e12
         x200 = None
+        budgets = {"views8": budget_sweep("views8", (4, 8, 16, 32, 43, 64)),
+                   "views100": budget_sweep("views100", (8, 16, 32, 64, 107, 215),
+                                            x if args.workload == "views100" else None)}
         # the tiny workload (float32 inputs) for the oracle's one-thread line
         wt, xt, _, lt, qkvt, outt = setup("tiny")
         lt(*qkvt, outt)
@@ -636,6 +705,8 @@ def main():
         "scoring_memory": mem,
         "refine_paths_ms": refine_paths,
         "projections": proj,
+        "select_paths_ms": sel_paths,
+        "budget_sweep": budgets,
         "views_sweep": sweep,
         "residual_drift": drift_report,
         "pages_context": PAGES_CONTEXT,

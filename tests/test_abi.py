@@ -259,6 +259,23 @@ def test_layer_argument_checks_before_any_allocation():
     assert refine_path(s, "rounds") == "rounds"
     with pytest.raises(ValueError):
         refine_path(s, "auto")
+    from block_sparse_global_amd.layer import SELECT_FUSED_AUTO_MAX_BLOCKS, select_path
+    short = b.Shape(1, SELECT_FUSED_AUTO_MAX_BLOCKS * 64, SELECT_FUSED_AUTO_MAX_BLOCKS * 64,
+                    64, 64)
+    longer = b.Shape(1, (SELECT_FUSED_AUTO_MAX_BLOCKS + 1) * 64,
+                     (SELECT_FUSED_AUTO_MAX_BLOCKS + 1) * 64, 64, 64)
+    # "auto": the fused pass on short rows without refinement or threshold
+    assert select_path(short, "auto", 0, None) == "fused"
+    assert select_path(longer, "auto", 0, None) == "unfused"
+    assert select_path(short, "auto", 1, None) == "unfused"
+    assert select_path(short, "auto", 0, 0.5) == "unfused"
+    assert select_path(longer, "fused", 0, None) == "fused"
+    assert select_path(s, "fused", 0, None) == "fused"
+    assert select_path(b.Shape(1, 2177 * 64, 2177 * 64, 64, 64), "fused", 0, None) == "unfused"
+    assert select_path(short, "fused", 2, None) == "unfused"
+    assert select_path(short, "unfused", 0, None) == "unfused"
+    with pytest.raises(ValueError):
+        select_path(short, "fast", 0, None)
     with pytest.raises(ValueError):
         b.BlockSparseGlobalAttention(s, [2], None, mode="drift", rounds=1, refine_impl="auto")
     with pytest.raises(ValueError, match="drift"):

@@ -67,8 +67,10 @@ def run_gpu(w, x, mode, M=None, stream=None, blocks_out=True):
     shape = b.Shape(*w.shape_args())
     rounds = w.rounds if mode == "drift" else 0
     Mt = torch.from_numpy(M).cuda() if M is not None else None
+    # the split score and top-k calls, whose block map and key are compared too
     layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=mode,
-                                         rounds=rounds, rho=w.rho, M=Mt, with_lse=True)
+                                         rounds=rounds, rho=w.rho, M=Mt, with_lse=True,
+                                         select_impl="unfused")
     q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
     out = torch.empty_like(q)
     layer.pool(q, k, v, stream)
