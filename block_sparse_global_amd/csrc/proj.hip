@@ -8,17 +8,18 @@
 // stream as W_O^h o^h).
 //
 // Both are C[M][Nc] = A[M][K] B[Nc][K]^T with K contiguous in both operands
-// (a linear layer's weight is [out][in]): 128 x 128 output tiles, k-tiles of
-// 32, four waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16 tiles each,
-// float32 accumulation), four workgroups per CU. The products are formed as
-// C^T (the weight rows as the MFMA's A operand), so each lane ends up with
-// four consecutive output channels of one token and stores them with one
-// 8-byte write. Operand tiles are staged in LDS, double-buffered, row-major
-// (64-byte rows of four 16-byte chunks) with the chunk index XORed by
-// (row >> 2) & 3, so that the operand reads (16 rows at one logical chunk per
-// 16-lane pass) are bank-conflict free; the next k-tile's global loads are in
-// flight while the current one is multiplied. The operand loaders and the
-// epilogue differ per map:
+// (a linear layer's weight is [out][in]), v_mfma_f32_32x32x16_bf16 with
+// float32 accumulation, in one of two tile shapes:
+//  * 256 x 256 output tiles, eight waves of 128 x 64 (4 x 2 MFMA tiles), one
+//    workgroup per CU, for products with at least four such tiles per CU;
+//  * 128 x 128 output tiles, four waves of 64 x 64, three workgroups per CU,
+//    for smaller ones (the big tile leaves CUs idle there).
+// The products are formed as C^T (the weight rows as the MFMA's A operand),
+// so each lane ends up with four consecutive output channels of one token
+// and stores them with one 8-byte write. k-tiles of 32 pass through a ring
+// of three LDS stages, copied straight from global memory (global_load_lds):
+// two k-tiles are in flight while one is multiplied. The operand loaders and
+// the epilogue differ per map:
 //  * QKV: A = x [N_pad][d_model]; B = W_qkv [3 H D][d_model]; output channel
 //    c = which * H D + h D + d goes to {q,k,v}[which][h][t][d] (the
 //    [H][N_pad][D] layout of the path), plus the bias; rows t >= N are
@@ -27,6 +28,8 @@
 //    (the columns of k-tile pair 2h, 2h+1 are head h's D); B = W_O
 //    [d_model][H D]; y[t][c] = residual[t][c] + bias[c] + sum_k A[t][k]
 //    W_O[c][k], rounded once to bf16.
+#include <type_traits>
+
 #include "ress_internal.h"
 
 namespace ress {
@@ -35,10 +38,24 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kThreads = 256;
-constexpr int kChunksPerTile = kBM * kBK / 8;                 // 16-byte chunks
-constexpr int kChunksPerThread = kChunksPerTile / kThreads;   // 2
-constexpr int kRowChunks = kBK / 8;                          // 16-byte chunks per row
+// WGM x WGN waves per workgroup, each wave owning TM x TN sub-tiles of
+// 32 x 32 outputs (TM along the tokens, TN along the output channels).
+template <int WGM, int WGN, int TM, int TN>
+struct TileCfg {
+  static constexpr int kWGM = WGM, kWGN = WGN, kTM = TM, kTN = TN;
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kBM = 32 * WGM * TM, kBN = 32 * WGN * TN;
+  static constexpr int kThreads = 64 * kWaves;
+  // a copy window is 16 tile rows x 64 bytes (1 KB), one 16-byte copy per
+  // lane; windows of each operand per wave
+  static constexpr int kWinA = kBM / 16 / kWaves, kWinB = kBN / 16 / kWaves;
+  static constexpr int kWinPerWave = kWinA + kWinB;
+  static_assert(kBM % (16 * kWaves) == 0 && kBN % (16 * kWaves) == 0,
+                "whole copy windows of each operand per wave");
+};
+using BigTile = TileCfg<2, 4, 4, 2>;    // 256 x 256, 8 waves
+using SmallTile = TileCfg<2, 2, 2, 2>;  // 128 x 128, 4 waves
+constexpr int kBK = 32;
 
 __device__ inline int swz(int row) { return (row >> 2) & 3; }
 
@@ -47,91 +64,166 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// C[M][Nc] = A B^T over K (a multiple of 32). la(row, k) / lb(row, k): the
-// 16 bytes of 8 consecutive k of a row (row < M, resp. < Nc; k a multiple of
-// 8). st(m, n, acc[4]): the epilogue of outputs (m, n .. n+3) (m < M; n a
-// multiple of 4, n + 3 < Nc, which holds as Nc is a multiple of 64).
-template <class LoadA, class LoadB, class Store>
-__global__ __launch_bounds__(kThreads, 4) void gemm_nt_kernel(int M, int Nc, int K, LoadA la,
-                                                              LoadB lb, Store st) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// 16 bytes global -> LDS without registers; lane l of the wave writes the
+// 16 bytes at `window` + 16 * l (window is wave-uniform). Issued as inline
+// assembly, which produces no register and which the compiler does not count
+// as an outstanding load: the kernel waits for these copies itself
+// (wait_vmem), so that one stage can be read while the copies into the next
+// two are in flight (the compiler, tracking the copies itself, waits for all
+// of them before any LDS read). The compiler's own vmcnt waits stay correct,
+// only stricter: the copies complete in issue order with its loads.
+__device__ inline void gload_lds16(const uint16_t* g, uint16_t* window) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)window);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+// waits until at most N of this wave's vector memory operations are in flight
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the LDS stages: waits for this wave's LDS reads (not
+// for copies still in flight, which wait_vmem covers) and keeps the compiler
+// from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// C[M][Nc] = A B^T over K (a multiple of 64). la.ptr(row, k) / lb.ptr(row,
+// k): the address of 8 consecutive k of a row (row < M, resp. < Nc; k a
+// multiple of 8; 16-byte aligned). st(m, n, acc[4]): the epilogue of outputs
+// (m, n .. n+3) (m < M; n a multiple of 4, n + 3 < Nc, which holds as Nc is a
+// multiple of 64).
+//
+// Operand tiles are row-major in LDS (64-byte rows of four 16-byte chunks,
+// the chunk index XORed by (row >> 2) & 3 so that the operand reads, 16 rows
+// at one logical chunk per 16-lane pass, are bank-conflict free). In a copy
+// window of 16 rows lane l fills row l / 4 at physical chunk l % 4, i.e.
+// logical chunk (l % 4) ^ (l / 16). The three stages are separate LDS arrays
+// named at compile time.
+template <class Cfg, int MINB, class LoadA, class LoadB, class Store>
+__global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int Nc, int K,
+                                                                     LoadA la, LoadB lb,
+                                                                     Store st) {
+  constexpr int kTM = Cfg::kTM, kTN = Cfg::kTN, kWGN = Cfg::kWGN, kWaves = Cfg::kWaves;
+  constexpr int kBM = Cfg::kBM, kBN = Cfg::kBN;
+  constexpr int kWinA = Cfg::kWinA, kWinB = Cfg::kWinB;
+  __shared__ __attribute__((aligned(16))) uint16_t As0[kBM * kBK], As1[kBM * kBK], As2[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBN * kBK], Bs1[kBN * kBK], Bs2[kBN * kBK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / kWGN, wn = w % kWGN;
   // column tiles vary fastest: consecutive workgroups share the A rows
   const int n_tiles = (Nc + kBN - 1) / kBN;
   const int m0 = (blockIdx.x / n_tiles) * kBM, n0 = (blockIdx.x % n_tiles) * kBN;
+  const int crow = lane >> 2, cchunk = (lane & 3) ^ (lane >> 4);
 
-  uint4 ra[kChunksPerThread], rb[kChunksPerThread];
-  auto load = [&](int k0) {
+  // the copies of k-tile kt into stage S: A windows w, w + kWaves, ... and
+  // B windows likewise
+  auto issue = [&](auto stagec, int kt) {
+    constexpr int S = decltype(stagec)::value;
+    uint16_t* const as = S == 0 ? As0 : (S == 1 ? As1 : As2);
+    uint16_t* const bs = S == 0 ? Bs0 : (S == 1 ? Bs1 : Bs2);
+    const int k = kt * kBK + 8 * cchunk;
 #pragma unroll
-    for (int u = 0; u < kChunksPerThread; ++u) {
-      const int q = tid + kThreads * u, row = q / kRowChunks, c = q % kRowChunks;
-      ra[u] = la(min(m0 + row, M - 1), k0 + 8 * c);
-      rb[u] = lb(min(n0 + row, Nc - 1), k0 + 8 * c);
+    for (int u = 0; u < kWinA; ++u) {
+      const int v = w + kWaves * u;  // wave-uniform
+      gload_lds16(la.ptr(min(m0 + 16 * v + crow, M - 1), k), as + 16 * v * kBK);
+    }
+#pragma unroll
+    for (int u = 0; u < kWinB; ++u) {
+      const int v = w + kWaves * u;
+      gload_lds16(lb.ptr(min(n0 + 16 * v + crow, Nc - 1), k), bs + 16 * v * kBK);
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kChunksPerThread; ++u) {
-      const int q = tid + kThreads * u, row = q / kRowChunks, c = q % kRowChunks;
-      const int off = row * kBK + ((c ^ swz(row)) << 3);
-      *reinterpret_cast<uint4*>(&As[buf][off]) = ra[u];
-      *reinterpret_cast<uint4*>(&Bs[buf][off]) = rb[u];
-    }
-  };
 
-  f32x16 acc[2][2];
+  f32x16 acc[kTM][kTN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kTM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kTN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int nk = K / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
+  // the products of one stage; the operands of 16-k step ks + 1 are read
+  // while step ks's MFMAs issue
+  auto compute = [&](auto stagec) {
+    constexpr int S = decltype(stagec)::value;
+    const uint16_t* const as = S == 0 ? As0 : (S == 1 ? As1 : As2);
+    const uint16_t* const bs = S == 0 ? Bs0 : (S == 1 ? Bs1 : Bs2);
+    bf16x8 af[2][kTM], bfr[2][kTN];
+    auto read = [&](int ks, bf16x8 (&a)[kTM], bf16x8 (&b)[kTN]) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int ra_row = 64 * wm + 32 * t + l32, rb_row = 64 * wn + 32 * t + l32;
-        af[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                               &As[buf][ra_row * kBK + (((2 * ks + half) ^ swz(ra_row)) << 3)]));
-        bfr[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                                &Bs[buf][rb_row * kBK + (((2 * ks + half) ^ swz(rb_row)) << 3)]));
+      for (int t = 0; t < kTM; ++t) {
+        const int r = 32 * (kTM * wm + t) + l32;
+        a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                              &as[r * kBK + (((2 * ks + half) ^ swz(r)) << 3)]));
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int t = 0; t < kTN; ++t) {
+        const int r = 32 * (kTN * wn + t) + l32;
+        b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                              &bs[r * kBK + (((2 * ks + half) ^ swz(r)) << 3)]));
+      }
+    };
+    read(0, af[0], bfr[0]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[b], af[a], acc[a][b], 0, 0, 0);
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      if (ks + 1 < kBK / 16) read(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keeps those reads ahead of the MFMAs
+#pragma unroll
+      for (int a = 0; a < kTM; ++a)
+#pragma unroll
+        for (int b = 0; b < kTN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ks & 1][b], af[ks & 1][a],
+                                                             acc[a][b], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+  };
+
+  // one k-tile from stage S: wait for its copies (the next tile's may stay in
+  // flight), a barrier (every wave's copies have landed, and every wave is
+  // done with the stage the copies of tile kt + 2 go to), those copies, the
+  // products
+  const int nk = K / kBK;
+  auto step = [&](auto stagec, int kt) {
+    constexpr int S = decltype(stagec)::value;
+    if (kt + 1 < nk) wait_vmem<Cfg::kWinPerWave>(); else wait_vmem<0>();
+    lds_barrier();
+    if (kt + 2 < nk) issue(std::integral_constant<int, (S + 2) % 3>{}, kt + 2);
+    compute(stagec);
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
+  for (int kt = 0;;) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (++kt >= nk) break;
+    step(std::integral_constant<int, 1>{}, kt);
+    if (++kt >= nk) break;
+    step(std::integral_constant<int, 2>{}, kt);
+    if (++kt >= nk) break;
   }
 
   // accumulator element r of lane l (C^T): output channel n = 8(r/4) +
   // 4(l/32) + r%4 of the sub-tile, token m = l%32, so r = 4g .. 4g+3 are four
   // consecutive channels of one token
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int m = m0 + 64 * wm + 32 * a + l32;
+  for (int a = 0; a < kTM; ++a) {
+    const int m = m0 + 32 * (kTM * wm + a) + l32;
     if (m >= M) continue;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kTN; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 64 * wn + 32 * b + 8 * g + 4 * half;
+        const int n = n0 + 32 * (kTN * wn + b) + 8 * g + 4 * half;
         if (n < Nc) {
           const float v[4] = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
                               acc[a][b][4 * g + 3]};
@@ -144,17 +236,15 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_nt_kernel(int M, int Nc, int
 struct RowMajorLoad {  // X[row][k], row stride ld (elements)
   const uint16_t* X;
   int ld;
-  __device__ uint4 operator()(int row, int k) const {
-    return *reinterpret_cast<const uint4*>(X + (size_t)row * ld + k);
-  }
+  __device__ const uint16_t* ptr(int row, int k) const { return X + (size_t)row * ld + k; }
 };
 
 struct HeadMajorLoad {  // o[h][t][d] read as A[t][h D + d] (8 k never cross a head)
   const uint16_t* o;
   int N_pad;
-  __device__ uint4 operator()(int t, int k) const {
+  __device__ const uint16_t* ptr(int t, int k) const {
     const int h = k >> 6, d = k & 63;
-    return *reinterpret_cast<const uint4*>(o + ((size_t)h * N_pad + t) * 64 + d);
+    return o + ((size_t)h * N_pad + t) * 64 + d;
   }
 };
 
@@ -212,9 +302,17 @@ struct OutStore {
 
 template <class LA, class LB, class ST>
 hipError_t launch_gemm(int M, int Nc, int K, LA la, LB lb, ST st, hipStream_t stream) {
-  const int tiles = ((M + kBM - 1) / kBM) * ((Nc + kBN - 1) / kBN);
-  hipLaunchKernelGGL((gemm_nt_kernel<LA, LB, ST>), dim3(tiles), dim3(kThreads), 0, stream, M, Nc,
-                     K, la, lb, st);
+  // the 256 x 256 tile once there are at least four of them per CU
+  const int big = ((M + BigTile::kBM - 1) / BigTile::kBM) * ((Nc + BigTile::kBN - 1) / BigTile::kBN);
+  if (big >= 4 * 256) {
+    hipLaunchKernelGGL((gemm_nt_kernel<BigTile, 1, LA, LB, ST>), dim3(big),
+                       dim3(BigTile::kThreads), 0, stream, M, Nc, K, la, lb, st);
+  } else {
+    const int tiles = ((M + SmallTile::kBM - 1) / SmallTile::kBM) *
+                      ((Nc + SmallTile::kBN - 1) / SmallTile::kBN);
+    hipLaunchKernelGGL((gemm_nt_kernel<SmallTile, 3, LA, LB, ST>), dim3(tiles),
+                       dim3(SmallTile::kThreads), 0, stream, M, Nc, K, la, lb, st);
+  }
   return hipGetLastError();
 }
 
