@@ -324,6 +324,51 @@ def budget_sweep(name, budgets, x=None, reps=10):
             "rows": int(w.heads * w.n_blocks)}
 
 
+def torch_sdpa(names=("views8", "views32", "views100"), reps=5):
+    """Outside context for the attention kernel: torch's own fused
+    scaled_dot_product_attention (dense, bf16, [1][H][N_pad][64]) on the same
+    GPU, restricted to its flash and memory-efficient kernels (never the
+    unfused math path); median ms and TFLOP/s on N_pad^2 (padding included),
+    next to this library's dense kernel at the same shape. None for a shape
+    torch has no fused kernel for."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    import block_sparse_global_amd as bsg
+    import synth
+    res = {}
+    for name in names:
+        w = synth.get_workload(name)
+        H, Np = w.heads, w.N_pad
+        g = torch.Generator(device="cuda").manual_seed(5)
+        q, k, v = (torch.randn((1, H, Np, 64), generator=g, device="cuda",
+                               dtype=torch.float32).to(torch.bfloat16) for _ in range(3))
+        flop = 4.0 * 64 * H * float(Np) * float(Np)
+        entry = {"N_pad": Np}
+        for label, backend in (("flash", SDPBackend.FLASH_ATTENTION),
+                               ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+            try:
+                with sdpa_kernel([backend]):
+                    f = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)  # noqa: E731
+                    f()
+                    torch.cuda.synchronize()
+                    ms = time_median(f, reps)
+                entry[label] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12}
+            except RuntimeError as e:
+                entry[label] = {"error": str(e).splitlines()[0][:120]}
+        shape = bsg.Shape(H, Np, Np, 64, w.block)
+        q3, k3, v3 = (t.view(H, Np, 64) for t in (q, k, v))
+        o3 = torch.empty_like(q3)
+        fd = lambda: bsg.dense_attention(q3, k3, v3, shape, o3)  # noqa: E731
+        fd()
+        ms = time_median(fd, reps)
+        entry["libress_dense"] = {"ms": ms, "tflops": flop / (ms * 1e-3) / 1e12}
+        res[name] = entry
+        del q, k, v, q3, k3, v3, o3
+        torch.cuda.empty_cache()
+    return res
+
+
 def projections(w, reps=20):
     """The linear maps around the attention call at this workload's token
     count with a 1024-wide model (16 heads x 64): the QKV projection and the
@@ -591,6 +636,7 @@ def main():
         del src, dst
     proj = None if args.no_sweep else projections(w)
     sel_paths = None if args.no_sweep else select_paths()
+    sdpa = None if args.no_sweep else torch_sdpa()
 
     sweep = {}
     budgets = None
@@ -707,6 +753,7 @@ def main():
         "projections": proj,
         "select_paths_ms": sel_paths,
         "budget_sweep": budgets,
+        "torch_sdpa": sdpa,
         "views_sweep": sweep,
         "residual_drift": drift_report,
         "pages_context": PAGES_CONTEXT,
