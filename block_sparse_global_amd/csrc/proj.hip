@@ -53,6 +53,9 @@ struct TileCfg {
   static_assert(kBM % (16 * kWaves) == 0 && kBN % (16 * kWaves) == 0,
                 "whole copy windows of each operand per wave");
 };
+#ifndef PROJ_XCD_ORDER
+#define PROJ_XCD_ORDER 1
+#endif
 using BigTile = TileCfg<2, 4, 4, 2>;    // 256 x 256, 8 waves
 using SmallTile = TileCfg<2, 2, 2, 2>;  // 128 x 128, 4 waves
 constexpr int kBK = 32;
@@ -121,9 +124,22 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = w / kWGN, wn = w % kWGN;
-  // column tiles vary fastest: consecutive workgroups share the A rows
+  // Tile order: workgroups are handed to the eight XCDs in turn, so the ones
+  // landing on XCD x (ids x, x + 8, ...) take a contiguous range of tiles,
+  // column tiles fastest: the column tiles of one row tile then run on one
+  // XCD and share its L2 copy of the A rows.
   const int n_tiles = (Nc + kBN - 1) / kBN;
-  const int m0 = (blockIdx.x / n_tiles) * kBM, n0 = (blockIdx.x % n_tiles) * kBN;
+#if PROJ_XCD_ORDER
+  int t;
+  {
+    const int T = gridDim.x, L = blockIdx.x;
+    const int x = L & 7, q = T >> 3, r = T & 7;
+    t = x * q + min(x, r) + (L >> 3);
+  }
+#else
+  const int t = blockIdx.x;
+#endif
+  const int m0 = (t / n_tiles) * kBM, n0 = (t % n_tiles) * kBN;
   const int crow = lane >> 2, cchunk = (lane & 3) ^ (lane >> 4);
 
   // the copies of k-tile kt into stage S: A windows w, w + kWaves, ... and
