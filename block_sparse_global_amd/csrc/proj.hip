@@ -12,14 +12,14 @@
 // float32 accumulation, in one of two tile shapes:
 //  * 256 x 256 output tiles, eight waves of 128 x 64 (4 x 2 MFMA tiles), one
 //    workgroup per CU, for products with at least four such tiles per CU;
-//  * 128 x 128 output tiles, four waves of 64 x 64, three workgroups per CU,
+//  * 128 x 128 output tiles, four waves of 64 x 64, two workgroups per CU,
 //    for smaller ones (the big tile leaves CUs idle there).
 // The products are formed as C^T (the weight rows as the MFMA's A operand),
 // so each lane ends up with four consecutive output channels of one token
-// and stores them with one 8-byte write. k-tiles of 32 pass through a ring
-// of three LDS stages, copied straight from global memory (global_load_lds):
-// two k-tiles are in flight while one is multiplied. The operand loaders and
-// the epilogue differ per map:
+// and stores them with one 8-byte write. k-tiles of 64 alternate between two
+// LDS stages, copied straight from global memory (global_load_lds): the next
+// k-tile streams in while one is multiplied. The operand loaders and the
+// epilogue differ per map:
 //  * QKV: A = x [N_pad][d_model]; B = W_qkv [3 H D][d_model]; output channel
 //    c = which * H D + h D + d goes to {q,k,v}[which][h][t][d] (the
 //    [H][N_pad][D] layout of the path), plus the bias; rows t >= N are
@@ -39,18 +39,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // WGM x WGN waves per workgroup, each wave owning TM x TN sub-tiles of
-// 32 x 32 outputs (TM along the tokens, TN along the output channels).
+// 32 x 32 outputs (TM along the tokens, TN along the output channels). A
+// copy window is 8 tile rows x 128 bytes (1 KB), one 16-byte copy per lane;
+// kWinA / kWinB: windows of each operand per wave.
 template <int WGM, int WGN, int TM, int TN>
 struct TileCfg {
   static constexpr int kWGM = WGM, kWGN = WGN, kTM = TM, kTN = TN;
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kBM = 32 * WGM * TM, kBN = 32 * WGN * TN;
   static constexpr int kThreads = 64 * kWaves;
-  // a copy window is 16 tile rows x 64 bytes (1 KB), one 16-byte copy per
-  // lane; windows of each operand per wave
-  static constexpr int kWinA = kBM / 16 / kWaves, kWinB = kBN / 16 / kWaves;
+  static constexpr int kWinA = kBM / 8 / kWaves, kWinB = kBN / 8 / kWaves;
   static constexpr int kWinPerWave = kWinA + kWinB;
-  static_assert(kBM % (16 * kWaves) == 0 && kBN % (16 * kWaves) == 0,
+  static_assert(kBM % (8 * kWaves) == 0 && kBN % (8 * kWaves) == 0,
                 "whole copy windows of each operand per wave");
 };
 #ifndef PROJ_XCD_ORDER
@@ -58,9 +58,9 @@ struct TileCfg {
 #endif
 using BigTile = TileCfg<2, 4, 4, 2>;    // 256 x 256, 8 waves
 using SmallTile = TileCfg<2, 2, 2, 2>;  // 128 x 128, 4 waves
-constexpr int kBK = 32;
+constexpr int kBK = 64;
 
-__device__ inline int swz(int row) { return (row >> 2) & 3; }
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -72,9 +72,9 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
 // 16 bytes at `window` + 16 * l (window is wave-uniform). Issued as inline
 // assembly, which produces no register and which the compiler does not count
 // as an outstanding load: the kernel waits for these copies itself
-// (wait_vmem), so that one stage can be read while the copies into the next
-// two are in flight (the compiler, tracking the copies itself, waits for all
-// of them before any LDS read). The compiler's own vmcnt waits stay correct,
+// (wait_vmem), so that one stage can be read while the copies into the other
+// are in flight (the compiler, tracking the copies itself, waits for all of
+// them before any LDS read). The compiler's own vmcnt waits stay correct,
 // only stricter: the copies complete in issue order with its loads.
 __device__ inline void gload_lds16(const uint16_t* g, uint16_t* window) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
@@ -105,12 +105,12 @@ __device__ inline void lds_barrier() {
 // (m, n .. n+3) (m < M; n a multiple of 4, n + 3 < Nc, which holds as Nc is a
 // multiple of 64).
 //
-// Operand tiles are row-major in LDS (64-byte rows of four 16-byte chunks,
-// the chunk index XORed by (row >> 2) & 3 so that the operand reads, 16 rows
-// at one logical chunk per 16-lane pass, are bank-conflict free). In a copy
-// window of 16 rows lane l fills row l / 4 at physical chunk l % 4, i.e.
-// logical chunk (l % 4) ^ (l / 16). The three stages are separate LDS arrays
-// named at compile time.
+// Operand tiles are row-major in LDS (128-byte rows of eight 16-byte chunks,
+// the chunk index XORed by (row >> 1) & 7 so that the operand reads, 16 rows
+// at one logical chunk per 16-lane pass, are bank-conflict free). In copy
+// window v (rows 8v .. 8v + 7) lane l fills row 8v + l / 8 at physical chunk
+// l % 8, i.e. logical chunk (l % 8) ^ ((l / 16 + 4v) % 8). The two stages are
+// separate LDS arrays named at compile time.
 template <class Cfg, int MINB, class LoadA, class LoadB, class Store>
 __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int Nc, int K,
                                                                      LoadA la, LoadB lb,
@@ -118,8 +118,8 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
   constexpr int kTM = Cfg::kTM, kTN = Cfg::kTN, kWGN = Cfg::kWGN, kWaves = Cfg::kWaves;
   constexpr int kBM = Cfg::kBM, kBN = Cfg::kBN;
   constexpr int kWinA = Cfg::kWinA, kWinB = Cfg::kWinB;
-  __shared__ __attribute__((aligned(16))) uint16_t As0[kBM * kBK], As1[kBM * kBK], As2[kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBN * kBK], Bs1[kBN * kBK], Bs2[kBN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t As0[kBM * kBK], As1[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[kBN * kBK], Bs1[kBN * kBK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
@@ -140,24 +140,25 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
   const int t = blockIdx.x;
 #endif
   const int m0 = (t / n_tiles) * kBM, n0 = (t % n_tiles) * kBN;
-  const int crow = lane >> 2, cchunk = (lane & 3) ^ (lane >> 4);
+  const int crow = lane >> 3;
 
   // the copies of k-tile kt into stage S: A windows w, w + kWaves, ... and
   // B windows likewise
   auto issue = [&](auto stagec, int kt) {
     constexpr int S = decltype(stagec)::value;
-    uint16_t* const as = S == 0 ? As0 : (S == 1 ? As1 : As2);
-    uint16_t* const bs = S == 0 ? Bs0 : (S == 1 ? Bs1 : Bs2);
-    const int k = kt * kBK + 8 * cchunk;
+    uint16_t* const as = S == 0 ? As0 : As1;
+    uint16_t* const bs = S == 0 ? Bs0 : Bs1;
 #pragma unroll
     for (int u = 0; u < kWinA; ++u) {
       const int v = w + kWaves * u;  // wave-uniform
-      gload_lds16(la.ptr(min(m0 + 16 * v + crow, M - 1), k), as + 16 * v * kBK);
+      const int c = (lane & 7) ^ (((lane >> 4) + 4 * v) & 7);
+      gload_lds16(la.ptr(min(m0 + 8 * v + crow, M - 1), kt * kBK + 8 * c), as + 8 * v * kBK);
     }
 #pragma unroll
     for (int u = 0; u < kWinB; ++u) {
       const int v = w + kWaves * u;
-      gload_lds16(lb.ptr(min(n0 + 16 * v + crow, Nc - 1), k), bs + 16 * v * kBK);
+      const int c = (lane & 7) ^ (((lane >> 4) + 4 * v) & 7);
+      gload_lds16(lb.ptr(min(n0 + 8 * v + crow, Nc - 1), kt * kBK + 8 * c), bs + 8 * v * kBK);
     }
   };
 
@@ -173,8 +174,8 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
   // while step ks's MFMAs issue
   auto compute = [&](auto stagec) {
     constexpr int S = decltype(stagec)::value;
-    const uint16_t* const as = S == 0 ? As0 : (S == 1 ? As1 : As2);
-    const uint16_t* const bs = S == 0 ? Bs0 : (S == 1 ? Bs1 : Bs2);
+    const uint16_t* const as = S == 0 ? As0 : As1;
+    const uint16_t* const bs = S == 0 ? Bs0 : Bs1;
     bf16x8 af[2][kTM], bfr[2][kTN];
     auto read = [&](int ks, bf16x8 (&a)[kTM], bf16x8 (&b)[kTN]) {
 #pragma unroll
@@ -204,27 +205,23 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
     }
   };
 
-  // one k-tile from stage S: wait for its copies (the next tile's may stay in
-  // flight), a barrier (every wave's copies have landed, and every wave is
-  // done with the stage the copies of tile kt + 2 go to), those copies, the
-  // products
+  // one k-tile from stage S: wait for its copies, a barrier (every wave's
+  // copies have landed, and every wave is done with the other stage), the
+  // copies of tile kt + 1 into the other stage, the products
   const int nk = K / kBK;
   auto step = [&](auto stagec, int kt) {
     constexpr int S = decltype(stagec)::value;
-    if (kt + 1 < nk) wait_vmem<Cfg::kWinPerWave>(); else wait_vmem<0>();
+    wait_vmem<0>();
     lds_barrier();
-    if (kt + 2 < nk) issue(std::integral_constant<int, (S + 2) % 3>{}, kt + 2);
+    if (kt + 1 < nk) issue(std::integral_constant<int, S ^ 1>{}, kt + 1);
     compute(stagec);
   };
 
   issue(std::integral_constant<int, 0>{}, 0);
-  if (nk > 1) issue(std::integral_constant<int, 1>{}, 1);
   for (int kt = 0;;) {
     step(std::integral_constant<int, 0>{}, kt);
     if (++kt >= nk) break;
     step(std::integral_constant<int, 1>{}, kt);
-    if (++kt >= nk) break;
-    step(std::integral_constant<int, 2>{}, kt);
     if (++kt >= nk) break;
   }
 
@@ -326,7 +323,7 @@ hipError_t launch_gemm(int M, int Nc, int K, LA la, LB lb, ST st, hipStream_t st
   } else {
     const int tiles = ((M + SmallTile::kBM - 1) / SmallTile::kBM) *
                       ((Nc + SmallTile::kBN - 1) / SmallTile::kBN);
-    hipLaunchKernelGGL((gemm_nt_kernel<SmallTile, 3, LA, LB, ST>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_nt_kernel<SmallTile, 2, LA, LB, ST>), dim3(tiles),
                        dim3(SmallTile::kThreads), 0, stream, M, Nc, K, la, lb, st);
   }
   return hipGetLastError();

@@ -1,4 +1,5 @@
-"""Guard bytes around every output buffer of every entry point.
+"""Guard bytes around every output buffer of every entry point (including the
+no-allocation refinement, the fused selection and both projections).
 
 Each output (and the refinement workspace) is a view into a larger device
 allocation whose 256 bytes before and after it are filled with a sentinel;
@@ -132,3 +133,35 @@ def test_guard_bytes_around_every_output(name, w):
     drift = Guarded((H, nq), f64)
     b.ress_residual_drift(out.t, dout.t, shape, drift.t, M)
     drift.check("ress_residual_drift drift")
+
+    ri, rc = Guarded((H, nq, k_max), torch.int32, idx0), Guarded((H, nq), torch.int32, cnt0)
+    J0, J1 = Guarded((H, nq), f64), Guarded((H, nq), f64)
+    b.ress_refine_dropset_noalloc(P.t, key.t, vp.t, vout.t, M, shape, keep, alw, 2, 0.5, 1e-4,
+                                  k_max, ri.t, rc.t, J0.t, J1.t)
+    for g, s in ((ri, "kept_idx"), (rc, "kept_cnt"), (J0, "J_init"), (J1, "J_final")):
+        g.check(f"ress_refine_dropset_noalloc {s}")
+
+    if nk <= b.SELECT_FUSED_MAX_BLOCKS:
+        fi, fc = Guarded((H, nq, k_max), torch.int32), Guarded((H, nq), torch.int32)
+        fv = Guarded((H, nk), f64)
+        b.ress_select_fused(qp.t, kp.t, vp.t, M, shape, b.RESS_SCORE_DRIFT, 0.125, 1e-4, keep,
+                            alw, k_max, fv.t, fi.t, fc.t)
+        for g, s in ((fi, "kept_idx"), (fc, "kept_cnt"), (fv, "vmv")):
+            g.check(f"ress_select_fused {s}")
+
+    if w.dtype == "bf16":
+        dm = 128
+        L = synth.make_sublayer(Np, H, D, dm, seed=7)
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(  # noqa: E731
+            torch.bfloat16).cuda()
+        xs, wq, bq, wo2, bo = (bf(L[n]) for n in ("x", "w_qkv", "b_qkv", "w_o", "b_o"))
+        pq, pk, pv = (Guarded((H, Np, D), torch.bfloat16) for _ in range(3))
+        b.ress_qkv_project(xs, wq, bq, shape, pq.t, pk.t, pv.t)
+        for g, s in ((pq, "q"), (pk, "k"), (pv, "v")):
+            g.check(f"ress_qkv_project {s}")
+        y = Guarded((Np, dm), torch.bfloat16)
+        b.ress_out_project(pq.t, wo2, bo, xs, shape, y.t)
+        y.check("ress_out_project y")
+        yr = Guarded((Np, dm), torch.bfloat16, xs)
+        b.ress_out_project(pq.t, wo2, bo, yr.t, shape, yr.t)
+        yr.check("ress_out_project y (in place)")
