@@ -44,9 +44,14 @@ SHAPES = [  # H, N, N_pad, B, d_model
     (1, 300, 320, 64, 64),        # partial 128-row tiles, 192 output channels
     (16, 10992, 11008, 128, 1024),  # the 8-view VGGT-L global layer
 ]
+# Products with at least four 256 x 256 tiles per CU take the big-tile kernel:
+# 86 x 12 tiles for this QKV projection (the last row tile partial), 256 x 4
+# for this output projection.
+BIG_QKV = (16, 22000, 22016, 128, 1024)
+BIG_OUT = (16, 65500, 65536, 128, 1024)
 
 
-@pytest.mark.parametrize("H,N,N_pad,B,dm", SHAPES)
+@pytest.mark.parametrize("H,N,N_pad,B,dm", SHAPES + [BIG_QKV])
 def test_qkv_project(H, N, N_pad, B, dm):
     import block_sparse_global_amd as b
     L = synth.make_sublayer(N_pad, H, 64, dm, seed=H + dm)
@@ -65,8 +70,9 @@ def test_qkv_project(H, N, N_pad, B, dm):
         assert np.all(g[:, N:] == 0), f"{name}: padded rows must be zero"
 
 
-@pytest.mark.parametrize("H,N,N_pad,B,dm", SHAPES)
-@pytest.mark.parametrize("mode", ["residual", "in_place", "plain"])
+@pytest.mark.parametrize("H,N,N_pad,B,dm,mode",
+                         [s + (m,) for s in SHAPES for m in ("residual", "in_place", "plain")]
+                         + [BIG_OUT + ("residual",), BIG_OUT + ("in_place",)])
 def test_out_project(H, N, N_pad, B, dm, mode):
     import block_sparse_global_amd as b
     L = synth.make_sublayer(N_pad, H, 64, dm, seed=7 * H + dm)
