@@ -27,7 +27,10 @@
 // weights that matter never underflow. A workgroup with any valid row
 // outside that range (logits beyond roughly +-44 in natural units) discards
 // its result and runs its rows again as a classical online softmax (running
-// max, lazy rescaling): the second pass below.
+// max, lazy rescaling): the second pass below. The first pass takes its row
+// sums on the matrix cores, as the product of the bf16 weights with a 0/1
+// selector (v_mfma_f32_16x16x32_bf16, eight per 32 x 128 wave tile), which
+// takes 32 vector instructions per tile off the vector ALU.
 //
 // MFMA 32x32x16 operand convention used here: lane l supplies 8 consecutive
 // k-slots of row/column (l % 32); lanes l and l+32 cover the two halves of
@@ -44,6 +47,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 64;
@@ -150,13 +154,17 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
 
   const float sl2 = scale * 1.4426950408889634f;  // scale * log2(e)
   // Q^T operand: dims 16*ks + 8*half + 0..7 of this lane's query row.
+  // Padded query rows (qrow >= N) load row N - 1 instead (their outputs are
+  // written as zeros): whatever the padding holds, their scores and weights
+  // stay finite, so the first pass's row-sum product (whose zero selector
+  // entries meet every query's weights) cannot turn NaN for the valid rows.
+  const bool qvalid = qrow < N;
   bf16x8 qb[4];
   {
-    const Tin* qp = Q + head_off + (size_t)qrow * kD + 8 * half;
+    const Tin* qp = Q + head_off + (size_t)min(qrow, N - 1) * kD + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[ks] = as_bf16x8(load_row8(qp + 16 * ks));
   }
-  const bool qvalid = qrow < N;
 
   f32x16 o[2];
 #pragma unroll
@@ -166,6 +174,19 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   float m_use = 0.f;  // running max in use (second pass), scaled log2 units
   float l_run = 0.f;
   const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+  // row sums of the first pass on the matrix cores: D = Sel P^T with Sel a
+  // 16 x 32 0/1 matrix whose row 0 adds the keys of queries 0-15 and row 1
+  // those of queries 16-31 (v_mfma_f32_16x16x32_bf16 reads the PV weights'
+  // register as 32 keys x 16 columns: column n, key group g = lane / 16
+  // holds query n + 16 (g & 1))
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 sel;
+  {
+    const int m = lane & 15, g = lane >> 4;
+    const __bf16 one = (m == 0 && !(g & 1)) || (m == 1 && (g & 1)) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
 
   // The keep list is read through the constant address space so that its
   // (workgroup-uniform) entries come in by scalar loads: vector loads would
@@ -340,9 +361,10 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
         va[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
-    // Two phases: first every bf16 weight of the block (exponentials and
-    // their row sum, VALU only) at wave priority 0, then all PV MFMAs back to
-    // back at priority 3; the S product before them runs at priority 2. A
+    // Two phases: first every bf16 weight of the block (exponentials, VALU
+    // only; the online pass also sums them here) at wave priority 0, then all
+    // PV MFMAs back to back at priority 3, with the first pass's row-sum
+    // MFMAs among them; the S product before them runs at priority 2. A
     // wave and its matrix core then alternate in long runs instead of one
     // exponential batch per MFMA pair, and a wave whose P is complete (or
     // whose K tile has landed) gets the matrix core ahead of waves still
@@ -352,9 +374,10 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     bf16x8 vops[2][2];
     bf16x8 pall[2 * kKT];
     // p = exp2(S * scale * log2 e) (first pass) or exp2(S * scale * log2 e
-    // - m) (online pass) as bf16, and the
-    // row sum of the very bf16 weights the PV product uses, two per
-    // instruction (bf16 dot product with (1, 1), float32 accumulation)
+    // - m) (online pass) as bf16; the online pass sums the very bf16 weights
+    // the PV product uses here, two per instruction (bf16 dot product with
+    // (1, 1), float32 accumulation), the first pass on the matrix cores
+    // below
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int step = 0; step < 2 * kKT; ++step) {
@@ -364,10 +387,12 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
         const float x = ONLINE ? fmaf(s[kt][8 * hf + r], sl2, -m_use) : s[kt][8 * hf + r] * sl2;
         pall[step][r] = (__bf16)__builtin_amdgcn_exp2f(x);
       }
+      if constexpr (ONLINE) {
 #pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        const bf16x2 pp = {pall[step][r], pall[step][r + 1]};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
+        for (int r = 0; r < 8; r += 2) {
+          const bf16x2 pp = {pall[step][r], pall[step][r + 1]};
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, psum, false);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -379,6 +404,7 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[step & 1][dt], pall[step], o[dt], 0, 0, 0);
+      if constexpr (!ONLINE) lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pall[step], lsum, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
     l_run += psum;
@@ -407,8 +433,14 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     }
   };
   run_row(std::false_type{});
+  float l_fast;
   {
-    const float lt = l_run + __shfl_xor(l_run, 32, 64);
+    // query q = lane % 32: D[0][q] (q < 16) or D[1][q - 16], held by lane
+    // q % 16 as its accumulator elements 0 and 1
+    const int q = lane & 31;
+    const float a = __shfl(lsum[0], q & 15, 64), b = __shfl(lsum[1], q & 15, 64);
+    l_fast = q < 16 ? a : b;
+    const float lt = l_fast;
     const bool bad = qvalid && kb0 < cnt && !(lt >= kSumMin && lt <= kSumMax);
     if (__any(bad) && lane == 0) rerun = 1;
   }
@@ -424,7 +456,7 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   }
 
   // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = rerun ? l_run + __shfl_xor(l_run, 32, 64) : l_fast;
   const bool valid = qvalid;
   const float inv = (valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   Tout* op = out + head_off + (size_t)qrow * kD;
