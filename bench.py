@@ -46,9 +46,9 @@ CDF_TAU = 0.05
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "0996fb866fa51de9d5ab466ccd2055a1e07d3f79f19c75349a9628ac703f0b51",
-    "read_bytes": 8833912192,
-    "write_bytes": 334332960,
+    "source_sha256": "1baf8b524016ef0a2fc6bbb645b8a985647e6ed8e691d234dfc5b29b62d094f7",
+    "read_bytes": 9830330624,
+    "write_bytes": 457515328,
 }
 
 
