@@ -6,8 +6,10 @@
 // i.e. the mean squared change ||W_O^h e_t||^2 that sparsification leaves in
 // the residual stream when M_h = (W_O^h)^T W_O^h (||e_t||^2 when M is NULL).
 // One workgroup per (query block, head): M_h in LDS, one wave per token at a
-// time (lane d holds e_d and forms (M e)_d from the symmetric M's column d),
-// fixed-order sums, so repeated calls give identical bits.
+// time (lane d holds e_d and forms (M e)_d from the symmetric M's column d);
+// each lane sums its dim's terms over the wave's tokens and the wave reduces
+// once. Without M, each thread takes four consecutive dims of every 16th
+// token instead. Fixed-order sums, so repeated calls give identical bits.
 #include "ress_internal.h"
 
 namespace ress {
@@ -34,8 +36,21 @@ __global__ __launch_bounds__(256) void drift_kernel(const T* __restrict__ os,
     for (int e = tid; e < kD * kD; e += 256) Ms[e / kD][e % kD] = M[(size_t)h * kD * kD + e];
   __syncthreads();
   const int t0 = i * B, t1 = min(t0 + B, N);
-  double acc = 0.0;  // lane 0 of each wave: its tokens, in order
-  for (int t = t0 + w; t < t1; t += 4) {
+  double accl = 0.0;  // this lane's terms over its tokens, in order
+  if (M == nullptr) {
+    // ||e_t||^2 only: thread tid takes dims 4 (tid % 16) .. + 3 of tokens
+    // t0 + tid / 16, + 16, ... (one load instruction covers four tokens)
+    const int tl = tid >> 4, d4 = 4 * (tid & 15);
+    for (int t = t0 + tl; t < t1; t += 16) {
+      const size_t off = ((size_t)h * N_pad + t) * kD + d4;
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const double e = elem(os, off + e4) - elem(od, off + e4);
+        accl = fma(e, e, accl);
+      }
+    }
+  }
+  for (int t = t0 + w; M != nullptr && t < t1; t += 4) {
     const size_t off = ((size_t)h * N_pad + t) * kD + d;
     const double e = elem(os, off) - elem(od, off);
     double me = e;
@@ -47,9 +62,9 @@ __global__ __launch_bounds__(256) void drift_kernel(const T* __restrict__ os,
       for (int f = 0; f < kD; ++f) me = fma(Ms[f][d], ev[w][f], me);
       wave_lds_sync();
     }
-    const double q = wave_sum64(e * me);
-    acc += q;
+    accl = fma(e, me, accl);
   }
+  const double acc = wave_sum64(accl);  // one reduction per wave
   if (d == 0) part[w] = acc;
   __syncthreads();
   if (tid == 0) {
