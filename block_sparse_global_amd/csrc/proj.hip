@@ -25,7 +25,7 @@
 //    [H][N_pad][D] layout of the path), plus the bias; rows t >= N are
 //    written as zeros.
 //  * Output: A = the attention output o [H][N_pad][D] read as [N_pad][H D]
-//    (the columns of k-tile pair 2h, 2h+1 are head h's D); B = W_O
+//    (k-tile h, 64 wide, is head h's D); B = W_O
 //    [d_model][H D]; y[t][c] = residual[t][c] + bias[c] + sum_k A[t][k]
 //    W_O[c][k], rounded once to bf16.
 #include <type_traits>
@@ -53,9 +53,6 @@ struct TileCfg {
   static_assert(kBM % (8 * kWaves) == 0 && kBN % (8 * kWaves) == 0,
                 "whole copy windows of each operand per wave");
 };
-#ifndef PROJ_XCD_ORDER
-#define PROJ_XCD_ORDER 1
-#endif
 using BigTile = TileCfg<2, 4, 4, 2>;    // 256 x 256, 8 waves
 using SmallTile = TileCfg<2, 2, 2, 2>;  // 128 x 128, 4 waves
 constexpr int kBK = 64;
@@ -129,17 +126,13 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
   // column tiles fastest: the column tiles of one row tile then run on one
   // XCD and share its L2 copy of the A rows.
   const int n_tiles = (Nc + kBN - 1) / kBN;
-#if PROJ_XCD_ORDER
-  int t;
+  int tile;
   {
     const int T = gridDim.x, L = blockIdx.x;
     const int x = L & 7, q = T >> 3, r = T & 7;
-    t = x * q + min(x, r) + (L >> 3);
+    tile = x * q + min(x, r) + (L >> 3);
   }
-#else
-  const int t = blockIdx.x;
-#endif
-  const int m0 = (t / n_tiles) * kBM, n0 = (t % n_tiles) * kBN;
+  const int m0 = (tile / n_tiles) * kBM, n0 = (tile % n_tiles) * kBN;
   const int crow = lane >> 3;
 
   // the copies of k-tile kt into stage S: A windows w, w + kWaves, ... and
@@ -179,15 +172,15 @@ __global__ __launch_bounds__(Cfg::kThreads, MINB) void gemm_nt_kernel(int M, int
     bf16x8 af[2][kTM], bfr[2][kTN];
     auto read = [&](int ks, bf16x8 (&a)[kTM], bf16x8 (&b)[kTN]) {
 #pragma unroll
-      for (int t = 0; t < kTM; ++t) {
-        const int r = 32 * (kTM * wm + t) + l32;
-        a[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+      for (int u = 0; u < kTM; ++u) {
+        const int r = 32 * (kTM * wm + u) + l32;
+        a[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
                                               &as[r * kBK + (((2 * ks + half) ^ swz(r)) << 3)]));
       }
 #pragma unroll
-      for (int t = 0; t < kTN; ++t) {
-        const int r = 32 * (kTN * wn + t) + l32;
-        b[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+      for (int u = 0; u < kTN; ++u) {
+        const int r = 32 * (kTN * wn + u) + l32;
+        b[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
                                               &bs[r * kBK + (((2 * ks + half) ^ swz(r)) << 3)]));
       }
     };
