@@ -261,7 +261,10 @@ def scoring_memory(layer):
         t = getattr(layer, name, None)
         if t is not None:
             parts[name] = int(t.numel() * t.element_size())
-    return {"bytes": sum(parts.values()), "by_buffer": parts}
+    total = sum(parts.values())
+    # the fused refinement keeps its per-row state on chip: no workspace
+    return {"bytes": total, "by_buffer": parts,
+            "bytes_with_fused_refinement": total - parts.get("workspace", 0)}
 
 
 def select_paths(names=("views8", "views32"), reps=20):
