@@ -440,6 +440,40 @@ def refine_paths_ms(w, x, shape, layer, reps):
     return res
 
 
+def one_pass_selection_ms(w, x, shape, layer, qkv, reps):
+    """Scoring, top-k and refinement by the split calls (the layer's: map,
+    key and the refinement workspace in HBM) against the one-pass call
+    (ress_select_refine_fused, map and key on chip), median ms from the same
+    pooled blocks, with how many rows' keep lists differ; None without
+    refinement or for rows longer than the one-pass kernel takes."""
+    import torch
+
+    import block_sparse_global_amd as bsg
+    if layer.rounds <= 0 or shape.nk > bsg.SELECT_REFINE_FUSED_MAX_BLOCKS:
+        return None
+    one = bsg.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode=layer.mode,
+                                         rounds=layer.rounds, rho=layer.rho, M=layer.M,
+                                         select_impl="fused")
+    assert one.select_impl == "fused"
+    res = {}
+    for name, L in (("split", layer), ("one_pass", one)):
+        L.pool(*qkv)
+
+        def run(L=L):
+            L.score()
+            L.select()
+            L.refine()
+        run()
+        res[name] = time_median(run, reps)
+    torch.cuda.synchronize()
+    differ = torch.any(layer.kept_idx != one.kept_idx, dim=-1) | (layer.kept_cnt != one.kept_cnt)
+    res["rows_differ"] = int(differ.sum().item())
+    res["rows"] = int(differ.numel())
+    del one
+    torch.cuda.empty_cache()
+    return res
+
+
 def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -612,6 +646,7 @@ def main():
                      "rows": int(J0.size)}
     stages = stage_breakdown(layer, qkv, out, max(20, args.steps))
     refine_paths = refine_paths_ms(w, x, shape, layer, max(3, args.steps // 2))
+    one_pass = one_pass_selection_ms(w, x, shape, layer, qkv, max(5, args.steps // 2))
     attn_reps = max(20, args.steps)
     attn_ms = time_events(lambda: layer.attend(q, k, v, out), attn_reps)
     attn_median = time_median(lambda: layer.attend(q, k, v, out), attn_reps)
@@ -753,6 +788,7 @@ def main():
         "refine_objective": objective,
         "scoring_memory": mem,
         "refine_paths_ms": refine_paths,
+        "one_pass_selection_ms": one_pass,
         "projections": proj,
         "select_paths_ms": sel_paths,
         "budget_sweep": budgets,

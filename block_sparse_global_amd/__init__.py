@@ -40,6 +40,8 @@ from ._lib import (  # noqa: F401
     ress_select_cdf,
     ress_select_fused,
     SELECT_FUSED_MAX_BLOCKS,
+    ress_select_refine_fused,
+    SELECT_REFINE_FUSED_MAX_BLOCKS,
     ress_sparse_attn_fwd,
     ress_version,
 )

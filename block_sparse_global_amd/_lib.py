@@ -38,6 +38,7 @@ ENTRY_POINTS = (
     "ress_select_topk",
     "ress_select_cdf",
     "ress_select_fused",
+    "ress_select_refine_fused",
     "ress_refine_dropset",
     "ress_refine_dropset_fused",
     "ress_refine_dropset_noalloc",
@@ -112,6 +113,9 @@ def _load():
     lib.ress_select_cdf.argtypes = [dp, ress_shape, ip, vp, ctypes.c_double, i32, ip, ip, vp]
     lib.ress_select_fused.argtypes = [dp, dp, dp, dp, ress_shape, ctypes.c_int, ctypes.c_double,
                                       ctypes.c_double, ip, vp, i32, dp, ip, ip, vp]
+    lib.ress_select_refine_fused.argtypes = [dp, dp, dp, dp, ress_shape, ctypes.c_double,
+                                             ctypes.c_double, ip, vp, i32, ctypes.c_double, i32,
+                                             dp, ip, ip, dp, dp, vp]
     lib.ress_refine_dropset.argtypes = [dp, dp, dp, dp, dp, ress_shape, ip, vp, i32,
                                         ctypes.c_double, ctypes.c_double, i32, ip, ip,
                                         dp, dp, vp, ctypes.c_size_t, vp]
@@ -131,7 +135,8 @@ def _load():
     lib.ress_qkv_project.argtypes = [vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp, vp, vp]
     lib.ress_out_project.argtypes = [vp, vp, vp, vp, ctypes.c_int, i32, ress_shape, vp, vp]
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk",
-              "ress_select_cdf", "ress_select_fused", "ress_refine_dropset", "ress_refine_dropset_fused",
+              "ress_select_cdf", "ress_select_fused", "ress_select_refine_fused",
+              "ress_refine_dropset", "ress_refine_dropset_fused",
               "ress_refine_dropset_noalloc", "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
               "ress_qkv_project", "ress_out_project"):
@@ -290,6 +295,35 @@ def ress_select_fused(qpool, kpool, vpool, M, shape: Shape, mode: int, scale: fl
         _ptr(vmv, "vmv", f64, (H, nk)),
         _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
         _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)), _stream(stream)))
+
+
+# key blocks per row up to which ress_select_refine_fused applies
+SELECT_REFINE_FUSED_MAX_BLOCKS = 1088
+
+
+def ress_select_refine_fused(qpool, kpool, vpool, M, shape: Shape, scale: float, eps: float,
+                             keep, always_keep, rounds: int, rho: float, k_max: int, vmv,
+                             kept_idx, kept_cnt, J_init=None, J_final=None, stream=None):
+    """Drift scoring, top-k and the refinement in one pass per tile of rows,
+    the map and key on chip (rows of at most SELECT_REFINE_FUSED_MAX_BLOCKS
+    key blocks); vmv [H][n_k] is written with V_j^T M V_j."""
+    H, nq, nk, D = shape.H, shape.nq, shape.nk, shape.D
+    f64 = torch.float64
+    keep_arr, keep_p = _host_i32(keep, "keep")
+    if keep_arr is not None and keep_arr.shape != (H,):
+        raise ValueError(f"keep must have shape ({H},)")
+    alw_arr, alw_p = _host_u8(always_keep, "always_keep")
+    if alw_arr is not None and alw_arr.shape != (nk,):
+        raise ValueError(f"always_keep must have shape ({nk},)")
+    _check("ress_select_refine_fused", LIB.ress_select_refine_fused(
+        _ptr(qpool, "qpool", f64, (H, nq, D)), _ptr(kpool, "kpool", f64, (H, nk, D)),
+        _ptr(vpool, "vpool", f64, (H, nk, D)), _ptr(M, "M", f64, (H, D, D)), shape.c(),
+        float(scale), float(eps), keep_p, alw_p, int(rounds), float(rho), int(k_max),
+        _ptr(vmv, "vmv", f64, (H, nk)),
+        _ptr(kept_idx, "kept_idx", torch.int32, (H, nq, k_max)),
+        _ptr(kept_cnt, "kept_cnt", torch.int32, (H, nq)),
+        _ptr(J_init, "J_init", f64, (H, nq)), _ptr(J_final, "J_final", f64, (H, nq)),
+        _stream(stream)))
 
 
 def ress_refine_workspace_size(shape: Shape) -> int:

@@ -358,6 +358,44 @@ int ress_refine_dropset_fused(const double* P, const double* key, const double* 
   return hip_status(e, "fused refine launch");
 }
 
+int ress_select_refine_fused(const double* qpool, const double* kpool, const double* vpool,
+                             const double* M, ress_shape shape, double scale, double eps,
+                             const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                             double rho, int32_t k_max, double* vmv, int32_t* kept_idx,
+                             int32_t* kept_cnt, double* J_init, double* J_final, void* stream) {
+  int rc;
+  if ((rc = check_shape(shape)) != RESS_OK) return rc;
+  if (ress::n_kblocks(shape) > ress::refine_fused_max_blocks())
+    return fail(RESS_ERR_UNSUPPORTED,
+                "n_k=%d key blocks exceed the %d of the fused selection with refinement",
+                ress::n_kblocks(shape), ress::refine_fused_max_blocks());
+  REQUIRE_PTR(qpool);
+  REQUIRE_PTR(kpool);
+  REQUIRE_PTR(vpool);
+  REQUIRE_PTR(vmv);
+  OPTIONAL_PTR(M);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  OPTIONAL_PTR(J_init);
+  OPTIONAL_PTR(J_final);
+  if (!(scale > 0.0) || !isfinite(scale))
+    return fail(RESS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!(eps > 0.0) || !isfinite(eps))
+    return fail(RESS_ERR_INVALID_ARG, "eps must be finite and > 0");
+  if (rounds < 0) return fail(RESS_ERR_INVALID_ARG, "rounds=%d < 0", rounds);
+  if (!(rho > 0.0 && rho <= 1.0))
+    return fail(RESS_ERR_INVALID_ARG, "rho must lie in (0, 1]");
+  ress::SelConfig cfg;
+  if ((rc = make_sel_config(shape, keep, always_keep, k_max, &cfg)) != RESS_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = ress::launch_vmv(vpool, M, shape, vmv, st);
+  if (e == hipSuccess)
+    e = ress::launch_select_refine_fused(qpool, kpool, vpool, M, vmv, shape, cfg, scale, rounds,
+                                         rho, eps, k_max, kept_idx, kept_cnt, J_init, J_final,
+                                         st);
+  return hip_status(e, "fused selection with refinement launch");
+}
+
 int ress_refine_dropset_noalloc(const double* P, const double* key, const double* vpool,
                                 const double* vout, const double* M, ress_shape shape,
                                 const int32_t* keep, const uint8_t* always_keep, int32_t rounds,

@@ -251,18 +251,8 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
         const int j = j0 + mp.col_of(tc);
         const double p = pv[r][tc];
         const double sv = kv[r][tc] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
-        const double s2 = sv * sv;
-        const double dMg = p * (svu[r] - acc[tr][tc][r]);  // d_j^T M g_i
-        double dJ;
-        if (fv[r][tc]) {  // restore (Eq. 13-14), u = +P_j
-          const double dG = -2.0 * dMg + s2;
-          const double Ku = sK[r] + p;
-          dJ = sJ[r] - (sG[r] + dG) / (Ku * Ku);
-        } else {  // drop (Eq. 15), u = -P_j
-          const double dG = 2.0 * dMg + s2;
-          const double Ku = sK[r] - p;
-          dJ = (Ku > 0.0) ? sJ[r] - (sG[r] + dG) / (Ku * Ku) : -INFINITY;
-        }
+        const double dJ = swap_gain(RowScalars{sK[r], sG[r], sJ[r], svu[r]}, p, sv,
+                                    acc[tr][tc][r], fv[r][tc] != 0);
         if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
       }
     }

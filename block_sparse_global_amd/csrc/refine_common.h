@@ -66,6 +66,59 @@ __device__ inline double g_from_sets(InD in_drop, int n, int nD, const double* _
   return acc;
 }
 
+// A row's state as the gains epilogue reads it: K (kept mass, Eq. 12), G,
+// J = G / K^2 and vu = vout^T M g.
+struct RowScalars {
+  double K, G, J, vu;
+};
+
+// The exact objective decrease of restoring (inD) or dropping block j of a
+// row (Eq. 13-16), from p = P_ij, s = s_ij, the product u_i . V_j and the
+// row's state.
+__device__ inline double swap_gain(const RowScalars& st, double p, double sv, double uv, bool inD) {
+  const double s2 = sv * sv;
+  const double dMg = p * (st.vu - uv);  // d_j^T M g_i
+  if (inD) {  // restore (Eq. 13-14), u = +P_j
+    const double dG = -2.0 * dMg + s2;
+    const double Ku = st.K + p;
+    return st.J - (st.G + dG) / (Ku * Ku);
+  }
+  // drop (Eq. 15), u = -P_j
+  const double dG = 2.0 * dMg + s2;
+  const double Ku = st.K - p;
+  return (Ku > 0.0) ? st.J - (st.G + dG) / (Ku * Ku) : -INFINITY;
+}
+
+// The row's changes chg[0 .. nchg) (+ (j + 1) for a drop, -(j + 1) for a
+// restore), in ascending block order, applied to g (lane d: dim d) and to
+// the change dk of K, in batches of 8 whose loads are all issued before
+// their sums.
+__device__ __attribute__((always_inline)) void apply_changes(const int32_t* chg, int nchg, const double* Prow,
+                                     const double* Vh, double vod, double& g, double& mag,
+                                     double& dk) {
+  const int d = threadIdx.x & 63;
+  for (int q0 = 0; q0 < nchg; q0 += 8) {
+    int ev[8];
+    double pv[8], vv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int q = min(q0 + t, nchg - 1);
+      ev[t] = chg[q];
+      const int j = (ev[t] > 0 ? ev[t] : -ev[t]) - 1;
+      pv[t] = Prow[j];
+      vv[t] = Vh[(size_t)j * kD + d];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (q0 + t >= nchg) break;
+      const double dj = pv[t] * (vod - vv[t]);
+      g = (ev[t] > 0) ? g + dj : g - dj;
+      mag += fabs(dj);
+      dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
+    }
+  }
+}
+
 // Bitwise AND / OR of a 64-bit value over the wave.
 __device__ inline uint64_t wave_and64(uint64_t v) {
 #pragma unroll

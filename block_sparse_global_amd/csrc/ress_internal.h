@@ -116,6 +116,15 @@ hipError_t launch_refine_fused(const double* P, const double* key, const double*
                                int32_t k_max, int32_t* kept_idx, int32_t* kept_cnt,
                                double* J_init, double* J_final, hipStream_t st);
 int refine_fused_max_blocks();
+// Drift scoring, top-k and the refinement in one kernel from the pooled
+// blocks (the pooled form of refine_fused.hip); the same row limit. vmv must
+// hold V_j^T M V_j already (launch_vmv).
+hipError_t launch_select_refine_fused(const double* qpool, const double* kpool,
+                                      const double* vpool, const double* M, const double* vmv,
+                                      const ress_shape& s, const SelConfig& cfg, double scale,
+                                      int32_t rounds, double rho, double eps, int32_t k_max,
+                                      int32_t* kept_idx, int32_t* kept_cnt, double* J_init,
+                                      double* J_final, hipStream_t st);
 
 hipError_t launch_gram(const void* w_o, int dtype, int d_model, const ress_shape& s, double* M,
                        hipStream_t st);

@@ -24,16 +24,12 @@
 // blocks: R = 16 rows up to 1088 blocks, R = 8 beyond (half of each
 // matrix-core row group then idles).
 #include "ress_internal.h"
-#include "refine_common.h"
+#include "select_fused_steps.h"
 
 namespace ress {
 namespace {
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kScratch = 16384;  // bytes: vout partials, then w and a, then histograms
-
-__host__ __device__ inline int row_stride(int n) { return ((n + 3) & ~3) + 4; }  // doubles
 
 __host__ __device__ inline size_t fused_sel_lds(int R, int n) {
   return (size_t)R * row_stride(n) * 8 + kScratch;
@@ -57,114 +53,24 @@ __global__ __launch_bounds__(64 * R) void select_fused_kernel(
   const double* kh = kpool + (size_t)h * n * kD;
   const double* vh = vpool ? vpool + (size_t)h * n * kD : nullptr;
 
-  // ---- 1. logits of the R rows against every key block ------------------
-  // A operand: row l16 (clamped to a valid row), dims 4s + q4
-  {
-    double qa[16];
-    const double* qr = qh + (size_t)min(i0 + min(l16, R - 1), nq - 1) * kD;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qa[s] = qr[4 * s + q4];
-    for (int g = w; g < ngroups; g += R) {
-      const double* kr = kh + (size_t)min(16 * g + l16, n - 1) * kD;
-      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int s = 0; s < 16; ++s)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[s], kr[4 * s + q4], acc, 0, 0, 0);
-      // element e: row q4 + 4e, key block 16 g + l16
-      const int j = 16 * g + l16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = q4 + 4 * e;
-        if (r < R && j < n) rows[r * ns + j] = scale * acc[e];
-      }
-    }
-  }
+  // ---- 1. logits of the R rows against every key block
+  fused_logits<R>(qh, kh, nq, n, i0, scale, rows, ns);
   __syncthreads();
 
-  // ---- 2. softmax of each row (its wave; padding blocks hold 0) --------
+  // ---- 2. softmax of each row (its wave; padding blocks hold 0)
   const bool live = i0 + w < nq;
   double* myrow = rows + w * ns;
-  {
-    double v[KPL];
-    double mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const int j = lane + 64 * k;
-      v[k] = j < n ? myrow[j] : -INFINITY;
-      mx = fmax(mx, v[k]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
-    double sum = 0.0;
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const int j = lane + 64 * k;
-      v[k] = j < n ? exp(v[k] - mx) : 0.0;
-      sum += v[k];
-    }
-    sum = wave_sum64(sum);
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const int j = lane + 64 * k;
-      if (j < ns) myrow[j] = j < n ? v[k] / sum : 0.0;  // P, zero past the row's end
-    }
-  }
+  fused_softmax<KPL>(myrow, n, ns);
   __syncthreads();
 
   if (drift) {
-    // ---- 3a. vout_r = sum_j P_rj V_j: wave w takes dims 16 (w & 3) ..
-    // +15 of the 16-row tile and one part of the key blocks (R / 4 parts,
-    // contiguous runs of 4-block steps); A = P (rows l16, blocks 4t + q4),
-    // B = V (blocks 4t + q4, dims 16 dg + l16)
+    // ---- 3a-3b. vout, w = M vout and a (w and a then take the place of the
+    // partial sums)
     double* part = reinterpret_cast<double*>(scratch);  // [2][R][64]
-    const int dg = w & 3, kq = w >> 2;
-    constexpr int kParts = R / 4;
-    const int steps = (n + 3) >> 2;
-    const int t0 = kq * steps / kParts, t1 = (kq + 1) * steps / kParts;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-    const double* prow = rows + min(l16, R - 1) * ns;
-    for (int t = t0; t < t1; ++t) {
-      const int j = 4 * t + q4;  // P is zero for j >= n (row padding)
-      const double a = l16 < R ? prow[j] : 0.0;
-      const double b = vh[(size_t)min(j, n - 1) * kD + 16 * dg + l16];
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
-    }
-    // parts 0 and 1 store, parts 2 and 3 add (fixed order: (p0 + p2) + (p1 + p3))
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if ((kq >> 1) == half) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = q4 + 4 * e;
-          if (r < R) {
-            double* dst = part + ((kq & 1) * R + r) * kD + 16 * dg + l16;
-            *dst = half == 0 ? acc[e] : *dst + acc[e];
-          }
-        }
-      }
-      __syncthreads();
-    }
-    // ---- 3b. per row: vout, w = M vout, a = vout . w (w and a then take
-    // the place of the partial sums)
-    double* wv = part;        // [R][64]
-    double* av = wv + R * kD;  // [R]
-    {
-      const double vo = part[w * kD + lane] + part[(R + w) * kD + lane];
-      __syncthreads();  // every row has read its partial sums
-      wv[w * kD + lane] = vo;
-      wave_lds_sync();
-      double x = vo;
-      if (M != nullptr) {
-        const double* Mrow = M + ((size_t)h * kD + lane) * kD;
-        x = 0.0;
-#pragma unroll 8
-        for (int e = 0; e < kD; ++e) x = fma(Mrow[e], wv[w * kD + e], x);
-      }
-      const double a = wave_sum64(vo * x);
-      wave_lds_sync();
-      wv[w * kD + lane] = x;
-      if (lane == 0) av[w] = a;
-    }
+    double* wv = part;                                  // [R][64]
+    double* av = wv + R * kD;                           // [R]
+    fused_vout<R>(rows, ns, n, vh, M ? M + (size_t)h * kD * kD : nullptr, part, nullptr, wv,
+                  av);
     __syncthreads();
     // ---- 3c. c_rj = w_r . V_j; the key replaces P in the row buffer
     {
@@ -185,11 +91,7 @@ __global__ __launch_bounds__(64 * R) void select_fused_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = q4 + 4 * e;
-            if (r < R) {
-              const double q = fmax(av[r] - 2.0 * acc2[e] + vmj, 0.0);
-              const double p = rows[r * ns + j];
-              rows[r * ns + j] = p * sqrt(q) / fmax(1.0 - p, eps);
-            }
+            if (r < R) rows[r * ns + j] = fused_drift_key(rows[r * ns + j], acc2[e], av[r], vmj, eps);
           }
         }
       }
@@ -197,24 +99,10 @@ __global__ __launch_bounds__(64 * R) void select_fused_kernel(
     __syncthreads();
   }
 
-  // ---- 4. exact top-c_h per row, keep list ascending ----------------------
+  // ---- 4. exact top-c_h per row, keep list ascending
   if (!live) return;  // whole wave; no barrier follows
   uint32_t* whist = reinterpret_cast<uint32_t*>(scratch) + 256 * w;
-  SelKeys<KPL> keys(reinterpret_cast<const uint64_t*>(myrow), n, lane);
-  uint64_t member = 0, always = 0;
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) {
-    const int j = lane + 64 * k;
-    keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
-    if (j < n) {
-      if (sel_always(cfg, j))
-        always |= 1ull << k;
-      else
-        member |= 1ull << k;
-    }
-  }
-  const int c = cfg.keep[h] - cfg.n_always;
-  const uint64_t kept = wave_select<KPL>(keys, member, n, c, whist) | always;
+  const uint64_t kept = fused_topk_bits<KPL>(myrow, n, cfg, cfg.keep[h] - cfg.n_always, whist);
   const size_t row = (size_t)h * nq + i0 + w;
   int32_t* out = kept_idx + row * k_max;
   const uint64_t below = (1ull << lane) - 1ull;

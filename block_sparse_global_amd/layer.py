@@ -19,6 +19,7 @@ from ._lib import (
     SELECT_FUSED_MAX_BLOCKS,
     RESS_SCORE_DRIFT,
     RESS_SCORE_PROB,
+    SELECT_REFINE_FUSED_MAX_BLOCKS,
     Shape,
     ress_block_pool,
     ress_block_score,
@@ -27,6 +28,7 @@ from ._lib import (
     ress_refine_workspace_size,
     ress_select_cdf,
     ress_select_fused,
+    ress_select_refine_fused,
     ress_select_topk,
     ress_sparse_attn_fwd,
 )
@@ -41,18 +43,23 @@ SELECT_FUSED_AUTO_MAX_BLOCKS = 128
 
 
 def select_path(shape: Shape, select_impl: str, rounds: int, tau) -> str:
-    """The selection calls used for ``select_impl`` on ``shape``: "fused"
-    (ress_select_fused: score and top-k in one pass, the block map and key
-    never written) applies to top-k selection without refinement (the
-    refinement reads P and the key) on rows of at most SELECT_FUSED_MAX_BLOCKS
-    key blocks; otherwise ress_block_score + ress_select_topk / _cdf. "auto"
-    takes the fused pass where it applies and the rows hold at most
-    SELECT_FUSED_AUTO_MAX_BLOCKS key blocks."""
+    """The selection calls used for ``select_impl`` on ``shape``: "fused" is
+    one pass per row tile with the block map and key never written:
+    ress_select_fused (score and top-k) on rows of at most
+    SELECT_FUSED_MAX_BLOCKS key blocks, or, with refinement rounds,
+    ress_select_refine_fused (score, top-k and refinement) on rows of at
+    most SELECT_REFINE_FUSED_MAX_BLOCKS; otherwise (and for the cumulative
+    threshold) ress_block_score + ress_select_topk / _cdf [+ the
+    refinement call]. "auto" takes the fused pass for top-k without
+    refinement on rows of at most SELECT_FUSED_AUTO_MAX_BLOCKS key blocks,
+    where it measured faster, else the unfused calls."""
     if select_impl not in ("fused", "unfused", "auto"):
         raise ValueError(select_impl)
-    applies = rounds == 0 and tau is None and shape.nk <= SELECT_FUSED_MAX_BLOCKS
+    limit = SELECT_FUSED_MAX_BLOCKS if rounds == 0 else SELECT_REFINE_FUSED_MAX_BLOCKS
+    applies = tau is None and shape.nk <= limit
     if select_impl == "auto":
-        return "fused" if applies and shape.nk <= SELECT_FUSED_AUTO_MAX_BLOCKS else "unfused"
+        return ("fused" if applies and rounds == 0 and shape.nk <= SELECT_FUSED_AUTO_MAX_BLOCKS
+                else "unfused")
     if select_impl == "fused" and not applies:
         return "unfused"
     return select_impl
@@ -85,12 +92,13 @@ class BlockSparseGlobalAttention:
         restoration kernel of ReSS Appendix E falls back to its unfused path
         outside its limits); both give the same bits. ``select_impl``:
         "unfused" (ress_block_score then ress_select_topk), "fused"
-        (ress_select_fused, the map and key never written; top-k selection
-        without refinement only, rows of at most SELECT_FUSED_MAX_BLOCKS key
-        blocks, else the unfused calls) or "auto" (the fused pass on rows of
-        at most SELECT_FUSED_AUTO_MAX_BLOCKS key blocks, where it measured
-        faster, else the unfused calls); all give the same lists up to
-        near-ties."""
+        (ress_select_fused, or ress_select_refine_fused with refinement
+        rounds, which then also refines: one pass per row tile, the map and
+        key never written, within the row limits of select_path, else the
+        unfused calls) or "auto" (the fused pass for top-k without
+        refinement on rows of at most SELECT_FUSED_AUTO_MAX_BLOCKS key
+        blocks, where it measured faster, else the unfused calls); all give
+        the same lists up to near-ties."""
         refine_impl = refine_path(shape, refine_impl)
         self.select_impl = select_path(shape, select_impl, int(rounds), tau)
         if mode not in ("prob", "drift"):
@@ -129,7 +137,7 @@ class BlockSparseGlobalAttention:
         self.refine_impl = refine_impl
         self.workspace = (torch.empty(ress_refine_workspace_size(shape), dtype=torch.uint8,
                                       device=device)
-                          if rounds > 0 and refine_impl == "rounds" else None)
+                          if rounds > 0 and refine_impl == "rounds" and not fused else None)
         self.lse = (torch.empty((H, Np), dtype=torch.float32, device=device)
                     if with_lse else None)
         self.out = None
@@ -148,6 +156,12 @@ class BlockSparseGlobalAttention:
                          stream)
 
     def select(self, stream=None):
+        if self.select_impl == "fused" and self.rounds > 0:
+            ress_select_refine_fused(self.qpool, self.kpool, self.vpool, self.M, self.shape,
+                                     self.scale, self.eps, self.keep, self.always, self.rounds,
+                                     self.rho, self.k_max, self.vmv, self.kept_idx,
+                                     self.kept_cnt, self.J_init, self.J_final, stream)
+            return
         if self.select_impl == "fused":
             mode = RESS_SCORE_DRIFT if self.mode == "drift" else RESS_SCORE_PROB
             ress_select_fused(self.qpool, self.kpool, self.vpool, self.M, self.shape, mode,
@@ -163,8 +177,8 @@ class BlockSparseGlobalAttention:
                          self.kept_idx, self.kept_cnt, stream)
 
     def refine(self, stream=None):
-        if self.rounds <= 0:
-            return
+        if self.rounds <= 0 or self.select_impl == "fused":
+            return  # the fused pass refines on chip
         if self.refine_impl == "fused":
             ress_refine_dropset_fused(self.P, self.key, self.vpool, self.vout, self.M,
                                       self.shape, self.keep, self.always, self.rounds,

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RESS_VERSION 4
+#define RESS_VERSION 5
 
 /* Status codes. */
 #define RESS_OK 0
@@ -164,6 +164,36 @@ int ress_select_fused(const double* qpool, const double* kpool, const double* vp
                       const double* M, ress_shape shape, int mode, double scale, double eps,
                       const int32_t* keep, const uint8_t* always_keep, int32_t k_max,
                       double* vmv, int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
+ * ress_select_refine_fused — the whole selection with refinement in one
+ * pass per tile of query-block rows: ress_block_score in drift mode,
+ * ress_select_topk and ress_refine_dropset, with the block map P and the
+ * drift key never leaving the chip (the fused selection of the ReSS page's
+ * Appendix E, whose kernel sweeps each row once and writes only the new
+ * drop set; §4.1-§4.3, Eq. 1-17). A workgroup takes 8 consecutive rows of
+ * one head: their map rows stay in LDS next to the refinement's gains,
+ * and the drift key of each (row, block), which the top-k and every
+ * round's gains need, is re-formed from the product w_r . V_j (Eq. 9
+ * expansion) in the same matrix-core instructions as the gains. The keep
+ * sets match the three calls up to ties whose keys or gains differ by
+ * float64 rounding (vout is summed in another fixed order, as in
+ * ress_select_fused); J_init and J_final agree to float64 rounding.
+ *
+ * qpool, kpool, vpool, M, scale, eps: as for ress_block_score in drift mode
+ * (vpool required). keep, always_keep, rounds, rho, k_max: as for
+ * ress_refine_dropset. vmv: device float64 [H][n_k], written first with
+ * V_j^T M_h V_j (as ress_select_fused). kept_idx [H][n_q][k_max], kept_cnt
+ * [H][n_q]: the refined keep lists (ascending, -1 padded). J_init, J_final
+ * (optional, float64 [H][n_q]): J of the top-k set and of the best set.
+ * Rows of at most 1088 key blocks (RESS_ERR_UNSUPPORTED beyond: use the
+ * separate calls). Each workgroup keeps about 156 KB of LDS. No workspace.
+ */
+int ress_select_refine_fused(const double* qpool, const double* kpool, const double* vpool,
+                             const double* M, ress_shape shape, double scale, double eps,
+                             const int32_t* keep, const uint8_t* always_keep, int32_t rounds,
+                             double rho, int32_t k_max, double* vmv, int32_t* kept_idx,
+                             int32_t* kept_cnt, double* J_init, double* J_final, void* stream);
 
 /*
  * ress_select_cdf — per (head, query-block row) keep set under a cumulative

@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_every_call():
     names = declared_functions()
     for f in ("ress_block_pool", "ress_block_score", "ress_select_topk", "ress_select_cdf",
-              "ress_refine_dropset", "ress_refine_dropset_fused", "ress_refine_dropset_noalloc",
+              "ress_select_fused", "ress_select_refine_fused", "ress_refine_dropset", "ress_refine_dropset_fused", "ress_refine_dropset_noalloc",
               "ress_refine_workspace_size",
               "ress_sparse_attn_fwd",
               "ress_gram_from_wo", "ress_head_budgets", "ress_residual_drift",
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(b.LIB_PATH)
     for f in declared_functions():
         assert hasattr(lib, f), f"{f} declared in ress.h but not exported"
-    assert b.ress_version() == 4
+    assert b.ress_version() == 5
     assert set(b.ENTRY_POINTS) == set(declared_functions())
 
 
@@ -221,6 +221,36 @@ def test_fused_refine_argument_checks():
     assert b.REFINE_FUSED_MAX_BLOCKS == 1088
 
 
+def test_select_refine_fused_argument_checks():
+    import block_sparse_global_amd as b
+    L = b.LIB
+    d = ctypes.c_double
+    _, keep = _arr([2, 3], np.int32)
+    _, alw = _arr([0, 0, 0, 1], np.uint8)
+
+    def call(s, qp=FAKE, vp=FAKE, vmv=FAKE, keep=keep, alw=alw, rounds=2, rho=0.5, eps=1e-4,
+             scale=0.125, k_max=3):
+        return L.ress_select_refine_fused(qp, FAKE, vp, None, s, d(scale), d(eps), keep, alw,
+                                          rounds, d(rho), k_max, vmv, FAKE, FAKE, None, None,
+                                          None)
+    # rows longer than the tile's LDS holds: unsupported, nothing launched
+    long = _shape(H=1, N=1089 * 64, N_pad=1089 * 64)
+    _, keep1 = _arr([2], np.int32)
+    assert call(long, keep=keep1, alw=None) == -2
+    assert "1088" in b.ress_last_error()
+    s = _shape(H=2)  # n = 4
+    assert call(s, qp=None) == -1 and "qpool" in b.ress_last_error()
+    assert call(s, vp=None) == -1 and "vpool" in b.ress_last_error()
+    assert call(s, vmv=None) == -1 and "vmv" in b.ress_last_error()
+    assert call(s, qp=MISALIGNED) == -1 and "aligned" in b.ress_last_error()
+    assert call(s, rounds=-1) == -1 and "rounds" in b.ress_last_error()
+    assert call(s, rho=0.0) == -1 and "rho" in b.ress_last_error()
+    assert call(s, eps=0.0) == -1 and "eps" in b.ress_last_error()
+    assert call(s, scale=float("inf")) == -1 and "scale" in b.ress_last_error()
+    assert call(s, k_max=2) == -1                     # k_max below a budget
+    assert b.SELECT_REFINE_FUSED_MAX_BLOCKS == 1088
+
+
 def test_noalloc_refine_argument_checks():
     import block_sparse_global_amd as b
     L = b.LIB
@@ -272,7 +302,11 @@ def test_layer_argument_checks_before_any_allocation():
     assert select_path(longer, "fused", 0, None) == "fused"
     assert select_path(s, "fused", 0, None) == "fused"
     assert select_path(b.Shape(1, 2177 * 64, 2177 * 64, 64, 64), "fused", 0, None) == "unfused"
-    assert select_path(short, "fused", 2, None) == "unfused"
+    # with refinement rounds "fused" is the one-pass selection up to 1088 blocks
+    assert select_path(short, "fused", 2, None) == "fused"
+    assert select_path(s, "fused", 2, None) == "unfused"
+    assert select_path(b.Shape(1, 1088 * 64, 1088 * 64, 64, 64), "fused", 2, None) == "fused"
+    assert select_path(short, "fused", 2, 0.5) == "unfused"
     assert select_path(short, "unfused", 0, None) == "unfused"
     with pytest.raises(ValueError):
         select_path(short, "fast", 0, None)

@@ -149,6 +149,15 @@ def test_guard_bytes_around_every_output(name, w):
         for g, s in ((fi, "kept_idx"), (fc, "kept_cnt"), (fv, "vmv")):
             g.check(f"ress_select_fused {s}")
 
+    if nk <= b.SELECT_REFINE_FUSED_MAX_BLOCKS:
+        fi, fc = Guarded((H, nq, k_max), torch.int32), Guarded((H, nq), torch.int32)
+        fv, J0, J1 = Guarded((H, nk), f64), Guarded((H, nq), f64), Guarded((H, nq), f64)
+        b.ress_select_refine_fused(qp.t, kp.t, vp.t, M, shape, 0.125, 1e-4, keep, alw, 2, 0.5,
+                                   k_max, fv.t, fi.t, fc.t, J0.t, J1.t)
+        for g, s in ((fi, "kept_idx"), (fc, "kept_cnt"), (fv, "vmv"), (J0, "J_init"),
+                     (J1, "J_final")):
+            g.check(f"ress_select_refine_fused {s}")
+
     if w.dtype == "bf16":
         dm = 128
         L = synth.make_sublayer(Np, H, D, dm, seed=7)

@@ -244,11 +244,12 @@ def test_select_cdf(case, tau):
 
 
 def _refine_rows_parity(P, vpool, vout, M, keep, always, start, rounds, rho, rows, g_idx,
-                        g_cnt, g_J0, g_J1, D):
+                        g_cnt, g_J0, g_J1, D, flagged_rows=None):
     """The oracle's refinement of `rows` (threads over chunks) against the
     GPU's: equal keep sets and J_final unless the oracle logged a near-tie on
     the row's trajectory (then the GPU's J_final must equal the oracle's J of
-    the GPU's own set), J_init always. Returns the number of flagged rows."""
+    the GPU's own set), J_init always. Returns the number of flagged rows;
+    their (h, i) are added to the set `flagged_rows` when one is given."""
     n = P.shape[-1]
     cand = always == 0
     chunks = [rows[j:j + 128] for j in range(0, len(rows), 128)]
@@ -267,6 +268,8 @@ def _refine_rows_parity(P, vpool, vout, M, keep, always, start, rounds, rho, row
                 continue
             assert mg[h, i] < 1e-6, f"row ({h},{i}) differs without a near-tie ({mg[h, i]:.3e})"
             flagged += 1
+            if flagged_rows is not None:
+                flagged_rows.add((h, i))
             Mh = np.eye(D) if M is None else M[h]
             e = vout[h, i][None] - vpool[h]
             d = P[h, i][:, None] * e
@@ -663,6 +666,95 @@ def test_fused_refine_matches_per_round_kernels(name):
                                                         "J_final")):
         assert np.array_equal(a, c), f"{what} differs"
     assert np.all(res["fused"][3] <= res["fused"][2])
+
+
+def _select_refine_fused_check(w, x, M):
+    """ress_select_refine_fused (drift scoring, top-k and refinement in one
+    pass per tile of 8 rows, the map and key never written) on every row:
+    against the oracle's refinement started from the oracle's own top-k
+    (rows whose top-k cut is a near-tie below 1e-6 relative excepted: their
+    starting set may be the other one), and against the split calls (the
+    same lists except on such near-tie rows, J_init to 1e-9)."""
+    b = _lib()
+    shape = b.Shape(*w.shape_args())
+    Mt = torch.from_numpy(M).cuda() if M is not None else None
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    res = {}
+    for impl in ("fused", "unfused"):
+        layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode="drift",
+                                             rounds=w.rounds, rho=w.rho, M=Mt, select_impl=impl)
+        assert layer.select_impl == impl
+        if impl == "fused":
+            assert layer.P is None and layer.key is None and layer.workspace is None
+        layer.pool(q, k, v)
+        layer.score()
+        layer.select()
+        layer.refine()
+        torch.cuda.synchronize()
+        res[impl] = [a.cpu().numpy() for a in (layer.kept_idx, layer.kept_cnt, layer.J_init,
+                                               layer.J_final)]
+        del layer
+    gi, gc, gJ0, gJ1 = res["fused"]
+    n = w.n_kblocks
+    check_lists_wellformed(gi, gc, x["keep"], x["always"], n)
+    assert np.all(gJ1 <= gJ0)
+    qp = oracle.block_pool(f64(x["q"], w), w.N, w.block)
+    kp = oracle.block_pool(f64(x["k"], w), w.N, w.kblock)
+    vp = oracle.block_pool(f64(x["v"], w), w.N, w.kblock)
+    P = oracle.block_map(qp, kp, 1.0 / math.sqrt(w.head_dim))
+    key, vout, _ = oracle.drift_key(P, vp, M, 1e-4)
+    start, tmargin = oracle.select_topk(key, x["keep"], x["always"])
+    tie_rows = {(h, i) for h in range(w.heads) for i in range(w.n_blocks) if tmargin[h, i] < 1e-6}
+    rows = [(h, i) for h in range(w.heads) for i in range(w.n_blocks) if (h, i) not in tie_rows]
+    flagged = set()
+    _refine_rows_parity(P, vp, vout, M, x["keep"], x["always"], start, w.rounds, w.rho, rows,
+                        gi, gc, gJ0, gJ1, w.head_dim, flagged)
+    ui, uc, uJ0, uJ1 = res["unfused"]
+    same = np.all(kept_mask_from_lists(gi, gc, n) == kept_mask_from_lists(ui, uc, n), axis=-1)
+    differ = {(int(h), int(i)) for h, i in zip(*np.nonzero(~same))}
+    assert differ <= tie_rows | flagged, sorted(differ - tie_rows - flagged)[:5]
+    ok = np.array([[(h, i) not in tie_rows for i in range(w.n_blocks)] for h in range(w.heads)])
+    assert np.allclose(gJ0[ok], uJ0[ok], rtol=1e-9, atol=0)
+    print(f"[select-refine-fused] {w.name}: {len(rows)} rows against the oracle, "
+          f"{len(tie_rows)} top-k near-tie rows, {len(flagged)} refinement near-tie rows, "
+          f"{len(differ)} rows differ from the split calls; mean J_init {gJ0.mean():.4e} -> "
+          f"J_final {gJ1.mean():.4e}")
+
+
+@pytest.mark.parametrize("name", ["views100", "views8-k64", "gram", "max1088", "short"])
+def test_select_refine_fused_matches_oracle(name):
+    _select_refine_fused_check(*_fused_case(name))
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_select_refine_fused_random_shapes(idx):
+    """Seeded ragged shapes: both block grids, one to three heads with unequal
+    budgets, special-token blocks or none, bf16 or float32 inputs, 1-4
+    rounds, with or without a Gram matrix, up to the 1088-block limit."""
+    rng = np.random.default_rng(900 + idx)
+    while True:
+        block = int(rng.choice([64, 128]))
+        ppv = int(rng.choice([int(rng.integers(20, 700)), int(rng.integers(5000, 17000))]))
+        views = 1 if ppv > 5000 else int(rng.integers(1, 4))
+        w = custom(name=f"srf{idx}", views=views, patches_per_view=ppv,
+                   specials_per_view=int(rng.choice([0, 5])), heads=int(rng.integers(1, 4)),
+                   block=block, key_block=int(rng.choice([0, 64])) if block == 128 else 0,
+                   dtype=str(rng.choice(["bf16", "f32"])),
+                   sparsity=tuple(sorted(float(s) for s in rng.uniform(0.3, 0.95, 2))),
+                   score="drift", rounds=int(rng.integers(1, 5)),
+                   rho=float(rng.choice([0.5, 1.0])), seed=int(rng.integers(1 << 30)))
+        if not 3 <= w.n_kblocks <= 1088:
+            continue
+        try:
+            x = synth.make_inputs(w)
+        except ValueError:
+            continue
+        break
+    M = synth.make_gram(w.heads, w.head_dim, seed=idx) if rng.random() < 0.5 else None
+    print(f"\n[select-refine-fused random {idx}] N={w.N} B={w.block} Bk={w.kblock} H={w.heads} "
+          f"n_k={w.n_kblocks} rounds={w.rounds} rho={w.rho} dtype={w.dtype} gram={M is not None}",
+          flush=True)
+    _select_refine_fused_check(w, x, M)
 
 
 def test_fused_refine_falls_back_beyond_its_row_limit():
