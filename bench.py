@@ -47,8 +47,8 @@ CDF_TAU = 0.05
 ATTN_TRAFFIC = {
     "workload": "views100",
     "source_sha256": "1baf8b524016ef0a2fc6bbb645b8a985647e6ed8e691d234dfc5b29b62d094f7",
-    "read_bytes": 9830330624,
-    "write_bytes": 457515328,
+    "read_bytes": 9806035712,
+    "write_bytes": 457514976,
 }
 
 
