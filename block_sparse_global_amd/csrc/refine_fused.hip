@@ -57,13 +57,12 @@ template <bool POOLED>
 constexpr int fused_rows() { return POOLED ? 8 : 16; }
 constexpr int kMaxWords = 17;           // 64-block words per row: n_k <= 1088
 constexpr int kSlotBytes = 1024;        // per-wave scratch
-// LDS strides padded off multiples of 64 banks: the 16 rows' u vectors (read
-// together as matrix operands) and the gains rows (stored four rows at a
+// LDS strides padded off multiples of 64 banks: the 16 operand rows (u, and
+// w in the pooled form; read together as matrix operands) and the gains rows (stored four rows at a
 // time) then spread over all banks
 constexpr int kSlotStride = kSlotBytes + 16;
 __host__ __device__ inline int gains_stride(int KW) { return 64 * KW + 16; }  // uint64 words
 constexpr int kChgCap = 128;            // change-list entries per flush
-
 
 // LDS layout of a tile of `rows` rows of n key blocks (KW = ceil(n / 64)
 // words per row), every region 16-byte aligned: about 159 KB for 16 rows
