@@ -46,9 +46,9 @@ CDF_TAU = 0.05
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "1baf8b524016ef0a2fc6bbb645b8a985647e6ed8e691d234dfc5b29b62d094f7",
-    "read_bytes": 9806035712,
-    "write_bytes": 457514976,
+    "source_sha256": "2074e01e40aee518a1e56c4da38db27d547a3c4592ad714851d760cecc92ccd6",
+    "read_bytes": 9854327936,
+    "write_bytes": 457514496,
 }
 
 

@@ -5,10 +5,12 @@
 // float32 accumulation, for gfx950.
 //
 // Work decomposition: one workgroup per (query block, head); BLK/32 waves,
-// each owning 32 query rows; key blocks hold KBLK <= BLK keys (KBLK = BLK, or
-// 64-key blocks under 128-query blocks). Per kept key block the K and V tiles are copied
-// straight from HBM into LDS (global_load_lds, double-buffered: the next kept
-// block streams in while the current one is computed) and every wave computes
+// each owning 32 query rows. A tile holds KBLK = BLK keys: one kept key block
+// of BLK keys, or, on the grid of 64-key blocks under 128-query blocks, two
+// kept key blocks (any two, in list order; the second half is masked when a
+// row's count is odd). Per tile the K and V tiles are copied
+// straight from HBM into LDS (global_load_lds, double-buffered: the next
+// tile streams in while the current one is computed) and every wave computes
 //   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16; A = K from LDS, B = Q^T held in
 //                  registers for the whole kernel)
 //   O^T += V^T P^T (A = V^T read from the row-major V tile with LDS
@@ -121,22 +123,26 @@ constexpr float kSumMax = 0x1p64f;
 // max exceeds the one in use by less than this keeps it, so p <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int BLK, int KBLK, typename Tin, typename Tout>
+template <int BLK, int KBLK, bool PAIR, typename Tin, typename Tout>
 __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     const Tin* __restrict__ Q, const Tin* __restrict__ Kx,
     const Tin* __restrict__ Vx, const int32_t* __restrict__ kept_idx,
     const int32_t* __restrict__ kept_cnt, int k_max, int n, int N, int N_pad,
     float scale, Tout* __restrict__ out, float* __restrict__ lse) {
-  // n: key blocks (of KBLK keys) per head; gridDim.x: query blocks per head
+  // n: key blocks (of kSrc keys, below) per head; gridDim.x: query blocks per head
   static_assert(KBLK <= BLK && BLK % KBLK == 0, "key blocks no larger than query blocks");
+  // PAIR: 64-key blocks taken two kept blocks at a time into one 128-key
+  // tile (waves 0-1 copy the first block, waves 2-3 the second)
+  static_assert(!PAIR || KBLK == 128, "pairs of 64-key blocks fill 128-key tiles");
+  constexpr int kSrc = PAIR ? 64 : KBLK;  // keys per key block of the list
   constexpr int kKT = KBLK / 32;     // 32-key tiles per key block
   constexpr int kTile = KBLK * kD;   // elements per K or V tile
   constexpr int kRowsPerWave = KBLK / (BLK / 32);  // tile rows each wave copies
   constexpr int kWin = kRowsPerWave / 8;           // 8-row copy windows per wave
   static_assert(kRowsPerWave % 16 == 0, "the K swizzle repeats every 16 rows");
   // One K buffer and two V buffers (48 KB at KBLK = 128, so three workgroups
-  // share a CU): V of the next kept block streams in during the whole of the
-  // current block, K of the next block once every wave has finished its
+  // share a CU): V of the next tile streams in during the whole of the
+  // current tile, K of the next tile once every wave has finished its
   // S = K Q^T product.
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kTile];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kTile];
@@ -214,14 +220,15 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   };
   auto block_of = [&](int kb) { return list ? list[kb] : kb; };
 
-  // ---- staging of the K or V tile of block j into an LDS buffer. Each wave
+  // ---- staging of a K or V tile into an LDS buffer. Each wave
   // copies kWin windows of 8 rows; in window it, lane l fills row
   // r = kRowsPerWave*w + 8*it + l/8 at physical chunk l%8, i.e. logical chunk
   // (l%8) ^ swz(r). For V, swz(r) = 2*((l/8)&3) does not depend on it; for
   // K, swz(r) = (l/16) ^ (4*(it&1)) (kRowsPerWave is a multiple of 16). So
   // two per-lane offsets (windows 0 and 1) plus compile-time row steps cover
-  // all windows. Rows past N (last block only) are read from row N-1: finite
-  // data whose scores are masked to -inf, so p = 0 multiplies a finite V row.
+  // all windows. Rows past N (last key block only) are read from row N-1:
+  // finite data whose scores are masked to -inf, so p = 0 multiplies a finite
+  // V row; so is the empty second half of a pair tile (block ja again).
   const int row0 = kRowsPerWave * w + (lane >> 3);
   const int kgo0 = row0 * kD + (((lane & 7) ^ (lane >> 4)) * 8);
   const int kgo1 = (row0 + 8) * kD + (((lane & 7) ^ (lane >> 4) ^ 4) * 8);
@@ -229,31 +236,49 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   auto tile_off = [&](int it, bool is_v) {
     return is_v ? vgo0 + 8 * it * kD : ((it & 1) ? kgo1 : kgo0) + 16 * (it >> 1) * kD;
   };
-  auto issue_tile = [&](const Tin* X, uint16_t* dst, int j, bool is_v) {
-    {
-      // block base (uniform) + 32-bit per-lane byte offset: the copies use
-      // the scalar-base addressing form
-      const char* base = reinterpret_cast<const char*>(
-          X + head_off + (size_t)__builtin_amdgcn_readfirstlane(j) * KBLK * kD);
-      const bool full = (j + 1) * KBLK <= N;
-      if (full) {
+  // the tile of key block ja (and, in pairs, jb): this wave copies its
+  // kRowsPerWave tile rows from block src, whose row 0 is tile row hrow
+  auto issue_tile = [&](const Tin* X, uint16_t* dst, int ja, int jb, bool is_v) {
+    const bool second = PAIR && w >= 2;
+    const int src = __builtin_amdgcn_readfirstlane(second ? jb : ja);
+    const int hrow = second ? 64 : 0;  // tile row of the source block's row 0
+    // block base (uniform) + 32-bit per-lane byte offset: the copies use
+    // the scalar-base addressing form
+    const char* base = reinterpret_cast<const char*>(X + head_off + (size_t)src * kSrc * kD);
+    const bool full = (src + 1) * kSrc <= N;
+    if (full) {
 #pragma unroll
-        for (int it = 0; it < kWin; ++it) {
-          const uint32_t off = 2u * (uint32_t)tile_off(it, is_v);
-          gload_lds16(reinterpret_cast<const uint16_t*>(base + off),
-                      dst + (kWin * w + it) * 512);
-        }
-      } else {
-        const int last = N - 1 - j * KBLK;
+      for (int it = 0; it < kWin; ++it) {
+        const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) - hrow * kD);
+        gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (kWin * w + it) * 512);
+      }
+    } else {
+      const int last = N - 1 - src * kSrc;
 #pragma unroll
-        for (int it = 0; it < kWin; ++it) {
-          const int r = row0 + 8 * it;
-          const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) + (min(r, last) - r) * kD);
-          gload_lds16(reinterpret_cast<const uint16_t*>(base + off),
-                      dst + (kWin * w + it) * 512);
-        }
+      for (int it = 0; it < kWin; ++it) {
+        const int r = row0 + 8 * it - hrow;  // row within the source block
+        const uint32_t off = 2u * (uint32_t)(tile_off(it, is_v) - hrow * kD + (min(r, last) - r) * kD);
+        gload_lds16(reinterpret_cast<const uint16_t*>(base + off), dst + (kWin * w + it) * 512);
       }
     }
+  };
+  // the tile starting at list position kb: its blocks, and where the next
+  // tile starts
+  struct TileAt { int ja, jb, next; bool has_b; };
+  auto tile_at = [&](int kb) {
+    TileAt t;
+    t.ja = block_of(kb);
+    if constexpr (PAIR) {
+      const int kb2 = next_valid(kb + 1);
+      t.has_b = kb2 < cnt;
+      t.jb = t.has_b ? block_of(kb2) : t.ja;
+      t.next = t.has_b ? next_valid(kb2 + 1) : cnt;
+    } else {
+      t.has_b = false;
+      t.jb = t.ja;
+      t.next = next_valid(kb + 1);
+    }
+    return t;
   };
 
   // Per-lane LDS element offsets of the MFMA operands (the buffer, the
@@ -271,17 +296,18 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
                  (q & 1) * 4;
   }
 
-  // ---- one kept block, V from buffer B (compile-time, so all LDS offsets
-  // are immediates); ONLINE: the second pass, with a running max. Returns
-  // the next list position.
+  // ---- one tile (from list position kb), V from buffer B (compile-time, so
+  // all LDS offsets are immediates); ONLINE: the second pass, with a running
+  // max. Returns the list position of the next tile.
   auto process = [&](auto bufc, auto onlinec, int kb) {
     constexpr int B = decltype(bufc)::value;
     constexpr bool ONLINE = decltype(onlinec)::value;
-    const int j = block_of(kb);
-    const int kb_next = next_valid(kb + 1);
+    const TileAt cur = tile_at(kb);
+    const int kb_next = cur.next;
     const bool more = kb_next < cnt;
-    const int j_next = more ? block_of(kb_next) : 0;
-    if (more) issue_tile(Vx, Vs[B ^ 1], j_next, true);
+    TileAt nxt{0, 0, 0, false};
+    if (more) nxt = tile_at(kb_next);
+    if (more) issue_tile(Vx, Vs[B ^ 1], nxt.ja, nxt.jb, true);
 
     // S^T = K Q^T; the K operands of tile kt+1 are read while tile kt's
     // MFMAs run
@@ -312,21 +338,39 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     // every wave has read its K operands: the K tile of the next block may
     // replace this one
     lds_barrier();
-    if (more) issue_tile(Kx, Ks, j_next, false);
+    if (more) issue_tile(Kx, Ks, nxt.ja, nxt.jb, false);
     // mask padded keys (only the last block has any). Branching on the
     // block's valid-key count, which changes with j, keeps the compiler from
     // hoisting loop-invariant compare masks; the lane-half term is folded
     // into the limit so that the compares use immediate key offsets only.
-    const int live_keys = N - j * KBLK;
-    if (live_keys < KBLK) {
-      const int lim = live_keys - 4 * half;
+    if constexpr (PAIR) {
+      // per half: the keys of block ja (tile keys 0-63) and of jb (64-127,
+      // none when the tile holds one block)
+      const int live_a = N - cur.ja * kSrc;
+      const int live_b = cur.has_b ? N - cur.jb * kSrc : 0;
+      if (live_a < kSrc || live_b < kSrc) {
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+        for (int kt = 0; kt < kKT; ++kt) {
+          const int lim = (kt < 2 ? live_a : kSrc + live_b) - 4 * half;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kc = 32 * kt + 8 * (r >> 2) + (r & 3);
-          if (kc >= lim) s[kt][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int kc = 32 * kt + 8 * (r >> 2) + (r & 3);
+            if (kc >= lim) s[kt][r] = -INFINITY;
+          }
         }
+      }
+    } else {
+      const int live_keys = N - cur.ja * KBLK;
+      if (live_keys < KBLK) {
+        const int lim = live_keys - 4 * half;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kc = 32 * kt + 8 * (r >> 2) + (r & 3);
+            if (kc >= lim) s[kt][r] = -INFINITY;
+          }
+      }
     }
     if constexpr (ONLINE) {
       // online softmax (per lane = per query), lazy rescaling
@@ -421,8 +465,9 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   auto run_row = [&](auto onlinec) {
     int kb = kb0;
     if (kb < cnt) {
-      issue_tile(Kx, Ks, block_of(kb), false);
-      issue_tile(Vx, Vs[0], block_of(kb), true);
+      const TileAt t0 = tile_at(kb);
+      issue_tile(Kx, Ks, t0.ja, t0.jb, false);
+      issue_tile(Vx, Vs[0], t0.ja, t0.jb, true);
       wait_vmem();
     }
     lds_barrier();
@@ -498,15 +543,15 @@ hipError_t launch_t(const Tin* q, const Tin* k, const Tin* v,
   using Tout = Tin;
   Tout* o = static_cast<Tout*>(out);
   if (s.B == 128 && key_block(s) == 128)
-    hipLaunchKernelGGL((attn_kernel<128, 128, Tin, Tout>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_kernel<128, 128, false, Tin, Tout>), grid, dim3(256), 0, st,
                        q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
                        scale, o, lse);
   else if (s.B == 128)
-    hipLaunchKernelGGL((attn_kernel<128, 64, Tin, Tout>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_kernel<128, 128, true, Tin, Tout>), grid, dim3(256), 0, st,
                        q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
                        scale, o, lse);
   else
-    hipLaunchKernelGGL((attn_kernel<64, 64, Tin, Tout>), grid, dim3(128), 0, st,
+    hipLaunchKernelGGL((attn_kernel<64, 64, false, Tin, Tout>), grid, dim3(128), 0, st,
                        q, k, v, kept_idx, kept_cnt, k_max, nk, s.N, s.N_pad,
                        scale, o, lse);
   return hipGetLastError();
