@@ -401,6 +401,56 @@ def test_invalid_list_entries_are_skipped_and_empty_rows_are_zero():
     assert np.all(np.isneginf(lse.cpu().numpy()[0, 3 * 128:]))
 
 
+def test_paired_key_blocks_with_invalid_entries_odd_counts_and_partial_blocks():
+    """On the grid of 64-key blocks under 128-query blocks the attention
+    kernel takes a row's valid list entries two at a time into one tile:
+    pairs must form from valid entries only (invalid ones skipped between
+    them), in list order (not sorted), with the second half of the last
+    tile of an odd count empty, and the partial last key block masked in
+    either half of a pair; an empty row is written as zeros."""
+    b = _lib()
+    w, x = _small(name="pe", views=3, patches_per_view=250, specials_per_view=0, heads=1,
+                  block=128, key_block=64)
+    shape = b.Shape(*w.shape_args())
+    nq, nk = w.n_blocks, w.n_kblocks
+    assert (nq, nk, w.N) == (6, 12, 750)  # key block 11 holds 46 keys
+    rows = [[1, -3, 99, 2, 11, 5],    # even: pairs (1, 2), (11, 5), block 11 partial
+            list(range(12)),          # every block: six pairs
+            [3, -1, 5, -1, 6],        # odd: (3, 5), then 6 alone
+            [11, -1],                 # a single partial block
+            [],                       # empty row
+            [10, 0, 11, 4, 7]]        # odd, partial block in a pair's second half
+    k_max = 12
+    idx = np.full((1, nq, k_max), -1, np.int32)
+    cnt = np.zeros((1, nq), np.int32)
+    kept = np.zeros((1, nq, nk), bool)
+    for i, r in enumerate(rows):
+        idx[0, i, :len(r)] = r
+        cnt[0, i] = len(r)
+        for j in r:
+            if 0 <= j < nk:
+                kept[0, i, j] = True
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    out = torch.full_like(q, 7.0)
+    lse = torch.empty((1, w.N_pad), dtype=torch.float32, device="cuda")
+    b.ress_sparse_attn_fwd(q, k, v, shape, torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(cnt).cuda(), k_max, 0.125, out, lse)
+    torch.cuda.synchronize()
+    blocks = [(0, i) for i in range(nq) if rows[i]]
+    O, L = oracle.masked_attention(*(f64(x[t], w) for t in ("q", "k", "v")), kept, w.N,
+                                   w.block, 0.125, blocks=blocks, Bk=64)
+    got = out.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    for _, i in blocks:
+        r0, r1 = i * 128, min((i + 1) * 128, w.N)
+        mx, mean, _ = attn_errors(got[0, r0:r1], O[0, r0:r1])
+        assert mx <= MAX_ABS and mean <= MEAN_ABS, (i, mx, mean)
+        assert np.allclose(gl[0, r0:r1], L[0, r0:r1], rtol=0, atol=LSE_TOL[w.dtype]), i
+    assert np.all(got[0, 4 * 128:5 * 128] == 0)                # the empty row
+    assert np.all(np.isneginf(gl[0, 4 * 128:5 * 128]))
+    assert np.all(got[0, w.N:] == 0)                           # padded query rows
+
+
 @pytest.mark.parametrize("kind", ["sharp", "negative", "mixed"])
 def test_large_logits_rerun_as_online_softmax(kind):
     """Rows whose logits leave the range the kernel's max-free pass accepts
