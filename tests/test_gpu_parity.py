@@ -451,8 +451,9 @@ def test_paired_key_blocks_with_invalid_entries_odd_counts_and_partial_blocks():
     assert np.all(got[0, w.N:] == 0)                           # padded query rows
 
 
+@pytest.mark.parametrize("bk", [128, 64])
 @pytest.mark.parametrize("kind", ["sharp", "negative", "mixed"])
-def test_large_logits_rerun_as_online_softmax(kind):
+def test_large_logits_rerun_as_online_softmax(kind, bk):
     """Rows whose logits leave the range the kernel's max-free pass accepts
     (a row sum outside [2^-64, 2^64], i.e. logits beyond about +-44) are run
     again with a running max. "sharp": queries and keys of large norm, logits
@@ -460,7 +461,8 @@ def test_large_logits_rerun_as_online_softmax(kind):
     of the max-free pass underflow); "mixed": only some query blocks of a head
     are sharp, so workgroups of both kinds run in one launch. Compared with
     the float64 oracle on every query block, and with the dense oracle in
-    dense mode."""
+    dense mode. With 64-key blocks (bk = 64) the kernel pairs kept blocks
+    into 128-key tiles; an odd budget leaves the last tile half empty."""
     b = _lib()
     r = np.random.default_rng({"sharp": 1, "negative": 2, "mixed": 3}[kind])
     H, N, B = 2, 1000, 128
@@ -483,13 +485,13 @@ def test_large_logits_rerun_as_online_softmax(kind):
     f = {t: synth.as_f64(x[t], "bf16") for t in x}
     s_max = np.max(np.abs(0.125 * np.einsum("htd,hud->htu", f["q"][:, :N], f["k"][:, :N])))
     print(f"\n[large-logits] {kind}: max |logit| {s_max:.1f}", flush=True)
-    shape = b.Shape(H, N, N_pad, 64, B)
-    n = shape.n
+    shape = b.Shape(H, N, N_pad, 64, B, bk)
+    nq, n = shape.nq, shape.nk
     rr = np.random.default_rng(11)
-    keep = 4
-    idx = np.stack([np.stack([np.sort(rr.choice(n, keep, replace=False)) for _ in range(n)])
+    keep = 4 if bk == 128 else 5
+    idx = np.stack([np.stack([np.sort(rr.choice(n, keep, replace=False)) for _ in range(nq)])
                     for _ in range(H)]).astype(np.int32)
-    cnt = np.full((H, n), keep, np.int32)
+    cnt = np.full((H, nq), keep, np.int32)
     qt, kt, vt = (to_torch_tokens(x[t], "bf16") for t in ("q", "k", "v"))
     out = torch.empty_like(qt)
     lse = torch.empty((H, N_pad), dtype=torch.float32, device="cuda")
@@ -500,15 +502,15 @@ def test_large_logits_rerun_as_online_softmax(kind):
     b.dense_attention(qt, kt, vt, shape, dense, lse=dlse)
     torch.cuda.synchronize()
     kept = kept_mask_from_lists(idx, cnt, n)
-    O, L = oracle.masked_attention(f["q"], f["k"], f["v"], kept, N, B, 0.125)
+    O, L = oracle.masked_attention(f["q"], f["k"], f["v"], kept, N, B, 0.125, Bk=bk)
     mx, mean, _ = attn_errors(out.float().cpu().numpy()[:, :N], O[:, :N])
-    print(f"[large-logits] {kind}: sparse max-abs {mx:.3e} mean-abs {mean:.3e}")
+    print(f"[large-logits] {kind} bk={bk}: sparse max-abs {mx:.3e} mean-abs {mean:.3e}")
     assert mx <= MAX_ABS and mean <= MEAN_ABS
     dl = np.abs(lse.cpu().numpy()[:, :N] - L[:, :N]) / np.maximum(1.0, np.abs(L[:, :N]))
     assert dl.max() <= 2e-3, dl.max()
     Od, Ld = oracle.dense_attention(f["q"], f["k"], f["v"], N, B, 0.125)
     mx, mean, _ = attn_errors(dense.float().cpu().numpy()[:, :N], Od[:, :N])
-    print(f"[large-logits] {kind}: dense max-abs {mx:.3e} mean-abs {mean:.3e}")
+    print(f"[large-logits] {kind} bk={bk}: dense max-abs {mx:.3e} mean-abs {mean:.3e}")
     assert mx <= MAX_ABS and mean <= MEAN_ABS
     dl = np.abs(dlse.cpu().numpy()[:, :N] - Ld[:, :N]) / np.maximum(1.0, np.abs(Ld[:, :N]))
     assert dl.max() <= 2e-3, dl.max()
