@@ -262,9 +262,15 @@ def scoring_memory(layer):
         if t is not None:
             parts[name] = int(t.numel() * t.element_size())
     total = sum(parts.values())
-    # the fused refinement keeps its per-row state on chip: no workspace
-    return {"bytes": total, "by_buffer": parts,
-            "bytes_with_fused_refinement": total - parts.get("workspace", 0)}
+    # the fused refinement keeps its per-row state on chip: no workspace; the
+    # one-pass selection with refinement also keeps P, the key and vout on
+    # chip
+    res = {"bytes": total, "by_buffer": parts,
+           "bytes_with_fused_refinement": total - parts.get("workspace", 0)}
+    if "workspace" in parts:
+        res["bytes_one_pass"] = total - sum(parts.get(b, 0) for b in ("P", "key", "vout",
+                                                                      "workspace"))
+    return res
 
 
 def select_paths(names=("views8", "views32"), reps=20):
