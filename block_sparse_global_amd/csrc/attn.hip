@@ -296,17 +296,19 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
                  (q & 1) * 4;
   }
 
-  // ---- one tile (from list position kb), V from buffer B (compile-time, so
-  // all LDS offsets are immediates); ONLINE: the second pass, with a running
-  // max. Returns the list position of the next tile.
-  auto process = [&](auto bufc, auto onlinec, int kb) {
+  // ---- one tile, cur, with V from buffer B (compile-time, so all LDS
+  // offsets are immediates); nxt is the tile after it. ONLINE: the second
+  // pass, with a running max. Moves cur and nxt one tile on and returns
+  // whether a tile followed.
+  auto process = [&](auto bufc, auto onlinec, TileAt& cur, TileAt& nxt) {
     constexpr int B = decltype(bufc)::value;
     constexpr bool ONLINE = decltype(onlinec)::value;
-    const TileAt cur = tile_at(kb);
-    const int kb_next = cur.next;
-    const bool more = kb_next < cnt;
-    TileAt nxt{0, 0, 0, false};
-    if (more) nxt = tile_at(kb_next);
+    const bool more = cur.next < cnt;
+    // square tiles: the next tile was looked up one block ahead; pairs
+    // (whose lookup scans for two valid entries) are looked up here
+    if constexpr (PAIR) {
+      if (more) nxt = tile_at(cur.next);
+    }
     if (more) issue_tile(Vx, Vs[B ^ 1], nxt.ja, nxt.jb, true);
 
     // S^T = K Q^T; the K operands of tile kt+1 are read while tile kt's
@@ -339,6 +341,12 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     // replace this one
     lds_barrier();
     if (more) issue_tile(Kx, Ks, nxt.ja, nxt.jb, false);
+    // the list entries of the tile after next, looked up now so that the
+    // next block issues its copies without waiting for scalar loads
+    TileAt nxt2{0, 0, cnt, false};
+    if constexpr (!PAIR) {
+      if (more && nxt.next < cnt) nxt2 = tile_at(nxt.next);
+    }
     // mask padded keys (only the last block has any). Branching on the
     // block's valid-key count, which changes with j, keeps the compiler from
     // hoisting loop-invariant compare masks; the lane-half term is folded
@@ -454,7 +462,9 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
     l_run += psum;
     wait_vmem();  // this wave's copies of the next block's tiles have landed
     lds_barrier();
-    return kb_next;
+    cur = nxt;
+    nxt = nxt2;
+    return more;
   };
 
   // ---- the row, first without a max; again with one if any valid row of
@@ -463,18 +473,20 @@ __global__ __launch_bounds__(BLK * 2, 3) void attn_kernel(
   if (tid == 0) rerun = 0;
   const int kb0 = next_valid(0);
   auto run_row = [&](auto onlinec) {
-    int kb = kb0;
-    if (kb < cnt) {
-      const TileAt t0 = tile_at(kb);
-      issue_tile(Kx, Ks, t0.ja, t0.jb, false);
-      issue_tile(Vx, Vs[0], t0.ja, t0.jb, true);
+    TileAt cur{0, 0, cnt, false}, nxt{0, 0, cnt, false};
+    if (kb0 < cnt) {
+      cur = tile_at(kb0);
+      if (!PAIR && cur.next < cnt) nxt = tile_at(cur.next);
+      issue_tile(Kx, Ks, cur.ja, cur.jb, false);
+      issue_tile(Vx, Vs[0], cur.ja, cur.jb, true);
       wait_vmem();
     }
     lds_barrier();
-    while (kb < cnt) {
-      kb = process(std::integral_constant<int, 0>{}, onlinec, kb);
-      if (kb >= cnt) break;
-      kb = process(std::integral_constant<int, 1>{}, onlinec, kb);
+    if (kb0 < cnt) {
+      for (;;) {
+        if (!process(std::integral_constant<int, 0>{}, onlinec, cur, nxt)) break;
+        if (!process(std::integral_constant<int, 1>{}, onlinec, cur, nxt)) break;
+      }
     }
   };
   run_row(std::false_type{});
