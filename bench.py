@@ -46,9 +46,9 @@ CDF_TAU = 0.05
 # for the kernel source they were taken on; any other source reports null.
 ATTN_TRAFFIC = {
     "workload": "views100",
-    "source_sha256": "2074e01e40aee518a1e56c4da38db27d547a3c4592ad714851d760cecc92ccd6",
-    "read_bytes": 9854327936,
-    "write_bytes": 457514496,
+    "source_sha256": "eb6ff29c685cdab33915feda1976406b89f456d3c9d7cba45c2b0c290ec67883",
+    "read_bytes": 8700902912,
+    "write_bytes": 457521152,
 }
 
 
