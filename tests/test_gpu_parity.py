@@ -778,6 +778,47 @@ def test_select_refine_fused_matches_oracle(name):
     _select_refine_fused_check(*_fused_case(name))
 
 
+@pytest.mark.parametrize("name", ["views8", "views8-k64"])
+def test_select_refine_fused_without_rounds_is_the_top_k(name):
+    """ress_select_refine_fused with no rounds: the lists are the drift
+    top-k sets (the oracle's, up to near-ties) and J_final equals J_init,
+    which equals the oracle's J of those sets (Eq. 11-12) to 1e-9."""
+    b = _lib()
+    w, x = case_inputs(name)
+    shape = b.Shape(*w.shape_args())
+    H, nq, nk = shape.H, shape.nq, shape.nk
+    q, k, v = (to_torch_tokens(x[t], w.dtype) for t in ("q", "k", "v"))
+    layer = b.BlockSparseGlobalAttention(shape, x["keep"], x["always"], mode="drift")
+    layer.pool(q, k, v)
+    f64t = dict(dtype=torch.float64, device="cuda")
+    vmv = torch.empty((H, nk), **f64t)
+    J0, J1 = torch.empty((H, nq), **f64t), torch.empty((H, nq), **f64t)
+    b.ress_select_refine_fused(layer.qpool, layer.kpool, layer.vpool, None, shape, layer.scale,
+                               layer.eps, x["keep"], x["always"], 0, 0.5, layer.k_max, vmv,
+                               layer.kept_idx, layer.kept_cnt, J0, J1)
+    torch.cuda.synchronize()
+    gi, gc = layer.kept_idx.cpu().numpy(), layer.kept_cnt.cpu().numpy()
+    check_lists_wellformed(gi, gc, x["keep"], x["always"], nk)
+    qp = oracle.block_pool(f64(x["q"], w), w.N, w.block)
+    kp = oracle.block_pool(f64(x["k"], w), w.N, w.kblock)
+    vp = oracle.block_pool(f64(x["v"], w), w.N, w.kblock)
+    P = oracle.block_map(qp, kp, 1.0 / math.sqrt(w.head_dim))
+    key, vout, _ = oracle.drift_key(P, vp, None, 1e-4)
+    kept, _ = oracle.select_topk(key, x["keep"], x["always"])
+    gm = kept_mask_from_lists(gi, gc, nk)
+    nd = compare_masks(gm, kept, key, x["always"], x["keep"])
+    g0, g1 = J0.cpu().numpy(), J1.cpu().numpy()
+    assert np.array_equal(g0, g1)
+    cand = x["always"] == 0
+    for h in range(H):
+        for i in range(nq):
+            d = P[h, i][:, None] * (vout[h, i][None] - vp[h])
+            Jo = oracle.drop_objective(P[h, i], d, np.eye(w.head_dim), cand & ~gm[h, i])[3]
+            assert g0[h, i] == pytest.approx(Jo, rel=1e-9), (h, i)
+    print(f"\n[select-refine-fused rounds=0] {name}: {nd} near-tie rows; J_init = J_final on "
+          f"all {H * nq} rows")
+
+
 @pytest.mark.parametrize("idx", range(6))
 def test_select_refine_fused_random_shapes(idx):
     """Seeded ragged shapes: both block grids, one to three heads with unequal
