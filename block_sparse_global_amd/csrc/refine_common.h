@@ -157,12 +157,14 @@ struct SelKeys<0> {  // long rows: the keys are read from LDS as needed
 // Exact top-m of one row's gains within one wave. Lane l owns key blocks
 // j = l + 64k; bit k of `member` marks membership (members have j < n).
 // Returns the selected elements of this lane as a bitmask over k. Radix
-// select on 8-bit digits; each pass first finds the bits that every key
-// still in play shares and takes its digit just below that common prefix,
-// so no pass is spent on digits that cannot separate the keys (the leading
-// bits of the gains are mostly equal) and the histogram counts spread over
-// many bins. KPL > 0: the lane's KPL >= ceil(n / 64) keys are in registers;
-// KPL = 0: up to 64 per lane, read from LDS.
+// select on 8-bit digits. The first digit is taken just below the bits that
+// every member shares (the leading bits of the gains are mostly equal), so
+// its histogram counts spread over many bins; each later pass takes the next
+// 8 bits down, since the keys still in play share every bit above them. The
+// per-key loops are branch-free (selects on the membership bits), and the
+// wave-wide reductions run once per select, not once per pass. KPL > 0: the
+// lane's KPL >= ceil(n / 64) keys are in registers; KPL = 0: up to 64 per
+// lane, read from LDS.
 template <int KPL>
 __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL>& key,
                                                               uint64_t member, int n, int m,
@@ -176,78 +178,83 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
   using Mask = typename std::conditional<(KPL > 0 && KPL <= 32), uint32_t, uint64_t>::type;
   Mask selected = 0, inplay = (Mask)member;
   int need = m;
-  // AND and OR of the keys in play; each pass's update loop forms those of
-  // the next pass
+  // AND and OR of the members' keys: their XOR marks the bits that differ
   uint64_t all1 = ~0ull, any1 = 0ull;
 #pragma unroll kU
-  for (int k = 0; k < kK; ++k)
-    if ((inplay >> k) & 1u) {
-      all1 &= key(k);
-      any1 |= key(k);
-    }
-  for (;;) {
-    const uint64_t diff = wave_and64(all1) ^ wave_or64(any1);
-    if (diff == 0ull) break;  // the keys in play are all equal
+  for (int k = 0; k < kK; ++k) {
+    const uint64_t kv = key(k);
+    const bool in = (inplay >> k) & 1u;
+    all1 &= in ? kv : ~0ull;
+    any1 |= in ? kv : 0ull;
+  }
+  const uint64_t diff = wave_and64(all1) ^ wave_or64(any1);
+  if (diff != 0ull) {
     const int top = 63 - __clzll((long long)diff);
-    const int shift = top >= 7 ? top - 7 : 0;
-    for (int b = lane; b < 256; b += 64) whist[b] = 0u;
-    wave_lds_sync();
+    // digit [shift, shift + 8): every key in play shares the bits above it
+    int shift = top >= 7 ? top - 7 : 0;
+    for (;;) {
+      for (int b = lane; b < 256; b += 64) whist[b] = 0u;
+      wave_lds_sync();
 #pragma unroll kU
-    for (int k = 0; k < kK; ++k)
-      if ((inplay >> k) & 1u) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
-    wave_lds_sync();
-    int c[4];
-    int s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = (int)whist[255 - 4 * lane - q];
-      s += c[q];
-    }
-    int x = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    const int before = x - s;
-    const bool found = before < need && need <= x;
-    int dsel = 0, above = 0, atd = 0;
-    if (found) {
-      int cum = before;
+      for (int k = 0; k < kK; ++k)
+        if ((inplay >> k) & 1u) atomicAdd(&whist[(uint32_t)(key(k) >> shift) & 255u], 1u);
+      wave_lds_sync();
+      int c[4];
+      int s = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (cum + c[q] >= need) {
-          dsel = 255 - 4 * lane - q;
-          above = cum;
-          atd = c[q];
-          break;
-        }
-        cum += c[q];
+        c[q] = (int)whist[255 - 4 * lane - q];
+        s += c[q];
       }
-    }
-    const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
-    dsel = __shfl(dsel, src, 64);
-    above = __shfl(above, src, 64);
-    atd = __shfl(atd, src, 64);
-    wave_lds_sync();
-    all1 = ~0ull;
-    any1 = 0ull;
+      int x = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const int before = x - s;
+      const bool found = before < need && need <= x;
+      int dsel = 0, above = 0, atd = 0;
+      if (found) {
+        int cum = before;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (cum + c[q] >= need) {
+            dsel = 255 - 4 * lane - q;
+            above = cum;
+            atd = c[q];
+            break;
+          }
+          cum += c[q];
+        }
+      }
+      const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+      dsel = __shfl(dsel, src, 64);
+      above = __shfl(above, src, 64);
+      atd = __shfl(atd, src, 64);
+      wave_lds_sync();
+      // keys above the chosen digit are selected; only those at it stay in
+      // play (a key already out of play keeps both of its bits). The digits
+      // are formed again rather than kept from the histogram loop (the shift
+      // passes through readfirstlane, so the compiler does not hold 17 or 34
+      // of them live), and the comparisons are integer arithmetic on values
+      // below 256, so no lane masks pile up in scalar registers.
+      const int sh = __builtin_amdgcn_readfirstlane(shift);
+      const uint32_t ds = (uint32_t)dsel;
 #pragma unroll kU
-    for (int k = 0; k < kK; ++k) {
-      if ((inplay >> k) & 1u) {
-        const uint64_t kv = key(k);
-        const int dig = (int)((uint32_t)(kv >> shift) & 255u);
-        if (dig > dsel) selected |= (Mask)1 << k;
-        if (dig != dsel) {
-          inplay &= ~((Mask)1 << k);
-        } else {
-          all1 &= kv;
-          any1 |= kv;
-        }
+      for (int k = 0; k < kK; ++k) {
+        const uint32_t dig = (uint32_t)(key(k) >> sh) & 255u;
+        const Mask in = (inplay >> k) & 1u;
+        const Mask gt = (Mask)((ds - dig) >> 31);         // dig > dsel
+        const Mask ne = (Mask)(((dig ^ ds) + 255u) >> 8);  // dig != dsel
+        selected |= (gt & in) << k;
+        inplay &= ~(ne << k);
       }
+      need -= above;
+      if (atd == need) return (uint64_t)(selected | inplay);
+      if (shift == 0) break;  // every bit decided: the keys in play are equal
+      shift = shift >= 8 ? shift - 8 : 0;
     }
-    need -= above;
-    if (atd == need) return (uint64_t)(selected | inplay);
   }
   // equal keys remain: take the lowest `need` block indices (k-major order)
   const uint64_t below = (1ull << lane) - 1ull;
