@@ -119,16 +119,46 @@ __device__ __attribute__((always_inline)) void apply_changes(const int32_t* chg,
   }
 }
 
-// Bitwise AND / OR of a 64-bit value over the wave.
+// Wave-wide AND / OR of a 64-bit value and an inclusive prefix sum of an
+// int, on DPP lane moves (vector ALU) and lane reads instead of LDS
+// permutes. The results are exact whatever the combination order.
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1 and
+// [2,3,0,1] = 0x4E, row_mirror 0x140, row_half_mirror 0x141,
+// row_shr:n 0x110 + n, row_bcast:15 0x142, row_bcast:31 0x143.
+template <bool kAnd>
+__device__ inline uint32_t wave_bitop32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return kAnd ? (a & b) : (a | b); };
+  // every lane of a 16-lane row ends with its row's value (no lane of these
+  // moves reads outside its row)
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
 __device__ inline uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v &= (uint64_t)__shfl_xor((long long)v, o, 64);
-  return v;
+  return ((uint64_t)wave_bitop32<true>((uint32_t)(v >> 32)) << 32) |
+         wave_bitop32<true>((uint32_t)v);
 }
 __device__ inline uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= (uint64_t)__shfl_xor((long long)v, o, 64);
-  return v;
+  return ((uint64_t)wave_bitop32<false>((uint32_t)(v >> 32)) << 32) |
+         wave_bitop32<false>((uint32_t)v);
+}
+// Lane l gets x_0 + ... + x_l. Row prefixes by shifts of 1, 2, 4 and 8
+// lanes (a source outside the row reads 0), then lane 15 of rows 0 and 2 is
+// added to rows 1 and 3, and lane 31 (the total of rows 0-1) to rows 2-3.
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
 }
 
 template <int KPL>
@@ -206,12 +236,7 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
         c[q] = (int)whist[255 - 4 * lane - q];
         s += c[q];
       }
-      int x = s;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
+      const int x = wave_incl_scan(s);
       const int before = x - s;
       const bool found = before < need && need <= x;
       int dsel = 0, above = 0, atd = 0;
@@ -228,6 +253,7 @@ __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL
           cum += c[q];
         }
       }
+      // exactly one lane finds the digit (the counts rise along the lanes)
       const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
       dsel = __shfl(dsel, src, 64);
       above = __shfl(above, src, 64);
