@@ -187,7 +187,10 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
 // ---------------------------------------------------------------- gains
 // C[i][j] = u_i . V_j over a 64 x 64 tile (rows i < nq, key blocks j < nk)
 // of one head on the float64 matrix cores (mfma_tile_f64); the epilogue
-// issues all its loads first, then forms the gain of each (i, j).
+// takes the lane's rows two at a time (the loads of a pass, then its gains),
+// which keeps the kernel within 128 VGPRs: four workgroups per CU, where the
+// latency of its HBM reads needs the extra waves (issuing the epilogue's
+// loads ahead of the product measured slower at 240 VGPRs).
 __device__ inline void load8d(const double* p, double (&x)[8]) {
   const double2* src = reinterpret_cast<const double2*>(p);
 #pragma unroll
@@ -198,7 +201,7 @@ __device__ inline void load8d(const double* p, double (&x)[8]) {
   }
 }
 
-__global__ __launch_bounds__(256) void refine_gains_kernel(
+__global__ __launch_bounds__(256, 4) void refine_gains_kernel(
     const double* __restrict__ P, const double* __restrict__ key,
     const double* __restrict__ vpool, int nq, int nk, SelConfig cfg, int round, double rho,
     double eps, RefineWs ws) {
@@ -218,42 +221,45 @@ __global__ __launch_bounds__(256) void refine_gains_kernel(
   // epilogue: the exact objective decrease of each swap (Eq. 13-16). Out
   // of range rows and blocks load from a clamped valid address and are not
   // stored. The lane's results cover 8 rows (tr, r) x 2 key blocks (tc),
-  // taken in two passes of 4 rows: all loads of a pass, then its gains.
+  // taken in four passes of 2 rows: all loads of a pass, then its gains.
   const TileF64Map mp;
   const int fs = flag_stride(nk);
 #pragma unroll
   for (int tr = 0; tr < 2; ++tr) {
-    double pv[4][2], kv[4][2];
-    uint8_t fv[4][2];
-    double sK[4], sG[4], sJ[4], svu[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t row = (size_t)h * nq + min(i0 + mp.row_of(tr, r), nq - 1);
-      const RowState* st = ws.rs + row;
-      sK[r] = st->K;
-      sG[r] = st->G;
-      sJ[r] = st->J;
-      svu[r] = st->vu;
+    for (int rh = 0; rh < 4; rh += 2) {
+      double pv[2][2], kv[2][2];
+      uint8_t fv[2][2];
+      double sK[2], sG[2], sJ[2], svu[2];
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
-        const int j = min(j0 + mp.col_of(tc), nk - 1);
-        pv[r][tc] = P[row * nk + j];
-        kv[r][tc] = key[row * nk + j];
-        fv[r][tc] = ws.fcur[row * fs + j];
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const size_t row = (size_t)h * nq + min(i0 + mp.row_of(tr, rh + r2), nq - 1);
+        const RowState* st = ws.rs + row;
+        sK[r2] = st->K;
+        sG[r2] = st->G;
+        sJ[r2] = st->J;
+        svu[r2] = st->vu;
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) {
+          const int j = min(j0 + mp.col_of(tc), nk - 1);
+          pv[r2][tc] = P[row * nk + j];
+          kv[r2][tc] = key[row * nk + j];
+          fv[r2][tc] = ws.fcur[row * fs + j];
+        }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + mp.row_of(tr, r);
-      const size_t row = (size_t)h * nq + i;
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const int i = i0 + mp.row_of(tr, rh + r2);
+        const size_t row = (size_t)h * nq + i;
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
-        const int j = j0 + mp.col_of(tc);
-        const double p = pv[r][tc];
-        const double sv = kv[r][tc] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
-        const double dJ = swap_gain(RowScalars{sK[r], sG[r], sJ[r], svu[r]}, p, sv,
-                                    acc[tr][tc][r], fv[r][tc] != 0);
-        if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
+        for (int tc = 0; tc < 2; ++tc) {
+          const int j = j0 + mp.col_of(tc);
+          const double p = pv[r2][tc];
+          const double sv = kv[r2][tc] * fmax(1.0 - p, eps);  // s_ij (Eq. 6)
+          const double dJ = swap_gain(RowScalars{sK[r2], sG[r2], sJ[r2], svu[r2]}, p, sv,
+                                      acc[tr][tc][rh + r2], fv[r2][tc] != 0);
+          if (i < nq && j < nk) ws.gains[row * nk + j] = order_key(dJ);
+        }
       }
     }
   }
