@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
   const double* Prow = P + row * n;
   const double* Vh = vpool + (size_t)h * n * kD;
 
-  for (int j = lane; j < n; j += 64) flags[j] = sel_always(cfg, j) ? 0 : 1;
+  for (int j = lane; j < n; j += 64) flags[j] = sel_always_wave(cfg, j) ? 0 : 1;
   wave_lds_sync();
   int cnt = kept_cnt[row];
   cnt = cnt < 0 ? 0 : (cnt > k_max ? k_max : cnt);
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64) void refine_init_kernel(
       const bool inD = in && f != 0, kept = in && f == 0;
       if (inD) ks += pv[u];
       nD += inD;
-      nS += kept && !sel_always(cfg, j);
+      nS += kept && !sel_always_wave(cfg, j);
       const uint64_t msk = __ballot(kept);
       if (kept) slist[pos + __popcll(msk & below)] = j;
       pos += __popcll(msk);
@@ -295,14 +295,30 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
   const int m = min(m_base, min(st.nD, st.nS));
   wave_lds_sync();
 
+  // membership over the candidates (always-kept blocks excluded). With 17
+  // keys per lane the loop is branch-free, so all the flag reads and bitmask
+  // words are issued together; with more keys that form holds too many of
+  // them live (156 VGPRs against 114 at 34 keys per lane), so it stays a
+  // loop that tests key by key.
   uint64_t memD = 0, memS = 0;
   constexpr int kU = KPL > 0 ? KPL : 4;
+  if constexpr (KPL == 17) {
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+      const int j = lane + 64 * k;
+      const bool cand = j < n && !sel_always_wave(cfg, j);
+      const bool inD = flags[min(j, n - 1)] != 0;
+      memD |= (uint64_t)(cand && inD) << k;
+      memS |= (uint64_t)(cand && !inD) << k;
+    }
+  } else {
 #pragma unroll kU
-  for (int k = 0; k < (KPL > 0 ? KPL : 64); ++k) {
-    const int j = lane + 64 * k;
-    if (j >= n) break;
-    if (sel_always(cfg, j)) continue;
-    if (flags[j]) memD |= 1ull << k; else memS |= 1ull << k;
+    for (int k = 0; k < (KPL > 0 ? KPL : 64); ++k) {
+      const int j = lane + 64 * k;
+      if (j >= n) break;
+      if (sel_always_wave(cfg, j)) continue;
+      if (flags[j]) memD |= 1ull << k; else memS |= 1ull << k;
+    }
   }
   const uint64_t restore = wave_select<KPL>(keys, memD, n, m, whist);
   const uint64_t drop = wave_select<KPL>(keys, memS, n, m, whist);
@@ -401,7 +417,7 @@ __global__ __launch_bounds__(64) void refine_final_kernel(
   int pos = 0;
   for (int j0 = 0; j0 < n; j0 += 64) {
     const int j = j0 + lane;
-    const bool kept = j < n && (sel_always(cfg, j) || !fb[j]);
+    const bool kept = j < n && (sel_always_wave(cfg, j) || !fb[j]);
     const uint64_t msk = __ballot(kept);
     const int p = pos + __popcll(msk & below);
     if (kept && p < k_max) out[p] = j;

@@ -227,10 +227,10 @@ __global__ __launch_bounds__(64 * fused_rows<POOLED>()) void refine_fused_kernel
       // dropped: the candidates outside the top-k
       for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
         const int j = j0 + lane;
-        if (j < n) flags[j] = (sel_always(cfg, j) || ((kept_bits >> k) & 1ull)) ? 0 : 1;
+        if (j < n) flags[j] = (sel_always_wave(cfg, j) || ((kept_bits >> k) & 1ull)) ? 0 : 1;
       }
     } else {
-      for (int j = lane; j < n; j += 64) flags[j] = sel_always(cfg, j) ? 0 : 1;
+      for (int j = lane; j < n; j += 64) flags[j] = sel_always_wave(cfg, j) ? 0 : 1;
       wave_lds_sync();
       int cnt = A.kept_cnt[row];
       cnt = cnt < 0 ? 0 : (cnt > A.k_max ? A.k_max : cnt);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * fused_rows<POOLED>()) void refine_fused_kernel
       const bool inD = in && f != 0, kept = in && f == 0;
       if (inD) ks += Prow[j];
       nD += inD;
-      nS += kept && !sel_always(cfg, j);
+      nS += kept && !sel_always_wave(cfg, j);
       const uint64_t dm = __ballot(inD);
       if (lane == 0) {
         mycur[k] = dm;
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * fused_rows<POOLED>()) void refine_fused_kernel
     int pos = 0;
     for (int k = 0, j0 = 0; j0 < n; ++k, j0 += 64) {
       const int j = j0 + lane;
-      const bool kept = j < n && (sel_always(cfg, j) || !((mybest[k] >> lane) & 1ull));
+      const bool kept = j < n && (sel_always_wave(cfg, j) || !((mybest[k] >> lane) & 1ull));
       const uint64_t msk = __ballot(kept);
       const int p = pos + __popcll(msk & below);
       if (kept && p < A.k_max) out[p] = j;

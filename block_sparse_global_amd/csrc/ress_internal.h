@@ -29,6 +29,14 @@ struct SelConfig {
 __host__ __device__ inline bool sel_always(const SelConfig& c, int j) {
   return (c.always_bits[j >> 6] >> (j & 63)) & 1ull;
 }
+// The same flag where each lane of a wave asks for block j = 64 q + lane, q
+// the same in every lane: the bitmask word is read once for the wave (a
+// scalar load from the kernel arguments) instead of by a vector load in each
+// lane, which a per-key loop would otherwise wait for key by key.
+__device__ inline bool sel_always_wave(const SelConfig& c, int j) {
+  const int q = __builtin_amdgcn_readfirstlane(j >> 6) & (RESS_MAX_BLOCKS / 64 - 1);
+  return (c.always_bits[q] >> (j & 63)) & 1ull;
+}
 
 // 64-bit key whose unsigned order is the float64 order (-0 counted as +0).
 __device__ inline uint64_t order_key(double x) {

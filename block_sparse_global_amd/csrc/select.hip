@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(
     const int j = lane + 64 * k;
     keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
     if (j < n) {
-      if (sel_always(cfg, j))
+      if (sel_always_wave(cfg, j))
         always |= 1ull << k;
       else
         member |= 1ull << k;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void cdf_wave_kernel(
     const int j = lane + 64 * k;
     keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
     if (j < n) {
-      if (sel_always(cfg, j))
+      if (sel_always_wave(cfg, j))
         always |= 1ull << k;
       else
         member |= 1ull << k;

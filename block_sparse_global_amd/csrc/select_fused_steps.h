@@ -159,7 +159,7 @@ __device__ inline uint64_t fused_topk_bits(const double* keyrow, int n, const Se
     const int j = lane + 64 * k;
     keys.v[k] = j < n ? order_key(__longlong_as_double((long long)keys.v[k])) : 0ull;
     if (j < n) {
-      if (sel_always(cfg, j))
+      if (sel_always_wave(cfg, j))
         always |= 1ull << k;
       else
         member |= 1ull << k;
