@@ -191,10 +191,10 @@ struct SelKeys<0> {  // long rows: the keys are read from LDS as needed
 // every member shares (the leading bits of the gains are mostly equal), so
 // its histogram counts spread over many bins; each later pass takes the next
 // 8 bits down, since the keys still in play share every bit above them. The
-// per-key loops are branch-free (selects on the membership bits), and the
-// wave-wide reductions run once per select, not once per pass. KPL > 0: the
-// lane's KPL >= ceil(n / 64) keys are in registers; KPL = 0: up to 64 per
-// lane, read from LDS.
+// per-key update loop is branch-free (integer arithmetic on the membership
+// bits), and the wave-wide AND / OR runs once per select, not once per pass.
+// KPL > 0: the lane's KPL >= ceil(n / 64) keys are in registers; KPL = 0: up
+// to 64 per lane, read from LDS.
 template <int KPL>
 __device__ __attribute__((always_inline)) uint64_t wave_select(const SelKeys<KPL>& key,
                                                               uint64_t member, int n, int m,
