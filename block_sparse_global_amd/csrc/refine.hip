@@ -345,25 +345,32 @@ __global__ __launch_bounds__(64) void refine_select_kernel(
   double g = ws.g[row * kD + d];
   double mag = fabs(g);  // what g is formed from, for the cancellation guard
   double dk = 0.0;
-  // batches of 16 changes: all loads of a batch are issued before its sums
+  // batches of 16 changes: all loads of a batch are issued before its sums.
+  // Lanes 0-15 read the batch's entries from LDS in one access; each entry
+  // then goes to a scalar register (readlane), so the block addresses are
+  // formed by scalar instructions and the P values come in by scalar loads.
   for (int q0 = 0; q0 < nchg; q0 += 16) {
     int ev[16];
     double pv[16], vv[16];
+    const int mine = chg[min(q0 + (lane & 15), nchg - 1)];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int q = min(q0 + t, nchg - 1);
-      ev[t] = chg[q];
+      ev[t] = __builtin_amdgcn_readlane(mine, t);
       const int j = (ev[t] > 0 ? ev[t] : -ev[t]) - 1;
       pv[t] = Prow[j];
       vv[t] = Vh[(size_t)j * kD + d];
     }
+    // a uniform bound instead of a break, so that the loop unrolls and the
+    // batch's registers are addressed directly
+    const int live = min(16, nchg - q0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      if (q0 + t >= nchg) break;
-      const double dj = pv[t] * (vod - vv[t]);
-      g = (ev[t] > 0) ? g + dj : g - dj;
-      mag += fabs(dj);
-      dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
+      if (t < live) {
+        const double dj = pv[t] * (vod - vv[t]);
+        g = (ev[t] > 0) ? g + dj : g - dj;
+        mag += fabs(dj);
+        dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
+      }
     }
   }
   if (g_cancelled(g, mag))

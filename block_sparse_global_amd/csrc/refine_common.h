@@ -100,21 +100,27 @@ __device__ __attribute__((always_inline)) void apply_changes(const int32_t* chg,
   for (int q0 = 0; q0 < nchg; q0 += 8) {
     int ev[8];
     double pv[8], vv[8];
+    // lanes 0-7 read the batch's entries in one LDS access; each goes to a
+    // scalar register (readlane), so the addresses are scalar work
+    const int mine = chg[min(q0 + (d & 7), nchg - 1)];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int q = min(q0 + t, nchg - 1);
-      ev[t] = chg[q];
+      ev[t] = __builtin_amdgcn_readlane(mine, t);
       const int j = (ev[t] > 0 ? ev[t] : -ev[t]) - 1;
       pv[t] = Prow[j];
       vv[t] = Vh[(size_t)j * kD + d];
     }
+    // a uniform bound instead of a break, so that the loop unrolls and the
+    // batch's registers are addressed directly
+    const int live = min(8, nchg - q0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      if (q0 + t >= nchg) break;
-      const double dj = pv[t] * (vod - vv[t]);
-      g = (ev[t] > 0) ? g + dj : g - dj;
-      mag += fabs(dj);
-      dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
+      if (t < live) {
+        const double dj = pv[t] * (vod - vv[t]);
+        g = (ev[t] > 0) ? g + dj : g - dj;
+        mag += fabs(dj);
+        dk = (ev[t] > 0) ? dk - pv[t] : dk + pv[t];  // K: +P for a restore, -P for a drop
+      }
     }
   }
 }

@@ -274,16 +274,19 @@ __global__ __launch_bounds__(64 * fused_rows<POOLED>()) void refine_fused_kernel
     const int len = overD ? dpos : pos;
     for (int q0 = 0; q0 < len; q0 += 16) {
       double pv[16], vv[16];
+      // lanes 0-15 read the batch's list entries in one LDS access; each
+      // goes to a scalar register, so the addresses are scalar work
+      const int qm = min(q0 + (lane & 15), len - 1);
+      const int mine = slist[overD ? n - 1 - qm : qm];
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int qq = min(q0 + t, len - 1);
-        const int j = slist[overD ? n - 1 - qq : qq];
+        const int j = __builtin_amdgcn_readlane(mine, t);
         pv[t] = Prow[j];
         vv[t] = Vh[(size_t)j * kD + d];
       }
 #pragma unroll
       for (int t = 0; t < 16; ++t)
-        if (q0 + t < len) acc += overD ? pv[t] * (vod - vv[t]) : pv[t] * (vv[t] - vod);
+        if (q0 + t < len) acc = fma(pv[t], overD ? vod - vv[t] : vv[t] - vod, acc);
     }
     g = acc;  // an empty D: the empty sum of Eq. 10
     ul[d] = g;
