@@ -47,8 +47,8 @@ CDF_TAU = 0.05
 ATTN_TRAFFIC = {
     "workload": "views100",
     "source_sha256": "eb6ff29c685cdab33915feda1976406b89f456d3c9d7cba45c2b0c290ec67883",
-    "read_bytes": 8811731328,
-    "write_bytes": 457520128,
+    "read_bytes": 8715566336,
+    "write_bytes": 457521152,
 }
 
 
