@@ -48,7 +48,9 @@ __device__ inline void load8d(const double* p, double (&x)[8]) {
 }
 
 // Logits scale * qpool_i . kpool_j of one 64 x 64 tile, written into P.
-__global__ __launch_bounds__(kThreads) void logits_kernel(
+// Within 128 VGPRs (four workgroups per CU, as its LDS allows): 98 -> 92 us
+// per call against the uncapped 132 VGPRs, the same bits.
+__global__ __launch_bounds__(kThreads, 4) void logits_kernel(
     const double* __restrict__ qpool, const double* __restrict__ kpool, double scale, int nq,
     int nk, double* __restrict__ P) {
   __shared__ TileF64Smem sm;
