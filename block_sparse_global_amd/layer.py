@@ -36,8 +36,8 @@ from ._lib import (
 
 # Rows up to this many key blocks take the fused selection under
 # select_impl="auto". Measured on the MI355X (score and top-k together):
-# 0.020 against 0.031 ms for the unfused calls at 86 key blocks (8 views),
-# 0.113 against 0.083 ms at 344 (32 views); longer rows stream more pooled
+# 0.020 against 0.030 ms for the unfused calls at 86 key blocks (8 views),
+# 0.110 against 0.081 ms at 344 (32 views); longer rows stream more pooled
 # blocks through each row tile than the split kernels read.
 SELECT_FUSED_AUTO_MAX_BLOCKS = 128
 
